@@ -1,0 +1,197 @@
+"""CPU oracle for the fused per-token-quantize -> int8 GEMM -> dequant linear layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package. The GPU library never
+imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C loops, compiled with gcc at
+``-O2 -fno-fast-math -ffp-contract=off``, OpenMP over rows only); this module
+builds it, loads it with ctypes and wraps it for numpy arrays. Every function
+cites the passage of the pages it follows in ``oracle.c``.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+against closed forms, exact rational arithmetic, brute force on tiny inputs and
+hand-worked fixtures under ``tests/golden/``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", "-std=c11"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc). Returns the path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_quantize_per_token.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+        lib.oracle_quantize_weight.argtypes = [vp, i64, i64, i32, i32, vp, vp]
+        lib.oracle_unpack_int4.argtypes = [vp, i64, i64, vp]
+        lib.oracle_gemm_i32.argtypes = [vp, vp, i64, i64, i64, vp]
+        lib.oracle_group_acc.argtypes = [vp, vp, i64, i64, i64, i32, vp]
+        lib.oracle_dequant_pc.argtypes = [vp, vp, vp, i64, i64, vp]
+        lib.oracle_dequant_pg.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
+        for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
+                  lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
+                  lib.oracle_dequant_pg):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc == 1:
+        raise ValueError(f"oracle {what}: bad argument")
+    if rc == 2:
+        raise OverflowError(f"oracle {what}: int32 accumulator overflow")
+    if rc != 0:
+        raise RuntimeError(f"oracle {what}: status {rc}")
+
+
+def quantize_per_token(x: np.ndarray):
+    """x: float16 (or a bf16 bit pattern array tagged via ``bf16=True`` wrapper) [M, K].
+
+    Returns (x_q int8 [M, K], s_x float32 [M]).
+    """
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        bits, is_bf16 = x.view(np.uint16), 0
+    else:
+        raise TypeError("quantize_per_token expects float16; use quantize_per_token_bf16 for bf16 bits")
+    return _qpt(bits, is_bf16)
+
+
+def quantize_per_token_bf16(bits: np.ndarray):
+    """Like quantize_per_token, for a uint16 array holding bfloat16 bit patterns."""
+    return _qpt(np.ascontiguousarray(bits, dtype=np.uint16), 1)
+
+
+def _qpt(bits: np.ndarray, is_bf16: int):
+    M, K = bits.shape
+    xq = np.empty((M, K), np.int8)
+    sx = np.empty((M,), np.float32)
+    _check(_load().oracle_quantize_per_token(_p(bits), is_bf16, M, K, K, _p(xq), _p(sx)),
+           "quantize_per_token")
+    return xq, sx
+
+
+def quantize_weight(W: np.ndarray, bits: int = 8, group_size: int = 0):
+    """W float32 [N, K] -> (w_q, s_w).
+
+    bits 8: w_q int8 [N, K]; bits 4: w_q uint8 [N, K/2] (even k in low nibble).
+    s_w float32 [N] (group_size 0) or [N, K/group_size].
+    """
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    wq = np.empty((N, K) if bits == 8 else (N, K // 2), np.int8 if bits == 8 else np.uint8)
+    sw = np.empty((N,) if group_size == 0 else (N, K // group_size), np.float32)
+    _check(_load().oracle_quantize_weight(_p(W), N, K, bits, group_size, _p(wq), _p(sw)),
+           "quantize_weight")
+    return wq, sw
+
+
+def unpack_int4(packed: np.ndarray, K: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    wq = np.empty((N, K), np.int8)
+    _check(_load().oracle_unpack_int4(_p(packed), N, K, _p(wq)), "unpack_int4")
+    return wq
+
+
+def gemm_i32(x_q: np.ndarray, w_q: np.ndarray):
+    """acc int32 [M, N] = x_q [M, K] . w_q [N, K]^T, exact."""
+    x_q = np.ascontiguousarray(x_q, dtype=np.int8)
+    w_q = np.ascontiguousarray(w_q, dtype=np.int8)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    assert w_q.shape[1] == K
+    acc = np.empty((M, N), np.int32)
+    _check(_load().oracle_gemm_i32(_p(x_q), _p(w_q), M, N, K, _p(acc)), "gemm_i32")
+    return acc
+
+
+def group_acc(x_q: np.ndarray, w_q: np.ndarray, group_size: int):
+    """acc_g int32 [M, N, G]: the integer product restricted to each K-group."""
+    x_q = np.ascontiguousarray(x_q, dtype=np.int8)
+    w_q = np.ascontiguousarray(w_q, dtype=np.int8)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    G = K // group_size
+    acc = np.empty((M, N, G), np.int32)
+    _check(_load().oracle_group_acc(_p(x_q), _p(w_q), M, N, K, group_size, _p(acc)), "group_acc")
+    return acc
+
+
+def dequant_pc(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray):
+    """fp64 y [M, N] = (acc * s_x[m]) * s_w[n]."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    M, N = acc.shape
+    y = np.empty((M, N), np.float64)
+    _check(_load().oracle_dequant_pc(_p(acc), _p(s_x), _p(s_w), M, N, _p(y)), "dequant_pc")
+    return y
+
+
+def dequant_pg(acc_g: np.ndarray, s_x: np.ndarray, s_w: np.ndarray):
+    """fp64 (y, mag) [M, N]: y = s_x * sum_g s_w[n,g] * acc_g; mag = sum of |terms|."""
+    acc_g = np.ascontiguousarray(acc_g, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    M, N, G = acc_g.shape
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    _check(_load().oracle_dequant_pg(_p(acc_g), _p(s_x), _p(s_w), M, N, G, _p(y), _p(mag)),
+           "dequant_pg")
+    return y, mag
+
+
+# ---- whole-path conveniences (the steps above, in the pages' order) --------------------
+
+def linear_pc(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray):
+    """Per-channel W8A8 linear: quantize x per token, int GEMM, dequant.
+
+    Returns dict with x_q, s_x, acc (int32) and y (fp64).
+    """
+    x_q, s_x = quantize_per_token(x)
+    acc = gemm_i32(x_q, w_q)
+    return {"x_q": x_q, "s_x": s_x, "acc": acc, "y": dequant_pc(acc, s_x, s_w)}
+
+
+def linear_pg(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int):
+    """Per-group W8A8 linear. Returns x_q, s_x, acc (sum of group accumulators), y, mag."""
+    x_q, s_x = quantize_per_token(x)
+    acc_g = group_acc(x_q, w_q, group_size)
+    y, mag = dequant_pg(acc_g, s_x, s_w)
+    acc = acc_g.astype(np.int64).sum(axis=2).astype(np.int32)
+    return {"x_q": x_q, "s_x": s_x, "acc": acc, "acc_g": acc_g, "y": y, "mag": mag}
+
+
+def linear_w4(x: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray, group_size: int):
+    """W4A8 per-group linear: unpack the int4 codes, then the per-group path."""
+    K = x.shape[1]
+    return linear_pg(x, unpack_int4(w_packed, K), s_w, group_size)

@@ -1,0 +1,267 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the fused
+ * per-token-quantize -> int8 GEMM -> dequant linear layer (W8A8 / W4A8).
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this file's library. It shares no code, header,
+ * table or helper with the GPU library, and includes nothing from it.
+ *
+ * Sources (page title and section; the pages are about the "Cider" project):
+ *  [P2] "在Mac上跑大模型，MLX 不是终点" (juejin.cn), section "W8A8 对称量化：Cider 的选择":
+ *       per-token symmetric scale = max|x| / 127, x_int8 = round(x / scale) clamped
+ *       to [-128, 127]; output = (x_int8 . w_int8) * scale_x * scale_w.
+ *       Section "INT8 TensorOps 内核设计": int8 x int8 products accumulate in int32.
+ *       Section "三种量化粒度的实现": per-channel = one weight scale per output
+ *       channel; per-group = one scale per 64 or 128 elements, dequant becomes a
+ *       segmented multiplication.
+ *  [P5] Cider README (gitea mirror), section "量化" (quantization table):
+ *       weights symmetric INT8 per-channel or per-group (gs = 64/128); W4A8 weights
+ *       symmetric INT4 with zero point 8 packed in uint8 (section "模式");
+ *       activations symmetric INT8 per token; INT32 accumulation;
+ *       output C = C_int32 * s_act * s_weight. Section "说明": weight scales use
+ *       the plain min-max method by default.
+ *
+ * Readings taken where the pages are silent (each is listed with its reason in
+ * the design notes of this repository):
+ *  - "round" is IEEE round-half-to-even of the correctly rounded fp32 quotient
+ *    x / scale (a true fp32 division, not a multiply by 1/scale);
+ *  - scales are fp32; scale = max / 127 is one correctly rounded fp32 division;
+ *  - a run whose scale is 0 (all-zero row or group) gets scale 0 and codes 0;
+ *  - int4: scale = max / 7, codes clamped to [-8, 7], stored as u = q + 8,
+ *    two per byte, even k in the low nibble;
+ *  - the int8 GEMM is exact integer arithmetic (accumulated here in int64 and
+ *    checked to fit in int32);
+ *  - dequantization is evaluated in fp64 (the exact value to within fp64
+ *    rounding); per-channel as (acc * s_x) * s_w, per-group as
+ *    s_x * sum_g s_w[n,g] * acc_g with acc_g the int32 sum over group g.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
+ * Parallelism: an OpenMP "parallel for" over independent rows only.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_OVERFLOW 2
+
+/* IEEE binary16 bit pattern -> float, exactly (every half is a float). */
+static float half_to_float(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u;
+    uint32_t expo = (uint32_t)(h >> 10) & 0x1Fu;
+    uint32_t mant = (uint32_t)h & 0x3FFu;
+    float mag;
+    if (expo == 0) {
+        /* zero or subnormal: mant * 2^-24 */
+        mag = ldexpf((float)mant, -24);
+    } else if (expo == 31) {
+        mag = mant ? NAN : INFINITY;
+    } else {
+        /* (1024 + mant) * 2^(expo - 15 - 10) */
+        mag = ldexpf((float)(1024u + mant), (int)expo - 25);
+    }
+    return sign ? -mag : mag;
+}
+
+/* bfloat16 bit pattern -> float: the upper 16 bits of a binary32. */
+static float bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/*
+ * Symmetric quantization of one run of n values (a token row, a weight row or
+ * a weight group) [P2 "W8A8 对称量化"; P5 "量化"]:
+ *   a = max |v|;  s = a / qdiv  (fp32 division);
+ *   q = clamp(rint(v / s), lo, hi)  (fp32 division, round half to even).
+ * Returns s. A zero scale gives all-zero codes.
+ */
+static float quantize_run(const float *v, int64_t n, float qdiv, int lo, int hi, int8_t *q)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float m = fabsf(v[i]);
+        if (m > a) a = m;
+    }
+    float s = a / qdiv;
+    for (int64_t i = 0; i < n; ++i) {
+        if (s == 0.0f) {
+            q[i] = 0;
+            continue;
+        }
+        float t = v[i] / s;
+        float r = rintf(t); /* default rounding mode: nearest, ties to even */
+        if (r < (float)lo) r = (float)lo;
+        if (r > (float)hi) r = (float)hi;
+        q[i] = (int8_t)r;
+    }
+    return s;
+}
+
+/*
+ * Per-token activation quantization [P2 "W8A8 对称量化"; P5 "Metal Kernel 流水线",
+ * step quantize_per_token]. x: M rows of K half (or bf16) values with row
+ * stride ldx elements. Outputs x_q int8 [M, K] (row stride K) and s_x [M].
+ */
+int oracle_quantize_per_token(const uint16_t *x, int x_is_bf16, int64_t M, int64_t K,
+                              int64_t ldx, int8_t *x_q, float *s_x)
+{
+    if (M < 0 || K <= 0 || ldx < K) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float row[K];
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t bits = x[m * ldx + k];
+            row[k] = x_is_bf16 ? bf16_to_float(bits) : half_to_float(bits);
+        }
+        s_x[m] = quantize_run(row, K, 127.0f, -128, 127, x_q + m * K);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Offline weight quantization, min-max [P5 "说明", "量化", "模式"; P2
+ * "三种量化粒度的实现"]. W fp32 [N, K] row-major (row n = output channel n).
+ *  bits 8, group_size 0    : s_w [N],        w_q int8 [N, K]
+ *  bits 8, group_size g>0  : s_w [N, K/g],   w_q int8 [N, K]   (groups along K)
+ *  bits 4, group_size g>0  : s_w [N, K/g],   w_q uint8 [N, K/2]; u = q + 8,
+ *                            byte j = u[2j] | u[2j+1] << 4 (even k low nibble)
+ */
+int oracle_quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_size,
+                           void *w_q, float *s_w)
+{
+    if (N < 0 || K <= 0) return ORACLE_BAD_ARG;
+    if (bits != 8 && bits != 4) return ORACLE_BAD_ARG;
+    if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return ORACLE_BAD_ARG;
+    if (bits == 4 && (group_size == 0 || group_size % 2 != 0)) return ORACLE_BAD_ARG;
+    const int64_t run = group_size ? group_size : K;
+    const int64_t G = K / run;
+    const float qdiv = bits == 8 ? 127.0f : 7.0f;
+    const int lo = bits == 8 ? -128 : -8;
+    const int hi = bits == 8 ? 127 : 7;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        int8_t codes[K];
+        for (int64_t g = 0; g < G; ++g)
+            s_w[n * G + g] = quantize_run(W + n * K + g * run, run, qdiv, lo, hi, codes + g * run);
+        if (bits == 8) {
+            memcpy((int8_t *)w_q + n * K, codes, (size_t)K);
+        } else {
+            uint8_t *dst = (uint8_t *)w_q + n * (K / 2);
+            for (int64_t j = 0; j < K / 2; ++j) {
+                unsigned lo_u = (unsigned)(codes[2 * j] + 8);
+                unsigned hi_u = (unsigned)(codes[2 * j + 1] + 8);
+                dst[j] = (uint8_t)(lo_u | (hi_u << 4));
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* int4 packed [N, K/2] -> int8 codes [N, K]: q[2j] = low nibble - 8, q[2j+1] = high - 8. */
+int oracle_unpack_int4(const uint8_t *packed, int64_t N, int64_t K, int8_t *w_q)
+{
+    if (N < 0 || K <= 0 || K % 2 != 0) return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < K / 2; ++j) {
+            uint8_t b = packed[n * (K / 2) + j];
+            w_q[n * K + 2 * j] = (int8_t)((int)(b & 0x0F) - 8);
+            w_q[n * K + 2 * j + 1] = (int8_t)((int)(b >> 4) - 8);
+        }
+    return ORACLE_OK;
+}
+
+/*
+ * Integer GEMM [P2 "INT8 TensorOps 内核设计"; P5 "量化" accumulation INT32]:
+ *   acc[m, n] = sum_k x_q[m, k] * w_q[n, k]
+ * over columns [k0, k0 + kn) (k0 = 0, kn = K for the full product; a group
+ * for the per-group path). Exact: int64 accumulation, then checked against
+ * the int32 range. Returns ORACLE_OVERFLOW if any sum leaves int32.
+ */
+static int gemm_i32_range(const int8_t *x_q, const int8_t *w_q, int64_t M, int64_t N,
+                          int64_t K, int64_t k0, int64_t kn, int32_t *acc, int64_t acc_stride)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t sum = 0;
+            for (int64_t k = k0; k < k0 + kn; ++k)
+                sum += (int64_t)x_q[m * K + k] * (int64_t)w_q[n * K + k];
+            if (sum > INT32_MAX || sum < INT32_MIN) bad = 1;
+            acc[(m * N + n) * acc_stride] = (int32_t)sum;
+        }
+    }
+    return bad ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+int oracle_gemm_i32(const int8_t *x_q, const int8_t *w_q, int64_t M, int64_t N, int64_t K,
+                    int32_t *acc)
+{
+    if (M < 0 || N < 0 || K <= 0) return ORACLE_BAD_ARG;
+    return gemm_i32_range(x_q, w_q, M, N, K, 0, K, acc, 1);
+}
+
+/*
+ * Group accumulators acc_g[m, n, g] = sum over k in [g*gs, (g+1)*gs) of
+ * x_q[m, k] * w_q[n, k]. Layout [M, N, G].
+ */
+int oracle_group_acc(const int8_t *x_q, const int8_t *w_q, int64_t M, int64_t N, int64_t K,
+                     int group_size, int32_t *acc_g)
+{
+    if (M < 0 || N < 0 || K <= 0 || group_size <= 0 || K % group_size != 0) return ORACLE_BAD_ARG;
+    const int64_t G = K / group_size;
+    int rc = ORACLE_OK;
+    for (int64_t g = 0; g < G; ++g) {
+        int r = gemm_i32_range(x_q, w_q, M, N, K, g * group_size, group_size, acc_g + g, G);
+        if (r != ORACLE_OK) rc = r;
+    }
+    return rc;
+}
+
+/*
+ * Per-channel dequant [P2 "W8A8 对称量化"; P5 "量化" C = C_int32 * s_act * s_weight],
+ * evaluated left to right in fp64: y[m, n] = (acc[m, n] * s_x[m]) * s_w[n].
+ */
+int oracle_dequant_pc(const int32_t *acc, const float *s_x, const float *s_w, int64_t M,
+                      int64_t N, double *y)
+{
+    if (M < 0 || N < 0) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = ((double)acc[m * N + n] * (double)s_x[m]) * (double)s_w[n];
+    return ORACLE_OK;
+}
+
+/*
+ * Per-group dequant [P2 "三种量化粒度的实现": each group has its own weight scale,
+ * so dequant is a segmented multiplication]:
+ *   y[m, n] = s_x[m] * sum_g s_w[n, g] * acc_g[m, n, g]      (fp64)
+ * Also returns mag[m, n] = |s_x[m]| * sum_g |s_w[n, g] * acc_g| (the size of the
+ * terms being summed; an fp32 evaluation of the sum can only be trusted
+ * relative to this, not to |y|, when terms cancel).
+ */
+int oracle_dequant_pg(const int32_t *acc_g, const float *s_x, const float *s_w, int64_t M,
+                      int64_t N, int64_t G, double *y, double *mag)
+{
+    if (M < 0 || N < 0 || G <= 0) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double t = 0.0, a = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double term = (double)s_w[n * G + g] * (double)acc_g[(m * N + n) * G + g];
+                t += term;
+                a += fabs(term);
+            }
+            y[m * N + n] = (double)s_x[m] * t;
+            if (mag) mag[m * N + n] = fabs((double)s_x[m]) * a;
+        }
+    return ORACLE_OK;
+}

@@ -1,0 +1,313 @@
+"""Pins for the CPU oracle: checks it against what the pages and mathematics fix.
+
+None of these tests re-derives a value with the oracle's own code path. They use
+hand-worked fixtures (tests/golden/), exact rational arithmetic with an
+independent correctly-rounded fp32 routine, closed-form invariants, brute force
+on tiny inputs and independent library routines (numpy int64/fp64 matmul).
+
+Which plausible oracle mistake each group of pins catches:
+  * wrong divisor (not 127 / 7), reciprocal-multiply instead of division,
+    round-half-away instead of half-even, missing clamp  -> golden rows, exact
+    rational brute force, exhaustive max -> +-127;
+  * dropped or transposed GEMM operand, wrong index     -> brute-force loops,
+    numpy int64 matmul on non-square shapes, golden linear;
+  * wrong dequant factor / order                         -> golden linear, exact
+    rational dequant, fake-quant identity;
+  * wrong group boundaries or scale indexing             -> per-group scales vs
+    per-slice brute force, gs = K equals per-channel;
+  * nibble order or offset in int4 packing               -> golden w4 bytes.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---- an independent, exact model of IEEE binary32 round-to-nearest-even ----------------
+
+def round_to_f32(fr: Fraction) -> Fraction:
+    """Correctly round a rational to the nearest binary32 value, ties to even."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    q_exp = max(e - 23, -149)  # 24-bit significand; subnormal quantum 2^-149
+    scaled = a / Fraction(2) ** q_exp
+    n, rem = divmod(scaled.numerator, scaled.denominator)
+    rem = Fraction(rem, scaled.denominator)
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * Fraction(n) * Fraction(2) ** q_exp
+
+
+def exact_quantize(values, qdiv=127, lo=-128, hi=127):
+    """Quantize one run with exact arithmetic + correct fp32 rounding of each step."""
+    a = max((abs(Fraction(float(v))) for v in values), default=Fraction(0))
+    s = round_to_f32(a / qdiv)
+    codes = []
+    for v in values:
+        if s == 0:
+            codes.append(0)
+            continue
+        t = round_to_f32(Fraction(float(v)) / s)
+        q = round(t)  # Python's round on a Fraction: nearest, ties to even
+        codes.append(int(min(max(q, lo), hi)))
+    return float(s), codes
+
+
+# ---- activation quantization -------------------------------------------------------------
+
+def test_golden_quantize_rows():
+    for case in _golden("quantize_rows.json")["cases"]:
+        x = np.array([case["x"]], np.float16)
+        q, s = oracle.quantize_per_token(x)
+        assert s[0] == np.float32(case["scale"]), case["why"]
+        assert q[0].tolist() == case["codes"], case["why"]
+
+
+def test_exhaustive_fp16_max_maps_to_127():
+    """Every positive finite fp16 maximum a: codes of [a, -a] are [127, -127] and
+    the scale equals the correctly rounded a/127 (so -128 is never produced)."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)  # all positive finite halves
+    a = bits.view(np.float16)
+    x = np.stack([a, -a, (a / 3).astype(np.float16)], axis=1)
+    q, s = oracle.quantize_per_token(x)
+    assert (q[:, 0] == 127).all() and (q[:, 1] == -127).all()
+    assert (np.abs(q[:, 2]) <= 127).all()
+    # scale against exact rational rounding on an evenly spaced subset (all 31743 is slow)
+    for i in range(0, len(a), 97):
+        assert Fraction(float(s[i])) == round_to_f32(Fraction(float(a[i])) / 127)
+
+
+def test_exact_rational_brute_force_rows():
+    rng = np.random.default_rng(1)
+    rows = []
+    for r in range(40):
+        v = rng.standard_normal(48).astype(np.float32)
+        v[rng.integers(0, 48, 2)] *= 50
+        if r % 5 == 1:
+            v *= 1e-3  # small magnitudes
+        if r % 5 == 2:
+            v[:] = np.ldexp(rng.integers(-20, 21, 48), -24).astype(np.float32)  # subnormals
+        rows.append(v.astype(np.float16))
+    x = np.stack(rows)
+    q, s = oracle.quantize_per_token(x)
+    for i in range(x.shape[0]):
+        es, ec = exact_quantize(x[i])
+        assert float(s[i]) == es
+        assert q[i].tolist() == ec
+
+
+def test_quantize_invariants():
+    rng = np.random.default_rng(2)
+    # values in [2^-6, 2^6] so that scaling by 2^j, |j| <= 4, stays exact in fp16
+    mag = np.ldexp(1.0 + rng.random((16, 64)), rng.integers(-6, 6, (16, 64)))
+    x = (mag * rng.choice([-1.0, 1.0], (16, 64))).astype(np.float16)
+    q, s = oracle.quantize_per_token(x)
+    for j in (-4, -1, 1, 3):
+        qj, sj = oracle.quantize_per_token((x.astype(np.float32) * 2.0 ** j).astype(np.float16))
+        assert (qj == q).all()
+        assert (sj == s * np.float32(2.0 ** j)).all()
+    qn, sn = oracle.quantize_per_token(-x)
+    assert (qn == -q).all() and (sn == s).all()
+    # reconstruction error: |x - s q| <= s (1/2 + 2^-17), checked exactly
+    for i in range(x.shape[0]):
+        si = Fraction(float(s[i]))
+        for k in range(x.shape[1]):
+            err = abs(Fraction(float(x[i, k])) - si * int(q[i, k]))
+            assert err <= si * (Fraction(1, 2) + Fraction(1, 2 ** 17))
+
+
+def test_zero_and_degenerate_rows():
+    x = np.zeros((3, 64), np.float16)
+    x[1, 5] = -0.0
+    x[2, 7] = np.float16(2.0 ** -24)  # smallest subnormal as the only nonzero
+    q, s = oracle.quantize_per_token(x)
+    assert s[0] == 0 and s[1] == 0 and (q[:2] == 0).all()
+    assert q[2, 7] == 127 and (np.delete(q[2], 7) == 0).all()
+    # empty batch
+    q0, s0 = oracle.quantize_per_token(np.zeros((0, 64), np.float16))
+    assert q0.shape == (0, 64) and s0.shape == (0,)
+
+
+def test_bf16_input_matches_exact():
+    rng = np.random.default_rng(3)
+    f = rng.standard_normal((8, 32)).astype(np.float32) * 10
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)  # truncate to bf16 (any bf16 values do)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    q, s = oracle.quantize_per_token_bf16(bits)
+    for i in range(8):
+        es, ec = exact_quantize(vals[i])
+        assert float(s[i]) == es and q[i].tolist() == ec
+
+
+# ---- weight quantization -----------------------------------------------------------------
+
+@pytest.mark.parametrize("gs", [0, 64, 128])
+def test_weight_quantize_against_exact_slices(gs):
+    rng = np.random.default_rng(4)
+    K = 256
+    W = (rng.standard_normal((6, K)) * 0.02).astype(np.float32)
+    W[2, 70] = 0.5  # one large weight affects only its own group
+    W[3, 128:192] = 0.0  # an all-zero group
+    wq, sw = oracle.quantize_weight(W, 8, gs)
+    run = gs or K
+    for n in range(6):
+        for g in range(K // run):
+            es, ec = exact_quantize(W[n, g * run:(g + 1) * run])
+            got_s = sw[n] if gs == 0 else sw[n, g]
+            assert float(got_s) == es
+            assert wq[n, g * run:(g + 1) * run].tolist() == ec
+
+
+def test_golden_w4_pack():
+    d = _golden("w4_pack.json")
+    W = np.array(d["W"], np.float32)
+    packed, s = oracle.quantize_weight(W, 4, d["group_size"])
+    assert s.tolist() == d["scale"]
+    assert packed.tolist() == d["packed"]
+    assert oracle.unpack_int4(packed, W.shape[1]).tolist() == d["codes"]
+
+
+def test_w4_against_exact_and_range():
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((5, 256)) * 0.02).astype(np.float32)
+    packed, sw = oracle.quantize_weight(W, 4, 128)
+    codes = oracle.unpack_int4(packed, 256)
+    assert codes.min() >= -7 and codes.max() <= 7  # -8 unreachable: max maps to +-7
+    for n in range(5):
+        for g in range(2):
+            es, ec = exact_quantize(W[n, g * 128:(g + 1) * 128], qdiv=7, lo=-8, hi=7)
+            assert float(sw[n, g]) == es
+            assert codes[n, g * 128:(g + 1) * 128].tolist() == ec
+    # nibble arithmetic: unpack inverts the documented packing for every code pair
+    q = np.array([[a, b] for a in range(-8, 8) for b in range(-8, 8)], np.int8).reshape(1, -1)
+    byte = ((q[0, 0::2].astype(np.int32) + 8) | ((q[0, 1::2].astype(np.int32) + 8) << 4)).astype(np.uint8)
+    assert (oracle.unpack_int4(byte.reshape(1, -1), q.shape[1]) == q).all()
+
+
+# ---- integer GEMM ------------------------------------------------------------------------
+
+def test_gemm_brute_force_tiny():
+    rng = np.random.default_rng(6)
+    xq = rng.integers(-128, 128, (3, 64), dtype=np.int8)
+    wq = rng.integers(-128, 128, (5, 64), dtype=np.int8)
+    acc = oracle.gemm_i32(xq, wq)
+    for m in range(3):
+        for n in range(5):
+            assert acc[m, n] == sum(int(xq[m, k]) * int(wq[n, k]) for k in range(64))
+
+
+def test_gemm_vs_numpy_int64():
+    rng = np.random.default_rng(7)
+    xq = rng.integers(-127, 128, (37, 320), dtype=np.int8)
+    wq = rng.integers(-127, 128, (53, 320), dtype=np.int8)
+    ref = xq.astype(np.int64) @ wq.astype(np.int64).T
+    assert (oracle.gemm_i32(xq, wq) == ref).all()
+
+
+def test_gemm_overflow_is_detected():
+    K = 140000  # 128*128*K > 2^31
+    xq = np.full((1, K), -128, np.int8)
+    wq = np.full((1, K), -128, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(xq, wq)
+
+
+def test_group_acc_sums_to_full():
+    rng = np.random.default_rng(8)
+    xq = rng.integers(-127, 128, (9, 256), dtype=np.int8)
+    wq = rng.integers(-127, 128, (11, 256), dtype=np.int8)
+    accg = oracle.group_acc(xq, wq, 64)
+    for g in range(4):
+        ref = xq[:, g * 64:(g + 1) * 64].astype(np.int64) @ wq[:, g * 64:(g + 1) * 64].astype(np.int64).T
+        assert (accg[:, :, g] == ref).all()
+
+
+# ---- dequantization ----------------------------------------------------------------------
+
+def test_golden_linear():
+    d = _golden("linear_small.json")
+    x = np.array(d["x"], np.float16)
+    W = np.array(d["W"], np.float32)
+    wq, sw = oracle.quantize_weight(W, 8, 0)
+    assert wq.tolist() == d["w_codes"] and sw.tolist() == d["w_scale"]
+    r = oracle.linear_pc(x, wq, sw)
+    assert r["x_q"].tolist() == d["x_codes"] and r["s_x"].tolist() == d["x_scale"]
+    assert r["acc"].tolist() == d["acc"]
+    assert r["y"].tolist() == d["y"]
+
+
+def test_dequant_pc_exact_rational():
+    rng = np.random.default_rng(9)
+    acc = rng.integers(-2 ** 26, 2 ** 26, (7, 9)).astype(np.int32)
+    sx = (rng.random(7) * 2).astype(np.float32)
+    sw = (rng.random(9) * 1e-3).astype(np.float32)
+    y = oracle.dequant_pc(acc, sx, sw)
+    for m in range(7):
+        for n in range(9):
+            exact = Fraction(int(acc[m, n])) * Fraction(float(sx[m])) * Fraction(float(sw[n]))
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 51)
+
+
+def test_dequant_pg_exact_rational_and_mag():
+    rng = np.random.default_rng(10)
+    G = 5
+    accg = rng.integers(-2 ** 20, 2 ** 20, (4, 6, G)).astype(np.int32)
+    sx = (rng.random(4) + 0.1).astype(np.float32)
+    sw = (rng.random((6, G)) * 1e-3).astype(np.float32)
+    y, mag = oracle.dequant_pg(accg, sx, sw)
+    for m in range(4):
+        for n in range(6):
+            terms = [Fraction(float(sw[n, g])) * int(accg[m, n, g]) for g in range(G)]
+            exact = Fraction(float(sx[m])) * sum(terms)
+            amag = Fraction(float(sx[m])) * sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y[m, n])) - exact) <= amag * (G + 2) * Fraction(1, 2 ** 53)
+            assert abs(Fraction(float(mag[m, n])) - amag) <= amag * (G + 2) * Fraction(1, 2 ** 53)
+
+
+def test_pg_with_one_group_equals_pc_and_fake_quant_identity():
+    rng = np.random.default_rng(11)
+    M, N, K = 20, 24, 256
+    x = (rng.standard_normal((M, K)) * 3).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq, sw = oracle.quantize_weight(W, 8, 0)
+    wq1, sw1 = oracle.quantize_weight(W, 8, K)
+    assert (wq1 == wq).all() and (sw1[:, 0] == sw).all()
+    pc = oracle.linear_pc(x, wq, sw)
+    pg = oracle.linear_pg(x, wq1, sw1, K)
+    assert (pg["acc"] == pc["acc"]).all()
+    np.testing.assert_allclose(pg["y"], pc["y"], rtol=1e-15, atol=0)
+    # fake-quant identity: y = (s_x x_q)(s_w w_q)^T, in an independent fp64 matmul
+    fq = (pc["s_x"][:, None].astype(np.float64) * pc["x_q"]) @ (sw[:, None].astype(np.float64) * wq).T
+    np.testing.assert_allclose(pc["y"], fq, rtol=1e-12, atol=1e-12)
+    # per-group fake-quant identity at gs = 64
+    wq64, sw64 = oracle.quantize_weight(W, 8, 64)
+    r = oracle.linear_pg(x, wq64, sw64, 64)
+    wdq = (np.repeat(sw64, 64, axis=1).astype(np.float64) * wq64)
+    fq64 = (r["s_x"][:, None].astype(np.float64) * r["x_q"]) @ wdq.T
+    np.testing.assert_allclose(r["y"], fq64, rtol=1e-12, atol=1e-12)
+
+
+def test_w4_path_equals_pg_on_unpacked_codes():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((5, 256)).astype(np.float16)
+    W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    packed, sw = oracle.quantize_weight(W, 4, 128)
+    r4 = oracle.linear_w4(x, packed, sw, 128)
+    r8 = oracle.linear_pg(x, oracle.unpack_int4(packed, 256), sw, 128)
+    assert (r4["acc"] == r8["acc"]).all() and (r4["y"] == r8["y"]).all()
