@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused quantize -> int8 GEMM -> dequant linear layer on one MI355X.
+
+One step = one pass of the hot path over one batch: per-token activation
+quantization (fp16 x -> int8 x_q + fp32 s_x) followed by the int8 GEMM with the
+per-channel dequantization fused into its store (fp16 y). Workload: M=4096 tokens,
+N=10240 output channels, K=2560 input channels, seeded synthetic inputs (weights
+quantized once, offline, outside the timed region). Inputs are resident in HBM
+before timing starts.
+
+Prints ONE JSON line: metric/value (INT8 TOPS = 2*M*N*K / step time), a roofline
+object for the dominant kernel (the GEMM, timed with HIP events on its stream over
+the timed region) and a cpu_baseline object (the CPU oracle timed on a bounded
+sample of the same workload on the host cores).
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+       [--workload pc|pg64|pg128|w4|m1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0    # MI355X HBM3E, 8 TB/s
+
+# name -> (M, N, K, weight bits, group size)
+WORKLOADS = {
+    "pc": (4096, 10240, 2560, 8, 0),
+    "pg128": (4096, 10240, 2560, 8, 128),
+    "pg64": (4096, 10240, 2560, 8, 64),
+    "w4": (4096, 10240, 2560, 4, 128),
+    "m1": (1, 10240, 2560, 8, 0),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, W, bits, gs, budget_s):
+    """Time the CPU oracle on a bounded row sample of the same workload."""
+    import oracle
+
+    oracle.build(force=False)
+    N, K = W.shape
+    if bits == 8:
+        wq, sw = oracle.quantize_weight(W, 8, gs)
+    else:
+        wq, sw = oracle.quantize_weight(W, 4, gs)
+    rows_done, chunk = 0, 64
+    t0 = time.perf_counter()
+    while rows_done < x.shape[0]:
+        xs = x[rows_done:rows_done + chunk]
+        if bits == 4:
+            oracle.linear_w4(xs, wq, sw, gs)
+        elif gs:
+            oracle.linear_pg(xs, wq, sw, gs)
+        else:
+            oracle.linear_pc(xs, wq, sw)
+        rows_done += xs.shape[0]
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows_done * N * K
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows_done} of {x.shape[0]} token rows (full N={N}, K={K}); "
+                      f"per-token quantize + int GEMM + fp64 dequant; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; see the sharding notes in the design document)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import w8a8_activation_quantized_amd as w8a8
+    from synth_inputs import linear_inputs
+
+    if not torch.cuda.is_available() or not w8a8.w8a8_is_available(0):
+        print("no gfx950 GPU available: " + w8a8.w8a8_last_error(), file=sys.stderr)
+        return 1
+
+    M, N, K, bits, gs = WORKLOADS[args.workload]
+    x_np, W_np = linear_inputs(M, N, K, seed=0)
+    x = torch.from_numpy(x_np).cuda()
+    Wd = torch.from_numpy(W_np).cuda()
+    wq, sw = w8a8.quantize_weight(Wd, bits, gs)  # offline: not timed
+    del Wd
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    if bits == 4:
+        def gemm():
+            w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, y=y, stream=stream)
+    elif gs:
+        def gemm():
+            w8a8.w8a8_gemm_pg(xq, sx, wq, sw, gs, y=y, stream=stream)
+    else:
+        def gemm():
+            w8a8.w8a8_gemm_pc(xq, sx, wq, sw, y=y, stream=stream)
+
+    def step(ev=None):
+        w8a8.quantize_per_token(x, xq, sx, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        gemm()
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    ops = 2.0 * M * N * K
+    value = ops / (ms_per_step * 1e-3) / 1e12
+
+    if M == 1:
+        wbytes = N * K * bits // 8 + sw.numel() * 4
+        alg_bytes = wbytes + K * 1 + 4 + N * 2  # weights + scales, x_q + s_x in, y out
+        achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    else:
+        achieved = ops / (gemm_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                    "frac": achieved / PEAK_INT8_TOPS, "traffic": None}
+
+    result = {
+        "metric": f"INT8 TOPS & % MFMA peak of fused quant-GEMM-dequant, M={M} N={N} K={K}",
+        "value": value,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"w8a8 linear ({args.workload}): per-token quantize + int8 GEMM + fused dequant",
+                   "M": M, "N": N, "K": K, "weight_bits": bits, "group_size": gs, "out": "fp16",
+                   "parallelism": "single GPU"},
+        "frac_of_peak_step": value / PEAK_INT8_TOPS,
+        "gemm_ms": gemm_ms,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x_np, W_np, bits, gs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

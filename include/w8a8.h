@@ -1,0 +1,150 @@
+/*
+ * w8a8.h -- C ABI of libw8a8: fused per-token activation quantization, int8 GEMM
+ * and dequantization (W8A8 / W4A8 linear layers) for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Cider project pages):
+ *  - juejin post "在Mac上跑大模型，MLX 不是终点", section "W8A8 对称量化：Cider 的选择":
+ *    per-token symmetric scale s_x = max|x| / 127, x_q = round(x / s_x) clamped to
+ *    [-128, 127]; y = (x_q . w_q) * s_x * s_w, dequantization fused into the GEMM store.
+ *  - same post, "INT8 TensorOps 内核设计": int8 x int8 products accumulate in int32;
+ *    "三种量化粒度的实现": weight scales per output channel, or per group of 64/128
+ *    elements along K (a segmented multiplication).
+ *  - Cider README, sections "模式" and "量化": W4A8 weights are symmetric int4 with
+ *    zero point 8, packed two per uint8; "Metal Kernel 流水线": quantize_per_token
+ *    then the fused int8 matmul with dequantization; for W4A8 the int4 -> int8
+ *    unpack happens inside the GEMM's operand load.
+ *
+ * Rounding: "round" is read as IEEE round-half-to-even of the correctly rounded
+ * fp32 quotient x / s (a true fp32 division). A row or group whose max is 0 has
+ * scale 0 and all-zero codes.
+ *
+ * Conventions for every entry point below:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates and frees nothing and keeps no per-call state (reentrant).
+ *  - All tensors are row-major with the last index contiguous. Base pointers must
+ *    be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream) on the current device.
+ *    Calls enqueue work and return; results are valid once the caller has
+ *    synchronized with the stream.
+ *  - Arguments are validated on the host BEFORE anything is enqueued; on any
+ *    non-OK return nothing was enqueued (except W8A8_ERR_HIP, where the launch
+ *    itself failed). w8a8_last_error() then gives a thread-local message.
+ *  - Device faults surface at the caller's next synchronization (HIP semantics).
+ *  - M = 0 (an empty batch) is valid and enqueues nothing.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8A8_OK = 0,
+    W8A8_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size/stride/alignment, bad enum */
+    W8A8_ERR_UNSUPPORTED_DEVICE = 2, /* no device, not gfx950, or W8A8_FORCE_UNAVAILABLE=1 */
+    W8A8_ERR_UNSUPPORTED_SHAPE = 3, /* shape outside the documented constraints */
+    W8A8_ERR_HIP = 4 /* a HIP runtime call or kernel launch failed */
+} w8a8_status;
+
+typedef enum {
+    W8A8_F16 = 0,
+    W8A8_BF16 = 1,
+    W8A8_F32 = 2,
+    W8A8_I32 = 3 /* GEMM output only: the raw int32 accumulator sum_k x_q*w_q (testing) */
+} w8a8_dtype;
+
+/* 1 iff `device` exists, is a gfx950 GPU, and W8A8_FORCE_UNAVAILABLE is not set to 1.
+ * Mirrors the pages' is_available() (README "条件编译"): callers fall back when 0. */
+int w8a8_is_available(int device);
+
+/* Static string for a status code. */
+const char *w8a8_status_string(int status);
+
+/* Thread-local detail for the last non-OK return on this thread ("" if none). */
+const char *w8a8_last_error(void);
+
+/* Library ABI version (increments on incompatible changes). */
+int w8a8_abi_version(void);
+
+/*
+ * quantize_per_token -- online per-token activation quantization
+ * (juejin post, "W8A8 对称量化：Cider 的选择"; README "Metal Kernel 流水线" step 1).
+ *   x       [M, K] fp16 or bf16 (x_dtype = W8A8_F16 | W8A8_BF16), row stride ldx elements
+ *   x_q     [M, K] int8 output, row stride K
+ *   s_x     [M]    fp32 output: s_x[m] = max_k |x[m,k]| / 127
+ * Codes: x_q = clamp(rne(x / s_x), -128, 127); 0 where s_x == 0.
+ * Constraints: M >= 0, K >= 8, K % 8 == 0, ldx >= K, ldx % 8 == 0. Inputs finite.
+ */
+int quantize_per_token(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                       int8_t *x_q, float *s_x, void *stream);
+
+/*
+ * quantize_weight -- offline min-max weight quantization (README "说明": min-max
+ * by default; "量化": symmetric int8 per channel / per group, int4 zero point 8).
+ *   W      [N, K] fp32 (row n = output channel n)
+ *   bits 8, group_size 0      : w_q int8 [N, K],        s_w [N]       = max_k |W[n,:]| / 127
+ *   bits 8, group_size 64|128 : w_q int8 [N, K],        s_w [N, K/gs] = max |W[n, group]| / 127
+ *   bits 4, group_size 64|128 : w_q uint8 [N, K/2],     s_w [N, K/gs] = max |W[n, group]| / 7
+ *       int4 codes q = clamp(rne(W / s), -8, 7) stored as u = q + 8, byte j of row n
+ *       = u[n, 2j] | u[n, 2j+1] << 4 (even k in the low nibble).
+ * Constraints: N >= 1, K >= 64, K % 64 == 0, K % group_size == 0. Inputs finite.
+ */
+int quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_size, void *w_q,
+                    float *s_w, void *stream);
+
+/*
+ * w8a8_gemm_pc -- int8 GEMM with per-channel dequant fused into the store
+ * (juejin post, "W8A8 对称量化" and "INT8 TensorOps 内核设计"; README "量化":
+ * C = C_int32 * s_act * s_weight).
+ *   x_q [M, K] int8, s_x [M] fp32, w_q [N, K] int8, s_w [N] fp32
+ *   y   [M, N] of y_dtype with row stride ldy elements:
+ *       acc = sum_k x_q[m,k] * w_q[n,k]  (exact int32)
+ *       y   = rne_out((fp32(acc) * s_x[m]) * s_w[n])       (fp32 arithmetic)
+ *       W8A8_I32 writes acc itself.
+ * Constraints: M >= 0, N >= 16, N % 16 == 0, K >= 64, K % 64 == 0, ldy >= N, ldy % 4 == 0.
+ */
+int w8a8_gemm_pc(const int8_t *x_q, const float *s_x, const int8_t *w_q, const float *s_w,
+                 void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                 void *stream);
+
+/*
+ * w8a8_gemm_pg -- int8 GEMM with per-group weight scales (juejin post
+ * "三种量化粒度的实现": each K-group has its own scale; dequant is segmented).
+ *   s_w [N, G] fp32 with G = K / group_size, group_size in {64, 128}
+ *   acc_g = sum over k in group g of x_q[m,k] * w_q[n,k]  (exact int32)
+ *   t = 0; for g = 0..G-1: t = fma(fp32(acc_g), s_w[n,g], t);  y = rne_out(t * s_x[m])
+ *   W8A8_I32 writes sum_g acc_g (= the full integer product).
+ * Constraints: as w8a8_gemm_pc, plus K % group_size == 0.
+ */
+int w8a8_gemm_pg(const int8_t *x_q, const float *s_x, const int8_t *w_q, const float *s_w,
+                 int group_size, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                 int64_t ldy, void *stream);
+
+/*
+ * w4a8_gemm_pg -- W4A8 GEMM: int4 weights packed two per byte, unpacked to int8
+ * inside the GEMM's weight-tile load (README "Metal Kernel 流水线", W4A8 note),
+ * then the per-group path of w8a8_gemm_pg on the codes q = u - 8.
+ *   w_packed [N, K/2] uint8 (layout of quantize_weight with bits = 4)
+ *   s_w      [N, K/group_size] fp32, group_size in {64, 128}
+ * Constraints: as w8a8_gemm_pg.
+ */
+int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, const float *s_w,
+                 int group_size, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                 int64_t ldy, void *stream);
+
+/*
+ * Debug knob: force the GEMM tile configuration (-1 = automatic choice by shape).
+ * Every configuration computes identical results; tests use this to run each one.
+ * Returns the number of configurations, or W8A8_ERR_INVALID_ARGUMENT (negated)
+ * for an unknown id. Process-wide.
+ */
+int w8a8_debug_force_config(int config_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,55 @@
+"""Shared helpers for the parity tests: tolerances derived from the arithmetic.
+
+Output tolerance (the reference value y64 is the oracle's fp64 dequantization):
+  * fp16 / bf16 outputs: |y - y64| <= 1 ulp of the output format at y64, plus the
+    worst-case error of an fp32 evaluation, (G + 2) * 2^-24 * mag, where mag is the
+    sum of the magnitudes of the terms (mag = |y64| for per-channel, G = 1).
+  * fp32 outputs: |y - y64| <= 1e-5 * max(|y64|, mag).
+Codes, scales and int32 accumulators are compared bit for bit.
+"""
+import numpy as np
+
+F16_MIN_NORMAL = 2.0 ** -14
+BF16_MIN_NORMAL = 2.0 ** -126
+
+
+def ulp(y64: np.ndarray, fmt: str) -> np.ndarray:
+    a = np.abs(y64)
+    if fmt == "f16":
+        e = np.floor(np.log2(np.maximum(a, F16_MIN_NORMAL)))
+        return np.exp2(e - 10)
+    if fmt == "bf16":
+        e = np.floor(np.log2(np.maximum(a, BF16_MIN_NORMAL)))
+        return np.exp2(e - 7)
+    raise ValueError(fmt)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_output(y_gpu: np.ndarray, fmt: str, y64: np.ndarray, mag: np.ndarray, G: int = 1,
+                 what: str = ""):
+    """y_gpu: float16 array (fmt f16), uint16 bf16 bits (fmt bf16) or float32 (fmt f32)."""
+    if fmt == "f16":
+        yg = y_gpu.astype(np.float64)
+    elif fmt == "bf16":
+        yg = bf16_bits_to_f64(y_gpu)
+    else:
+        yg = y_gpu.astype(np.float64)
+    err = np.abs(yg - y64)
+    if fmt == "f32":
+        tol = 1e-5 * np.maximum(np.abs(y64), mag)
+    else:
+        tol = ulp(y64, fmt) + (G + 2) * 2.0 ** -24 * mag
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance; first at {tuple(i)}: "
+            f"gpu={yg[tuple(i)]!r} ref={y64[tuple(i)]!r} tol={tol[tuple(i)]!r}")
+    if fmt == "f16":
+        # rounding mode: almost every output must equal the correctly rounded reference
+        exact = (y_gpu == y64.astype(np.float16)).mean()
+        assert exact >= 0.99, f"{what}: only {exact:.4f} of fp16 outputs are RNE(y64)"
+    return float(err.max()) if err.size else 0.0

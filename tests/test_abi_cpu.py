@@ -1,0 +1,135 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status codes BEFORE touching a device.
+
+No compute call is made here: every call either fails argument validation or runs
+with W8A8_FORCE_UNAVAILABLE=1, so nothing can be launched on any machine.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+OK, INVALID, UNSUPPORTED_DEVICE, UNSUPPORTED_SHAPE = 0, 1, 2, 3
+F16, BF16, F32, I32 = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def w8a8():
+    import w8a8_activation_quantized_amd as pkg
+    return pkg
+
+
+@pytest.fixture
+def unavailable(monkeypatch):
+    monkeypatch.setenv("W8A8_FORCE_UNAVAILABLE", "1")
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for required in ("quantize_per_token", "quantize_weight", "w8a8_gemm_pc", "w8a8_gemm_pg",
+                     "w4a8_gemm_pg", "w8a8_is_available", "w8a8_last_error", "w8a8_status_string"):
+        assert required in names, names
+
+
+def test_library_exports_every_declared_symbol(w8a8):
+    lib = ctypes.CDLL(w8a8.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libw8a8.so does not export {name}"
+
+
+def test_status_strings(w8a8):
+    lib = w8a8.lib()
+    assert lib.w8a8_status_string(OK) == b"ok"
+    assert lib.w8a8_status_string(INVALID) == b"invalid argument"
+    assert lib.w8a8_status_string(99) == b"unknown status"
+    assert lib.w8a8_abi_version() >= 1
+
+
+def test_forced_unavailable(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert lib.w8a8_is_available(0) == 0
+    rc = lib.w8a8_gemm_pc(FAKE, FAKE, FAKE, FAKE, FAKE, F16, 128, 256, 256, 256, None)
+    assert rc == UNSUPPORTED_DEVICE
+    assert b"W8A8_FORCE_UNAVAILABLE" in lib.w8a8_last_error()
+    rc = lib.quantize_per_token(FAKE, F16, 4, 64, 64, FAKE, FAKE, None)
+    assert rc == UNSUPPORTED_DEVICE
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (M, N, K, ldy, y_dtype)
+    ((-1, 256, 256, 256, F16), INVALID, "M"),
+    ((8, 250, 256, 256, F16), UNSUPPORTED_SHAPE, "N"),
+    ((8, 0, 256, 256, F16), UNSUPPORTED_SHAPE, "N"),
+    ((8, 256, 100, 256, F16), UNSUPPORTED_SHAPE, "K"),
+    ((8, 256, 0, 256, F16), UNSUPPORTED_SHAPE, "K"),
+    ((8, 256, 256, 255, F16), INVALID, "ldy"),
+    ((8, 256, 256, 128, F16), INVALID, "ldy"),
+    ((8, 256, 256, 256, 7), INVALID, "y_dtype"),
+])
+def test_gemm_pc_validation(w8a8, args, status, needle):
+    lib = w8a8.lib()
+    M, N, K, ldy, dt = args
+    rc = lib.w8a8_gemm_pc(FAKE, FAKE, FAKE, FAKE, FAKE, dt, M, N, K, ldy, None)
+    assert rc == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_gemm_null_and_misaligned_pointers(w8a8):
+    lib = w8a8.lib()
+    rc = lib.w8a8_gemm_pc(None, FAKE, FAKE, FAKE, FAKE, F16, 8, 256, 256, 256, None)
+    assert rc == INVALID and b"null" in lib.w8a8_last_error()
+    odd = ctypes.c_void_p(0x100004)
+    rc = lib.w8a8_gemm_pc(FAKE, FAKE, odd, FAKE, FAKE, F16, 8, 256, 256, 256, None)
+    assert rc == INVALID and b"aligned" in lib.w8a8_last_error()
+
+
+def test_group_size_validation(w8a8):
+    lib = w8a8.lib()
+    for gs in (0, 32, 96, 256):
+        rc = lib.w8a8_gemm_pg(FAKE, FAKE, FAKE, FAKE, gs, FAKE, F16, 8, 256, 256, 256, None)
+        assert rc == INVALID, gs
+        rc = lib.w4a8_gemm_pg(FAKE, FAKE, FAKE, FAKE, gs, FAKE, F16, 8, 256, 256, 256, None)
+        assert rc == INVALID, gs
+    rc = lib.w8a8_gemm_pg(FAKE, FAKE, FAKE, FAKE, 128, FAKE, F16, 8, 256, 192, 256, None)
+    assert rc == UNSUPPORTED_SHAPE  # K not a multiple of the group size
+
+
+def test_quantize_validation(w8a8):
+    lib = w8a8.lib()
+    assert lib.quantize_per_token(FAKE, F32, 4, 64, 64, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_per_token(FAKE, F16, 4, 60, 64, FAKE, FAKE, None) == UNSUPPORTED_SHAPE
+    assert lib.quantize_per_token(FAKE, F16, 4, 64, 60, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_per_token(FAKE, F16, 4, 64, 68, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_per_token(None, F16, 4, 64, 64, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_weight(FAKE, 16, 256, 3, 0, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_weight(FAKE, 16, 256, 4, 0, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_weight(FAKE, 16, 256, 8, 32, FAKE, FAKE, None) == INVALID
+    assert lib.quantize_weight(FAKE, 16, 200, 8, 0, FAKE, FAKE, None) == UNSUPPORTED_SHAPE
+    assert lib.quantize_weight(FAKE, 0, 256, 8, 0, FAKE, FAKE, None) == INVALID
+
+
+def test_debug_force_config_bounds(w8a8):
+    lib = w8a8.lib()
+    n = lib.w8a8_debug_force_config(-1)
+    assert n >= 1
+    assert lib.w8a8_debug_force_config(n) < 0
+    assert lib.w8a8_debug_force_config(-2) < 0
+    assert lib.w8a8_debug_force_config(-1) == n
+
+
+def test_binding_raises_on_bad_input(w8a8):
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        w8a8.quantize_per_token(x)

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: int8 codes, fp32 scales, int32 accumulators. Outputs: within the
+tolerance of tests/_parity.py (1 ulp for fp16/bf16, 1e-5 relative for fp32, plus
+the fp32 evaluation bound for per-group sums). Inputs come from synth_inputs (the
+same seeded generator for both sides); every expected value comes from the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth_inputs import linear_inputs, qwen3_8b_block_inputs, QWEN3_8B_BLOCK, QWEN3_8B_BLOCK_INPUTS
+from _parity import check_output
+
+pytestmark = pytest.mark.gpu
+
+OUT_FMT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def w8a8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w8a8_activation_quantized_amd as w
+    assert w.w8a8_is_available(0), w.w8a8_last_error()
+    w.w8a8_debug_force_config(-1)
+    return w
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def gpu_quantize(w8a8, x_np):
+    xq, sx = w8a8.quantize_per_token(dev(x_np))
+    torch.cuda.synchronize()
+    return host(xq), host(sx)
+
+
+# ---- activation quantization -----------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 2560), (3, 64), (65, 2560), (128, 2560), (300, 10240), (129, 4096),
+                                 (17, 12288), (5, 8), (7, 24), (2, 20000), (1000, 2560)])
+def test_quantize_per_token(w8a8, M, K):
+    note(f"quantize_per_token M={M} K={K}")
+    x, _ = linear_inputs(M, 16, K, seed=M * 7 + K)
+    xq, sx = gpu_quantize(w8a8, x)
+    rq, rs = oracle.quantize_per_token(x)
+    assert (sx.view(np.uint32) == rs.view(np.uint32)).all()
+    assert (xq == rq).all()
+
+
+def edge_rows(K=256):
+    rng = np.random.default_rng(99)
+    rows = [np.zeros(K), np.full(K, 3.0), np.full(K, -7.25), np.full(K, 65504.0),
+            np.where(np.arange(K) % 2 == 0, 65504.0, -65504.0),
+            np.ldexp(rng.integers(-1023, 1024, K).astype(np.float64), -24),  # subnormals
+            np.eye(1, K, 17)[0] * 1000.0,  # one-hot outlier
+            -np.abs(rng.standard_normal(K)),  # all negative
+            rng.standard_normal(K) * 1e-3]
+    ties = np.zeros(K)  # max 127 -> scale 1 exactly; half-integers are exact ties
+    ties[:8] = [127.0, 2.5, -2.5, 3.5, -3.5, 0.5, -0.5, 126.5]
+    ties[8:] = (rng.integers(-254, 255, K - 8) / 2.0)
+    rows.append(ties)
+    return np.stack(rows).astype(np.float16)
+
+
+def test_quantize_edge_rows(w8a8):
+    note("quantize edge rows")
+    x = edge_rows()
+    xq, sx = gpu_quantize(w8a8, x)
+    rq, rs = oracle.quantize_per_token(x)
+    assert (sx.view(np.uint32) == rs.view(np.uint32)).all()
+    assert (xq == rq).all()
+    assert sx[0] == 0 and (xq[0] == 0).all()
+    assert xq[-1, :8].tolist() == [127, 2, -2, 4, -4, 0, 0, 126]
+
+
+def test_quantize_strided_and_bf16(w8a8):
+    note("quantize strided + bf16")
+    x, _ = linear_inputs(70, 16, 2560, seed=5)
+    wide = np.zeros((70, 2560 + 64), np.float16)
+    wide[:, :2560] = x
+    t = dev(wide)[:, :2560]
+    xq, sx = w8a8.quantize_per_token(t)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_per_token(x)
+    assert (host(xq) == rq).all() and (host(sx) == rs).all()
+    # bf16 input
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    xq, sx = w8a8.quantize_per_token(xb.cuda())
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_per_token_bf16(bits)
+    assert (host(xq) == rq).all() and (host(sx).view(np.uint32) == rs.view(np.uint32)).all()
+
+
+def test_quantize_empty_batch(w8a8):
+    xq, sx = w8a8.quantize_per_token(torch.zeros((0, 256), dtype=torch.float16, device="cuda"))
+    torch.cuda.synchronize()
+    assert xq.shape == (0, 256) and sx.shape == (0,)
+
+
+# ---- weight quantization ---------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,gs,N,K", [(8, 0, 272, 2560), (8, 64, 272, 2560), (8, 128, 48, 384),
+                                         (4, 128, 272, 2560), (4, 64, 48, 384),
+                                         (8, 0, 10240, 2560), (4, 128, 10240, 2560)])
+def test_quantize_weight(w8a8, bits, gs, N, K):
+    note(f"quantize_weight bits={bits} gs={gs} N={N} K={K}")
+    _, W = linear_inputs(0, N, K, seed=N + K + gs)
+    W[3, :gs or K] = 0.0  # an all-zero group / row
+    wq, sw = w8a8.quantize_weight(dev(W), bits, gs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_weight(W, bits, gs)
+    assert (host(sw).view(np.uint32) == rs.view(np.uint32)).all()
+    assert (host(wq) == rq).all()
+
+
+# ---- GEMM + dequant ----------------------------------------------------------------------
+
+MODES = ["pc", "pg64", "pg128", "w4_128", "w4_64"]
+
+
+def run_mode(w8a8, mode, x, W, out_dtype, y=None):
+    """GPU path end to end from raw x and W. Returns (y, x_q, s_x)."""
+    xq, sx = w8a8.quantize_per_token(dev(x))
+    Wd = dev(W)
+    if mode == "pc":
+        wq, sw = w8a8.quantize_weight(Wd, 8, 0)
+        yt = w8a8.w8a8_gemm_pc(xq, sx, wq, sw, out_dtype, y=y)
+    elif mode.startswith("pg"):
+        gs = int(mode[2:])
+        wq, sw = w8a8.quantize_weight(Wd, 8, gs)
+        yt = w8a8.w8a8_gemm_pg(xq, sx, wq, sw, gs, out_dtype, y=y)
+    else:
+        gs = int(mode[3:])
+        wq, sw = w8a8.quantize_weight(Wd, 4, gs)
+        yt = w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, out_dtype, y=y)
+    torch.cuda.synchronize()
+    return yt
+
+
+def oracle_mode(mode, x, W):
+    if mode == "pc":
+        wq, sw = oracle.quantize_weight(W, 8, 0)
+        r = oracle.linear_pc(x, wq, sw)
+        r["mag"], r["G"] = np.abs(r["y"]), 1
+    elif mode.startswith("pg"):
+        gs = int(mode[2:])
+        wq, sw = oracle.quantize_weight(W, 8, gs)
+        r = oracle.linear_pg(x, wq, sw, gs)
+        r["G"] = W.shape[1] // gs
+    else:
+        gs = int(mode[3:])
+        wq, sw = oracle.quantize_weight(W, 4, gs)
+        r = oracle.linear_w4(x, wq, sw, gs)
+        r["G"] = W.shape[1] // gs
+    return r
+
+
+def compare(yt, r, what):
+    if yt.dtype == torch.int32:
+        got = host(yt)
+        assert (got == r["acc"]).all(), f"{what}: int32 accumulators differ"
+        return
+    check_output(host(yt), OUT_FMT[yt.dtype], r["y"], r["mag"], r["G"], what)
+
+
+SHAPES = [(37, 272, 384), (300, 1040, 2560), (128, 512, 640), (1, 16, 128), (65, 48, 256), (513, 272, 1280)]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_parity(w8a8, mode, M, N, K):
+    x, W = linear_inputs(M, N, K, seed=M + N + K)
+    r = oracle_mode(mode, x, W)
+    for out in (torch.float16, torch.bfloat16, torch.float32, torch.int32):
+        note(f"gemm {mode} M={M} N={N} K={K} out={out}")
+        compare(run_mode(w8a8, mode, x, W, out), r, f"{mode} {M}x{N}x{K} {out}")
+
+
+def test_gemm_strided_output_and_empty(w8a8):
+    note("gemm strided y, M=0")
+    x, W = linear_inputs(50, 272, 512, seed=3)
+    r = oracle_mode("pc", x, W)
+    ybig = torch.full((50, 272 + 32), 7.0, dtype=torch.float16, device="cuda")
+    run_mode(w8a8, "pc", x, W, torch.float16, y=ybig[:, :272])
+    got = host(ybig)
+    check_output(got[:, :272], "f16", r["y"], r["mag"], 1, "strided y")
+    assert (got[:, 272:] == np.float16(7.0)).all()  # padding columns untouched
+    xq = torch.zeros((0, 512), dtype=torch.int8, device="cuda")
+    sx = torch.zeros((0,), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((272, 512), dtype=torch.int8, device="cuda")
+    sw = torch.zeros((272,), dtype=torch.float32, device="cuda")
+    y = w8a8.w8a8_gemm_pc(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 272)
+
+
+@pytest.mark.parametrize("mode", ["pc", "pg64", "w4_128"])
+def test_every_config_identical(w8a8, mode):
+    """Every tile configuration gives bit-identical results (catches edge-mask and LDS races)."""
+    M, N, K = 300, 528, 1280
+    x, W = linear_inputs(M, N, K, seed=11)
+    r = oracle_mode(mode, x, W)
+    n_cfg = w8a8.w8a8_debug_force_config(-1)
+    outs = {}
+    try:
+        for cfg in range(-1, n_cfg):
+            w8a8.w8a8_debug_force_config(cfg)
+            for out in (torch.float16, torch.int32):
+                note(f"config {cfg} {mode} {out}")
+                y = run_mode(w8a8, mode, x, W, out)
+                compare(y, r, f"cfg {cfg} {mode}")
+                outs.setdefault(out, []).append(host(y))
+                y2 = run_mode(w8a8, mode, x, W, out)
+                assert (host(y2) == outs[out][-1]).all(), "non-deterministic"
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
+    for out, ys in outs.items():
+        for y in ys[1:]:
+            assert (y.view(np.uint8) == ys[0].view(np.uint8)).all(), f"configs differ ({out})"
+
+
+# ---- full workload sizes (the benchmark's launch configuration), sampled -------------------
+
+def sample_rows(M, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1, M // 2}
+    rows.update(rng.choice(M, min(n, M), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("mode,M,N,K", [
+    ("pc", 128, 10240, 2560),
+    ("pc", 4096, 10240, 2560),
+    ("pc", 8192, 2560, 10240),
+    ("pc", 1, 10240, 2560),
+    ("pc", 1024, 2560, 10240),
+    ("pg128", 4096, 10240, 2560),
+    ("pg64", 8192, 2560, 10240),
+    ("pg64", 128, 10240, 2560),
+    ("w4_128", 1, 10240, 2560),
+    ("w4_128", 1024, 10240, 2560),
+    ("w4_128", 4096, 10240, 2560),
+])
+def test_full_size_sampled(w8a8, mode, M, N, K):
+    note(f"full size {mode} M={M} N={N} K={K}")
+    x, W = linear_inputs(M, N, K, seed=0)
+    rows = sample_rows(M)
+    # codes and scales of every row
+    xq, sx = gpu_quantize(w8a8, x)
+    rq, rs = oracle.quantize_per_token(x)
+    assert (xq == rq).all() and (sx.view(np.uint32) == rs.view(np.uint32)).all()
+    r = oracle_mode(mode, x[rows], W)
+    for out in (torch.float16, torch.int32):
+        y = host(run_mode(w8a8, mode, x, W, out))
+        if out == torch.int32:
+            assert (y[rows] == r["acc"]).all(), "int32 accumulators differ"
+        else:
+            check_output(y[rows], "f16", r["y"], r["mag"], r["G"], f"{mode} {M}x{N}x{K}")
+
+
+def test_qwen3_block_sampled(w8a8):
+    """One Qwen3-8B-shaped block's seven linears at M=2048, per-channel, bf16 output."""
+    inputs, weights = qwen3_8b_block_inputs(M=2048, seed=0)
+    rows = sample_rows(2048, n=24)
+    for in_name, K, projs in QWEN3_8B_BLOCK_INPUTS:
+        x = inputs[in_name]
+        xq, sx = w8a8.quantize_per_token(dev(x))
+        xq_o, sx_o = oracle.quantize_per_token(x)
+        assert (host(xq) == xq_o).all() and (host(sx) == sx_o).all()
+        for name in projs:
+            note(f"qwen3 block {name}")
+            W = weights[name]
+            wq, sw = w8a8.quantize_weight(dev(W), 8, 0)
+            y = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.bfloat16))
+            torch.cuda.synchronize()
+            owq, osw = oracle.quantize_weight(W, 8, 0)
+            r = oracle.linear_pc(x[rows], owq, osw)
+            check_output(y[rows], "bf16", r["y"], np.abs(r["y"]), 1, f"qwen3 {name}")

@@ -1,0 +1,160 @@
+"""Python binding of libw8a8 (fused per-token quantize -> int8 GEMM -> dequant on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+of ``libw8a8.so``; PyTorch provides device memory and the current stream. The
+functions keep the C names of ``include/w8a8.h``.
+
+Importing this package loads the built library and raises ImportError when it is
+missing (build it with ``python -m w8a8_activation_quantized_amd.build``). There is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8a8.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libw8a8.so not found at {LIB_PATH}; build it with "
+        "`python -m w8a8_activation_quantized_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_SIGNATURES = {
+    "w8a8_is_available": ([_int], _int),
+    "w8a8_status_string": ([_int], ctypes.c_char_p),
+    "w8a8_last_error": ([], ctypes.c_char_p),
+    "w8a8_abi_version": ([], _int),
+    "w8a8_debug_force_config": ([_int], _int),
+    "quantize_per_token": ([_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp], _int),
+    "quantize_weight": ([_vp, _i64, _i64, _int, _int, _vp, _vp, _vp], _int),
+    "w8a8_gemm_pc": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
+    "w8a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
+    "w4a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
+}
+for _name, (_args, _res) in _SIGNATURES.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+# dtype enum of the C ABI
+F16, BF16, F32, I32 = 0, 1, 2, 3
+_DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, torch.int32: I32}
+STATUS = {0: "W8A8_OK", 1: "W8A8_ERR_INVALID_ARGUMENT", 2: "W8A8_ERR_UNSUPPORTED_DEVICE",
+          3: "W8A8_ERR_UNSUPPORTED_SHAPE", 4: "W8A8_ERR_HIP"}
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise W8A8Error(rc, _lib.w8a8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def lib():
+    """The ctypes handle of libw8a8.so (raw C entry points)."""
+    return _lib
+
+
+def w8a8_is_available(device: int = 0) -> bool:
+    return bool(_lib.w8a8_is_available(device))
+
+
+def w8a8_last_error() -> str:
+    return _lib.w8a8_last_error().decode()
+
+
+def w8a8_debug_force_config(config_id: int) -> int:
+    n = _lib.w8a8_debug_force_config(config_id)
+    if n < 0:
+        raise W8A8Error(-n, f"unknown config id {config_id}")
+    return n
+
+
+def quantize_per_token(x: torch.Tensor, x_q: torch.Tensor | None = None,
+                       s_x: torch.Tensor | None = None, stream=None):
+    """x [M, K] fp16/bf16 (row stride x.stride(0)) -> (x_q int8 [M, K], s_x fp32 [M])."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last dimension")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    M, K = x.shape
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(_lib.quantize_per_token(_ptr(x), _DTYPE_CODE[x.dtype], M, K, x.stride(0), _ptr(x_q),
+                                   _ptr(s_x), _stream(stream)))
+    return x_q, s_x
+
+
+def quantize_weight(W: torch.Tensor, bits: int = 8, group_size: int = 0, stream=None):
+    """W fp32 [N, K] -> (w_q, s_w); int8 [N, K] or packed uint8 [N, K/2]."""
+    if W.dtype != torch.float32 or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous fp32 [N, K] tensor")
+    N, K = W.shape
+    if bits == 8:
+        w_q = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    else:
+        w_q = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    s_w = torch.empty((N,) if group_size == 0 else (N, K // max(group_size, 1)), dtype=torch.float32,
+                      device=W.device)
+    _check(_lib.quantize_weight(_ptr(W), N, K, bits, group_size, _ptr(w_q), _ptr(s_w), _stream(stream)))
+    return w_q, s_w
+
+
+def _out(y, M, N, out_dtype, device):
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=device)
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be 2-D with a contiguous last dimension")
+    return y
+
+
+def w8a8_gemm_pc(x_q, s_x, w_q, s_w, out_dtype=torch.float16, y=None, stream=None):
+    """y [M, N] = (acc * s_x[m]) * s_w[n], acc = x_q . w_q^T (int32)."""
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    y = _out(y, M, N, out_dtype, x_q.device)
+    _check(_lib.w8a8_gemm_pc(_ptr(x_q), _ptr(s_x), _ptr(w_q), _ptr(s_w), _ptr(y), _DTYPE_CODE[y.dtype],
+                             M, N, K, y.stride(0), _stream(stream)))
+    return y
+
+
+def w8a8_gemm_pg(x_q, s_x, w_q, s_w, group_size, out_dtype=torch.float16, y=None, stream=None):
+    """Per-group dequant: y = s_x[m] * sum_g s_w[n, g] * acc_g."""
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    y = _out(y, M, N, out_dtype, x_q.device)
+    _check(_lib.w8a8_gemm_pg(_ptr(x_q), _ptr(s_x), _ptr(w_q), _ptr(s_w), group_size, _ptr(y),
+                             _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
+    return y
+
+
+def w4a8_gemm_pg(x_q, s_x, w_packed, s_w, group_size, out_dtype=torch.float16, y=None, stream=None):
+    """W4A8: int4 weights packed two per byte, unpacked in-kernel; per-group dequant."""
+    M, K = x_q.shape
+    N = w_packed.shape[0]
+    y = _out(y, M, N, out_dtype, x_q.device)
+    _check(_lib.w4a8_gemm_pg(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(s_w), group_size, _ptr(y),
+                             _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
+    return y

@@ -1,0 +1,240 @@
+// C-ABI layer of libw8a8: argument validation, device checks, status codes and
+// dispatch to the kernel launchers. Every check runs on the host before anything is
+// enqueued, so an invalid call leaves the stream untouched.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/w8a8.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return W8A8_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool forced_unavailable() {
+    const char *e = getenv("W8A8_FORCE_UNAVAILABLE");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_force_cfg{-1};
+
+bool device_is_gfx950(int device) {
+    if (device < 0 || device >= kMaxDevices) return false;
+    int cached = g_arch_ok[device].load(std::memory_order_relaxed);
+    if (cached == 0) {
+        int count = 0;
+        hipDeviceProp_t prop;
+        bool good = hipGetDeviceCount(&count) == hipSuccess && device < count &&
+                    hipGetDeviceProperties(&prop, device) == hipSuccess &&
+                    strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        cached = good ? 1 : 2;
+        g_arch_ok[device].store(cached, std::memory_order_relaxed);
+    }
+    return cached == 1;
+}
+
+// Checks the current device; returns W8A8_OK or an error status (message set).
+int check_device() {
+    if (forced_unavailable())
+        return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "W8A8_FORCE_UNAVAILABLE=1 is set");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "no HIP device available");
+    }
+    if (!device_is_gfx950(dev))
+        return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "device %d is not a gfx950 (MI355X) GPU", dev);
+    return W8A8_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(W8A8_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool valid_out(int d) { return d == W8A8_F16 || d == W8A8_BF16 || d == W8A8_F32 || d == W8A8_I32; }
+
+// Shared validation of the three GEMM entry points.
+int check_gemm(const char *fn, const void *x_q, const float *s_x, const void *w, const float *s_w,
+               int gs, const void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+               bool per_group) {
+    if (M < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: M = %lld < 0", fn, (long long)M);
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || N * K > ((int64_t)1 << 40) ||
+        M * K > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (N < 16 || N % 16 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: N = %lld must be a positive multiple of 16", fn,
+                    (long long)N);
+    if (K < 64 || K % 64 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 64", fn,
+                    (long long)K);
+    if (per_group) {
+        if (gs != 64 && gs != 128)
+            return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size = %d must be 64 or 128", fn, gs);
+        if (K % gs != 0)
+            return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld not a multiple of group_size %d", fn,
+                        (long long)K, gs);
+    }
+    if (!valid_out(y_dtype)) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: bad y_dtype %d", fn, y_dtype);
+    if (ldy < N || ldy % 4 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldy = %lld must be >= N and a multiple of 4", fn,
+                    (long long)ldy);
+    if (M == 0) return W8A8_OK;
+    if (!x_q || !s_x || !w || !s_w || !y) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (!aligned16(x_q) || !aligned16(s_x) || !aligned16(w) || !aligned16(s_w) || !aligned16(y))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    return W8A8_OK;
+}
+
+int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w, const float *s_w,
+             int gs, int wkind, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+             void *stream) {
+    int rc = check_gemm(fn, x_q, s_x, w, s_w, gs, y, y_dtype, M, N, K, ldy, gs != 0 || wkind == w8a8::W_INT4);
+    if (rc != W8A8_OK) return rc;
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    w8a8::GemmProblem p;
+    p.xq = x_q;
+    p.sx = s_x;
+    p.wq = w;
+    p.sw = s_w;
+    p.y = y;
+    p.ldy = ldy;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.gs = gs;
+    p.wkind = wkind;
+    p.out = y_dtype;
+    return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed),
+                                      static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int w8a8_is_available(int device) {
+    if (forced_unavailable()) return 0;
+    return device_is_gfx950(device) ? 1 : 0;
+}
+
+const char *w8a8_status_string(int status) {
+    switch (status) {
+        case W8A8_OK: return "ok";
+        case W8A8_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case W8A8_ERR_UNSUPPORTED_DEVICE: return "unsupported device";
+        case W8A8_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case W8A8_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char *w8a8_last_error(void) { return g_last_error; }
+
+int w8a8_abi_version(void) { return 1; }
+
+int w8a8_debug_force_config(int config_id) {
+    if (config_id < -1 || config_id >= w8a8::gemm_num_configs()) return -W8A8_ERR_INVALID_ARGUMENT;
+    g_force_cfg.store(config_id, std::memory_order_relaxed);
+    return w8a8::gemm_num_configs();
+}
+
+int quantize_per_token(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t *x_q,
+                       float *s_x, void *stream) {
+    const char *fn = "quantize_per_token";
+    if (x_dtype != W8A8_F16 && x_dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: x_dtype must be F16 or BF16", fn);
+    if (M < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: M = %lld < 0", fn, (long long)M);
+    if (K < 8 || K % 8 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 8", fn,
+                    (long long)K);
+    if (M > INT32_MAX || K > INT32_MAX || M * K > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (ldx < K || ldx % 8 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldx = %lld must be >= K and a multiple of 8", fn,
+                    (long long)ldx);
+    if (M > 0) {
+        if (!x || !x_q || !s_x) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if (!aligned16(x) || !aligned16(x_q) || !aligned16(s_x))
+            return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    }
+    int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    return launched(w8a8::launch_quantize_per_token(x, x_dtype == W8A8_BF16, ldx, (int)M, (int)K, x_q,
+                                                    s_x, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_size, void *w_q,
+                    float *s_w, void *stream) {
+    const char *fn = "quantize_weight";
+    if (bits != 8 && bits != 4) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: bits must be 8 or 4", fn);
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
+    if (bits == 4 && group_size == 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
+    if (N < 1) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: N = %lld < 1", fn, (long long)N);
+    if (K < 64 || K % 64 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 64", fn,
+                    (long long)K);
+    if (group_size && K % group_size != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K not a multiple of group_size", fn);
+    if (N > INT32_MAX || K > INT32_MAX || N * K > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (!W || !w_q || !s_w) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (!aligned16(W) || !aligned16(w_q) || !aligned16(s_w))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    return launched(w8a8::launch_quantize_weight(W, (int)N, (int)K, bits, group_size, w_q, s_w,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int w8a8_gemm_pc(const int8_t *x_q, const float *s_x, const int8_t *w_q, const float *s_w, void *y,
+                 int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream) {
+    return run_gemm("w8a8_gemm_pc", x_q, s_x, w_q, s_w, 0, w8a8::W_INT8, y, y_dtype, M, N, K, ldy, stream);
+}
+
+int w8a8_gemm_pg(const int8_t *x_q, const float *s_x, const int8_t *w_q, const float *s_w,
+                 int group_size, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                 void *stream) {
+    if (group_size == 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "w8a8_gemm_pg: group_size must be 64 or 128");
+    return run_gemm("w8a8_gemm_pg", x_q, s_x, w_q, s_w, group_size, w8a8::W_INT8, y, y_dtype, M, N, K,
+                    ldy, stream);
+}
+
+int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, const float *s_w,
+                 int group_size, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                 void *stream) {
+    if (group_size == 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "w4a8_gemm_pg: group_size must be 64 or 128");
+    return run_gemm("w4a8_gemm_pg", x_q, s_x, w_packed, s_w, group_size, w8a8::W_INT4, y, y_dtype, M, N,
+                    K, ldy, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,426 @@
+// int8 GEMM with fused dequantization for gfx950 (CDNA4) matrix cores.
+//
+// Computes, for x_q [M, K] int8 (row-major) and w_q [N, K] int8 (row-major, one row
+// per output channel):
+//   acc[m, n] = sum_k x_q[m, k] * w_q[n, k]             exact int32 (MFMA i8 -> i32)
+// and then, in the store stage, one of (juejin post "在Mac上跑大模型，MLX 不是终点",
+// sections "W8A8 对称量化" and "三种量化粒度的实现"; Cider README "量化"):
+//   per-channel:  y = (fp32(acc) * s_x[m]) * s_w[n]
+//   per-group:    t = 0; for each K-group g ascending: t = fma(fp32(acc_g), s_w[n, g], t);
+//                 y = t * s_x[m]
+// For W4A8 the weight tile arrives as packed nibbles (u = q + 8, even k low) and is
+// unpacked to int8 codes while it is written to LDS (README "Metal Kernel 流水线":
+// the unpack is part of the operand load); the rest is the per-group path.
+//
+// Design (MI355X-first):
+//  * v_mfma_i32_16x16x64_i8: each lane feeds 16 contiguous K-bytes of one row of
+//    each operand. Both operands are K-contiguous in HBM, so tiles are copied to
+//    LDS row-major and read back as 16-byte fragments (ds_read_b128).
+//  * The weight tile is the MFMA "A" operand and the activation tile the "B"
+//    operand, so each lane's four accumulator values are four consecutive output
+//    channels n of one token m: the epilogue writes 8 (fp16/bf16) or 16 (fp32)
+//    contiguous bytes per lane.
+//  * LDS rows are BK bytes; 16-byte chunks are XOR-swizzled by row so that the
+//    16 lanes reading one fragment column, and the lanes writing one row, touch
+//    distinct banks.
+//  * Two LDS stages: global loads for tile k+1 are issued into registers before the
+//    MFMAs of tile k and written to the other stage afterwards; one barrier per
+//    K-tile.
+//  * Workgroup -> tile mapping is XCD-aware: the hardware deals workgroups to the
+//    8 XCDs round-robin, so the block id is remapped to give each XCD a contiguous
+//    run of tiles, which are then walked in groups of GROUP_M tile-rows so the
+//    tiles that run together on one XCD share activation and weight panels in
+//    that XCD's L2.
+//  * Ragged M and N: out-of-range rows are clamped to the last valid row for
+//    loads (always in bounds) and masked at the store. A K that is a multiple of 64
+//    but not of the 128-byte K-tile ends in a half tile whose missing chunks are
+//    loaded from a clamped address and replaced by zero codes (int4: nibble 8),
+//    which add nothing to the integer sums.
+#include "internal.h"
+
+namespace w8a8 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a swizzled [rows][BK] tile.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    if constexpr (BK == 128)
+        return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+    else
+        return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// Eight packed bytes (two dwords; 16 nibbles, even k in the low nibble) -> sixteen int8
+// codes q = u - 8 in k order.
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t lo, uint32_t hi) {
+    // bytes [lo0, hi0, lo1, hi1]
+    return (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t lo, uint32_t hi) {
+    // bytes [lo2, hi2, lo3, hi3]
+    return ((lo >> 16) & 0xFFu) | (((hi >> 16) & 0xFFu) << 8) | ((lo >> 8) & 0xFF0000u) | (hi & 0xFF000000u);
+}
+__device__ __forceinline__ uint32_t recentre(uint32_t u4) {
+    // per byte u - 8 without borrows: u + 0x78 stays below 0x100, xor 0x80 recentres
+    return (u4 + 0x78787878u) ^ 0x80808080u;
+}
+__device__ __forceinline__ v4u unpack_nibbles(uint32_t d0, uint32_t d1) {
+    const uint32_t lo0 = d0 & 0x0F0F0F0Fu, hi0 = (d0 >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo1 = d1 & 0x0F0F0F0Fu, hi1 = (d1 >> 4) & 0x0F0F0F0Fu;
+    return v4u{recentre(interleave_lo(lo0, hi0)), recentre(interleave_hi(lo0, hi0)),
+               recentre(interleave_lo(lo1, hi1)), recentre(interleave_hi(lo1, hi1))};
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Store four consecutive outputs y[m, n..n+3].
+__device__ __forceinline__ void store4(void *y, int64_t off, int out, float v0, float v1, float v2,
+                                       float v3) {
+    if (out == OUT_F16) {
+        uint2 w = make_uint2(f16_bits(v0) | (f16_bits(v1) << 16), f16_bits(v2) | (f16_bits(v3) << 16));
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + off) = w;
+    } else if (out == OUT_BF16) {
+        uint2 w = make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + off) = w;
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(y) + off) = make_float4(v0, v1, v2, v3);
+    }
+}
+
+struct TileMap {
+    int tiles_m, tiles_n, group_m;
+};
+
+// XCD-aware block -> (tile_m, tile_n).
+__device__ __forceinline__ void map_tile(const TileMap &t, int &tm, int &tn) {
+    const int T = t.tiles_m * t.tiles_n;
+    const int b = blockIdx.x;
+    const int x = b & 7, i = b >> 3;
+    const int q = T >> 3, r = T & 7;
+    const int logical = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+    const int per_group = t.group_m * t.tiles_n;
+    const int grp = logical / per_group;
+    const int first_m = grp * t.group_m;
+    const int gsize = min(t.tiles_m - first_m, t.group_m);
+    const int in_grp = logical - grp * per_group;
+    tm = first_m + in_grp % gsize;
+    tn = in_grp / gsize;
+}
+
+// Compile-time shape of one kernel instantiation.
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int GS_, int WK_>
+struct Shape {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, GS = GS_, WK = WK_;
+    static constexpr int NT = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int FM = WM / 16, FN = WN / 16;
+    static constexpr int CPR = BK / 16;  // 16-byte chunks per LDS row
+    static constexpr int KSTEPS = BK / 64;
+    static constexpr bool GROUPED = GS > 0;
+    static constexpr int GPT = GROUPED ? BK / GS : 1;  // groups per K-tile
+    static constexpr int KS_PER_G = GROUPED ? GS / 64 : 1;
+    static constexpr int W_TILE = BN * BK, X_TILE = BM * BK, STAGE = W_TILE + X_TILE;
+    static constexpr int W_LOADS = (WK == W_INT4 ? BN * CPR / 2 : BN * CPR);
+    static constexpr int X_LOADS = BM * CPR;
+    static constexpr int WL = W_LOADS / NT, XL = X_LOADS / NT;
+    static constexpr int SW_N = GROUPED ? BN * GPT : 0;
+    static constexpr int SWL = GROUPED ? (SW_N + NT - 1) / NT : 1;
+    static_assert(!GROUPED || BK % GS == 0, "a K-tile must hold whole groups");
+    static_assert(W_LOADS % NT == 0 && X_LOADS % NT == 0, "loader shape");
+};
+
+// Issue the global loads of K-tile kt into registers.
+template <class S>
+__device__ __forceinline__ void tile_gload(const GemmProblem &p, int kt, int tid, int m0, int n0,
+                                           v4u (&wreg)[S::WL], v4u (&xreg)[S::XL],
+                                           float (&swreg)[S::SWL]) {
+    const int k0 = kt * S::BK;
+    const int M = p.M, N = p.N, K = p.K;
+#pragma unroll
+    for (int i = 0; i < S::WL; ++i) {
+        const int c = tid + i * S::NT;
+        if constexpr (S::WK == W_INT4) {
+            const int row = c / (S::CPR / 2), pc = c % (S::CPR / 2);
+            const int n = min(n0 + row, N - 1);
+            const int kk = k0 + pc * 32;  // first code of this 16-byte packed chunk
+            const v4u v = *reinterpret_cast<const v4u *>(static_cast<const uint8_t *>(p.wq) +
+                                                         (int64_t)n * (K / 2) + min(kk, K - 32) / 2);
+            wreg[i] = kk < K ? v : v4u{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        } else {
+            const int row = c / S::CPR, cc = c % S::CPR;
+            const int n = min(n0 + row, N - 1);
+            const int kk = k0 + cc * 16;
+            const v4u v = *reinterpret_cast<const v4u *>(static_cast<const int8_t *>(p.wq) +
+                                                         (int64_t)n * K + min(kk, K - 16));
+            wreg[i] = kk < K ? v : v4u{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::XL; ++i) {
+        const int c = tid + i * S::NT;
+        const int row = c / S::CPR, cc = c % S::CPR;
+        const int m = min(m0 + row, M - 1);
+        const int kk = k0 + cc * 16;
+        const v4u v = *reinterpret_cast<const v4u *>(p.xq + (int64_t)m * K + min(kk, K - 16));
+        xreg[i] = kk < K ? v : v4u{0u, 0u, 0u, 0u};
+    }
+    if constexpr (S::GROUPED) {
+        const int G = K / S::GS;
+#pragma unroll
+        for (int i = 0; i < S::SWL; ++i) {
+            const int idx = tid + i * S::NT;
+            if (idx < S::SW_N) {
+                const int j = idx / S::BN, nn = idx % S::BN;
+                const int n = min(n0 + nn, N - 1);
+                const int g = kt * S::GPT + j;
+                swreg[i] = g < G ? p.sw[(int64_t)n * G + g] : 0.f;
+            }
+        }
+    }
+}
+
+// Write the registers of one K-tile into LDS stage `stage` (int4 weights unpacked here).
+template <class S>
+__device__ __forceinline__ void tile_lstore(int8_t *smem, float *s_sw, int stage, int tid,
+                                            const v4u (&wreg)[S::WL], const v4u (&xreg)[S::XL],
+                                            const float (&swreg)[S::SWL]) {
+    int8_t *Ws = smem + stage * S::STAGE;
+    int8_t *Xs = Ws + S::W_TILE;
+#pragma unroll
+    for (int i = 0; i < S::WL; ++i) {
+        const int c = tid + i * S::NT;
+        if constexpr (S::WK == W_INT4) {
+            const int row = c / (S::CPR / 2), pc = c % (S::CPR / 2);
+            const v4u v = wreg[i];
+            const v4u lo = unpack_nibbles(v[0], v[1]), hi = unpack_nibbles(v[2], v[3]);
+            *reinterpret_cast<v4u *>(Ws + swz<S::BK>(row, 2 * pc)) = lo;
+            *reinterpret_cast<v4u *>(Ws + swz<S::BK>(row, 2 * pc + 1)) = hi;
+        } else {
+            const int row = c / S::CPR, cc = c % S::CPR;
+            *reinterpret_cast<v4u *>(Ws + swz<S::BK>(row, cc)) = wreg[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::XL; ++i) {
+        const int c = tid + i * S::NT;
+        const int row = c / S::CPR, cc = c % S::CPR;
+        *reinterpret_cast<v4u *>(Xs + swz<S::BK>(row, cc)) = xreg[i];
+    }
+    if constexpr (S::GROUPED) {
+#pragma unroll
+        for (int i = 0; i < S::SWL; ++i) {
+            const int idx = tid + i * S::NT;
+            if (idx < S::SW_N) s_sw[stage * S::SW_N + idx] = swreg[i];
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int GS, int WK>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmProblem p, TileMap tmap) {
+    using S = Shape<BM, BN, BK, WGM, WGN, GS, WK>;
+    constexpr int FM = S::FM, FN = S::FN, WM = S::WM, WN = S::WN;
+    constexpr bool GROUPED = S::GROUPED;
+
+    __shared__ __attribute__((aligned(16))) int8_t smem[2 * S::STAGE];
+    __shared__ __attribute__((aligned(16))) float s_sw[GROUPED ? 2 * S::SW_N : 4];
+
+    int tm, tn;
+    map_tile(tmap, tm, tn);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    v4u wreg[S::WL], xreg[S::XL];
+    float swreg[S::SWL];
+
+    v4i acc[FN][FM];
+    float facc[GROUPED ? FN : 1][GROUPED ? FM : 1][4];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) facc[i][j][e] = 0.f;
+    }
+
+    const int KT = (p.K + BK - 1) / BK;  // K % 64 == 0: a last half tile is zero-filled
+    const int frow = lane & 15, fchunk = lane >> 4;
+    tile_gload<S>(p, 0, tid, m0, n0, wreg, xreg, swreg);
+    tile_lstore<S>(smem, s_sw, 0, tid, wreg, xreg, swreg);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) tile_gload<S>(p, kt + 1, tid, m0, n0, wreg, xreg, swreg);
+        const int8_t *Ws = smem + cur * S::STAGE;
+        const int8_t *Xs = Ws + S::W_TILE;
+#pragma unroll
+        for (int ks = 0; ks < S::KSTEPS; ++ks) {
+            v4i a[FN], b[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                a[fn] = *reinterpret_cast<const v4i *>(Ws + swz<BK>(wn * WN + fn * 16 + frow, ks * 4 + fchunk));
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                b[fm] = *reinterpret_cast<const v4i *>(Xs + swz<BK>(wm * WM + fm * 16 + frow, ks * 4 + fchunk));
+            if constexpr (GROUPED) {
+                const bool first = (ks % S::KS_PER_G) == 0;
+                const bool last = (ks % S::KS_PER_G) == S::KS_PER_G - 1;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        acc[fn][fm] = mfma_i8(a[fn], b[fm], first ? v4i{0, 0, 0, 0} : acc[fn][fm]);
+                if (last) {
+                    const int j = ks / S::KS_PER_G;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const float4 s4 = *reinterpret_cast<const float4 *>(
+                            s_sw + cur * S::SW_N + j * BN + wn * WN + fn * 16 + 4 * fchunk);
+#pragma unroll
+                        for (int fm = 0; fm < FM; ++fm) {
+                            facc[fn][fm][0] = __builtin_fmaf((float)acc[fn][fm][0], s4.x, facc[fn][fm][0]);
+                            facc[fn][fm][1] = __builtin_fmaf((float)acc[fn][fm][1], s4.y, facc[fn][fm][1]);
+                            facc[fn][fm][2] = __builtin_fmaf((float)acc[fn][fm][2], s4.z, facc[fn][fm][2]);
+                            facc[fn][fm][3] = __builtin_fmaf((float)acc[fn][fm][3], s4.w, facc[fn][fm][3]);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+            }
+        }
+        if (kt + 1 < KT) tile_lstore<S>(smem, s_sw, cur ^ 1, tid, wreg, xreg, swreg);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dequant + store -------------------------------------------------
+    const int out = p.out;
+    const int M = p.M, N = p.N;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm * WM + fm * 16 + frow;
+        const bool mok = m < M;
+        const float sxm = mok ? p.sx[m] : 0.f;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + wn * WN + fn * 16 + 4 * fchunk;
+            if (!mok || n >= N) continue;
+            const int64_t off = (int64_t)m * p.ldy + n;
+            if constexpr (GROUPED) {
+                store4(p.y, off, out, facc[fn][fm][0] * sxm, facc[fn][fm][1] * sxm, facc[fn][fm][2] * sxm,
+                       facc[fn][fm][3] * sxm);
+            } else {
+                const v4i v = acc[fn][fm];
+                if (out == OUT_I32) {
+                    *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = make_int4(v[0], v[1], v[2], v[3]);
+                } else {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(p.sw + n);
+                    store4(p.y, off, out, ((float)v[0] * sxm) * s4.x, ((float)v[1] * sxm) * s4.y,
+                           ((float)v[2] * sxm) * s4.z, ((float)v[3] * sxm) * s4.w);
+                }
+            }
+        }
+    }
+}
+
+// ---- configuration table ------------------------------------------------------------
+
+struct Config {
+    int bm, bn, group_m;
+};
+
+// Index = config id for w8a8_debug_force_config.
+constexpr Config kConfigs[] = {
+    {128, 128, 4},  // 0: 4 waves, 64x64 per wave
+    {256, 256, 4},  // 1: 8 waves, 128x64 per wave
+    {256, 128, 4},  // 2: 4 waves, 128x64 per wave
+    {128, 256, 4},  // 3: 4 waves, 64x128 per wave
+    {64, 64, 4},    // 4: 4 waves, 32x32 per wave (small M / narrow N)
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+template <int BM, int BN, int WGM, int WGN, int GS, int WK>
+hipError_t launch_cfg(const GemmProblem &p, int group_m, hipStream_t stream) {
+    TileMap t;
+    t.tiles_m = (p.M + BM - 1) / BM;
+    t.tiles_n = (p.N + BN - 1) / BN;
+    t.group_m = group_m;
+    dim3 grid(t.tiles_m * t.tiles_n), block(64 * WGM * WGN);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, 128, WGM, WGN, GS, WK>), grid, block, 0, stream, p, t);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_shape(const GemmProblem &p, int group_m, hipStream_t stream) {
+    // I32 output is the raw sum over all of K: the ungrouped kernel.
+    if (p.wkind == W_INT4) return launch_cfg<BM, BN, WGM, WGN, 0, W_INT4>(p, group_m, stream);
+    return launch_cfg<BM, BN, WGM, WGN, 0, W_INT8>(p, group_m, stream);
+}
+
+// Grouped (per-group scale) kernels keep an fp32 accumulator beside the int32 one, so
+// only the tile shapes whose registers hold both without spilling are instantiated.
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_grouped(const GemmProblem &p, int group_m, hipStream_t stream) {
+    if (p.wkind == W_INT4) {
+        if (p.gs == 64) return launch_cfg<BM, BN, WGM, WGN, 64, W_INT4>(p, group_m, stream);
+        return launch_cfg<BM, BN, WGM, WGN, 128, W_INT4>(p, group_m, stream);
+    }
+    if (p.gs == 64) return launch_cfg<BM, BN, WGM, WGN, 64, W_INT8>(p, group_m, stream);
+    return launch_cfg<BM, BN, WGM, WGN, 128, W_INT8>(p, group_m, stream);
+}
+
+int choose_config(const GemmProblem &p) {
+    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (p.M <= 128) return 4;
+    if (big_tiles >= 256) return 1;
+    return 0;
+}
+
+}  // namespace
+
+int gemm_num_configs() { return kNumConfigs; }
+
+hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) {
+    int id = (force_cfg >= 0 && force_cfg < kNumConfigs) ? force_cfg : choose_config(p);
+    const bool grouped = p.gs > 0 && p.out != OUT_I32;
+    if (grouped) {
+        if (id != 4) id = 0;
+        const int gm = kConfigs[id].group_m;
+        if (id == 4) return launch_grouped<64, 64, 2, 2>(p, gm, stream);
+        return launch_grouped<128, 128, 2, 2>(p, gm, stream);
+    }
+    const int gm = kConfigs[id].group_m;
+    switch (id) {
+        case 0: return launch_shape<128, 128, 2, 2>(p, gm, stream);
+        case 1: return launch_shape<256, 256, 2, 4>(p, gm, stream);
+        case 2: return launch_shape<256, 128, 2, 2>(p, gm, stream);
+        case 3: return launch_shape<128, 256, 2, 2>(p, gm, stream);
+        default: return launch_shape<64, 64, 2, 2>(p, gm, stream);
+    }
+}
+
+}  // namespace w8a8

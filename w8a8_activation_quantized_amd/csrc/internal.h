@@ -1,0 +1,40 @@
+// Internal launcher interface between the C-ABI layer (abi.hip) and the kernel
+// translation units. Arguments reaching these launchers are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+enum OutType { OUT_F16 = 0, OUT_BF16 = 1, OUT_F32 = 2, OUT_I32 = 3 };
+enum WeightKind { W_INT8 = 0, W_INT4 = 1 };
+
+struct GemmProblem {
+    const int8_t *xq;  // [M, K]
+    const float *sx;   // [M]
+    const void *wq;    // int8 [N, K] or packed uint8 [N, K/2]
+    const float *sw;   // [N] (per-channel) or [N, K/gs]
+    void *y;           // [M, N], row stride ldy
+    int64_t ldy;
+    int M, N, K;
+    int gs;            // 0 = per-channel, else 64 | 128
+    int wkind;         // WeightKind
+    int out;           // OutType
+};
+
+// Activation quantization (fp16 / bf16 rows -> int8 + fp32 scale).
+hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int M, int K,
+                                     int8_t *xq, float *sx, hipStream_t stream);
+
+// Offline weight quantization.
+hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
+                                  float *sw, hipStream_t stream);
+
+// GEMM + fused dequant. `force_cfg` < 0 lets the launcher choose by shape.
+hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream);
+
+// Number of GEMM tile configurations selectable via force_cfg.
+int gemm_num_configs();
+
+}  // namespace w8a8

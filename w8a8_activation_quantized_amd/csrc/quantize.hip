@@ -1,0 +1,204 @@
+// Activation and weight quantization kernels for gfx950.
+//
+// Per-token symmetric int8 quantization (juejin post "在Mac上跑大模型，MLX 不是终点",
+// section "W8A8 对称量化：Cider 的选择"): s = max|x| / 127, q = clamp(round(x / s)).
+// "round" is IEEE round-half-to-even of the correctly rounded fp32 quotient; the
+// division below is a true IEEE fp32 division (hipcc's default correctly rounded
+// divide; this file must never be built with fast-math or approximate division).
+//
+// Activation kernel layout: one wavefront per token row, 4 rows per 256-thread
+// workgroup. Each lane loads 16-byte chunks (8 halves) at chunk index lane + 64*j,
+// so every load instruction of the wave covers 1 KiB of contiguous row data. The
+// row is cached in registers between the absmax pass and the quantize pass (up to
+// CPL chunks per lane), so HBM sees exactly one read of x and one write of x_q.
+// The absmax works on the magnitude bit patterns (bits & 0x7fff), which order
+// like the magnitudes for finite fp16/bf16 values.
+#include "internal.h"
+
+namespace w8a8 {
+namespace {
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+    return (float)v;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+    return __builtin_bit_cast(float, h << 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_float(uint32_t bits) {
+    return BF16 ? bf16_bits_to_float(bits) : half_bits_to_float(bits);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// One code: clamp(rne(v / s), lo, hi); 0 when s == 0.
+__device__ __forceinline__ int quant_one(float v, float s, float lo, float hi) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, lo), hi);
+    return (int)r;
+}
+
+__device__ __forceinline__ uint32_t absmax8(uint4 c) {
+    uint32_t m = 0;
+    uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+    }
+    return m;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint2 quant8(uint4 c, float s) {
+    uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int q0 = quant_one(to_float<BF16>(w[i] & 0xffffu), s, -128.f, 127.f);
+        int q1 = quant_one(to_float<BF16>(w[i] >> 16), s, -128.f, 127.f);
+        uint32_t pair = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8);
+        out[i >> 1] |= pair << (16 * (i & 1));
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+// CPL = chunks per lane kept in registers; rows with more chunks than 64*CPL take
+// a second read pass for the remainder.
+template <int CPL, bool BF16>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__restrict__ x,
+                                                             int64_t ldx, int M, int K,
+                                                             int8_t *__restrict__ xq,
+                                                             float *__restrict__ sx) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const uint16_t *row = x + (int64_t)m * ldx;
+    int8_t *qrow = xq + (int64_t)m * K;
+    const int nch = K >> 3;
+
+    uint4 cache[CPL];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        int c = lane + 64 * j;
+        cache[j] = c < nch ? *reinterpret_cast<const uint4 *>(row + 8 * c) : make_uint4(0, 0, 0, 0);
+        amax = max(amax, absmax8(cache[j]));
+    }
+    for (int c = lane + 64 * CPL; c < nch; c += 64)
+        amax = max(amax, absmax8(*reinterpret_cast<const uint4 *>(row + 8 * c)));
+    amax = wave_max_u32(amax);
+
+    const float a = to_float<BF16>(amax);
+    const float s = a / 127.0f;
+    if (lane == 0) sx[m] = s;
+
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        int c = lane + 64 * j;
+        if (c < nch) *reinterpret_cast<uint2 *>(qrow + 8 * c) = quant8<BF16>(cache[j], s);
+    }
+    for (int c = lane + 64 * CPL; c < nch; c += 64)
+        *reinterpret_cast<uint2 *>(qrow + 8 * c) =
+            quant8<BF16>(*reinterpret_cast<const uint4 *>(row + 8 * c), s);
+}
+
+template <bool BF16>
+hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, float *sx,
+                       hipStream_t stream) {
+    const int nch = K / 8;
+    const int per_lane = (nch + 63) / 64;
+    dim3 grid((M + 3) / 4), block(256);
+    const uint16_t *xp = static_cast<const uint16_t *>(x);
+    if (per_lane <= 1)
+        hipLaunchKernelGGL((quantize_rows_kernel<1, BF16>), grid, block, 0, stream, xp, ldx, M, K, xq, sx);
+    else if (per_lane <= 2)
+        hipLaunchKernelGGL((quantize_rows_kernel<2, BF16>), grid, block, 0, stream, xp, ldx, M, K, xq, sx);
+    else if (per_lane <= 4)
+        hipLaunchKernelGGL((quantize_rows_kernel<4, BF16>), grid, block, 0, stream, xp, ldx, M, K, xq, sx);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL((quantize_rows_kernel<8, BF16>), grid, block, 0, stream, xp, ldx, M, K, xq, sx);
+    else if (per_lane <= 16)
+        hipLaunchKernelGGL((quantize_rows_kernel<16, BF16>), grid, block, 0, stream, xp, ldx, M, K, xq, sx);
+    else
+        hipLaunchKernelGGL((quantize_rows_kernel<32, BF16>), grid, block, 0, stream, xp, ldx, M, K, xq, sx);
+    return hipGetLastError();
+}
+
+// ---- offline weight quantization ------------------------------------------------------
+// One wavefront per run (a weight row for per-channel, one K-group for per-group).
+// Min-max symmetric (Cider README "说明"): s = max|W| / qdiv, q = clamp(rne(W / s)).
+// int4: s = max / 7, codes in [-8, 7] stored as u = q + 8, even k in the low nibble
+// (README "模式" / "量化").
+template <int BITS>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(const float *__restrict__ W, int N,
+                                                               int K, int run,
+                                                               void *__restrict__ wq,
+                                                               float *__restrict__ sw) {
+    const int lane = threadIdx.x & 63;
+    const int runs_per_row = K / run;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= (int64_t)N * runs_per_row) return;
+    const int64_t n = r / runs_per_row;
+    const int g = (int)(r % runs_per_row);
+    const float *src = W + n * K + (int64_t)g * run;
+
+    float a = 0.f;
+    for (int i = lane; i < run; i += 64) a = fmaxf(a, fabsf(src[i]));
+    a = wave_max_f32(a);
+    const float qdiv = BITS == 8 ? 127.0f : 7.0f;
+    const float s = a / qdiv;
+    if (lane == 0) sw[r] = s;
+
+    if (BITS == 8) {
+        int8_t *dst = static_cast<int8_t *>(wq) + n * K + (int64_t)g * run;
+        for (int i = lane; i < run; i += 64) dst[i] = (int8_t)quant_one(src[i], s, -128.f, 127.f);
+    } else {
+        uint8_t *dst = static_cast<uint8_t *>(wq) + n * (K / 2) + (int64_t)g * (run / 2);
+        for (int p = lane; p < run / 2; p += 64) {
+            int q0 = quant_one(src[2 * p], s, -8.f, 7.f);
+            int q1 = quant_one(src[2 * p + 1], s, -8.f, 7.f);
+            dst[p] = (uint8_t)((q0 + 8) | ((q1 + 8) << 4));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int M, int K,
+                                     int8_t *xq, float *sx, hipStream_t stream) {
+    return bf16 ? launch_rows<true>(x, ldx, M, K, xq, sx, stream)
+                : launch_rows<false>(x, ldx, M, K, xq, sx, stream);
+}
+
+hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
+                                  float *sw, hipStream_t stream) {
+    const int run = gs ? gs : K;
+    const int64_t runs = (int64_t)N * (K / run);
+    dim3 grid((unsigned)((runs + 3) / 4)), block(256);
+    if (bits == 8)
+        hipLaunchKernelGGL(quantize_weight_kernel<8>, grid, block, 0, stream, W, N, K, run, wq, sw);
+    else
+        hipLaunchKernelGGL(quantize_weight_kernel<4>, grid, block, 0, stream, W, N, K, run, wq, sw);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8
