@@ -20,9 +20,10 @@
 //    operand, so each lane's four accumulator values are four consecutive output
 //    channels n of one token m: the epilogue writes 8 (fp16/bf16) or 16 (fp32)
 //    contiguous bytes per lane.
-//  * LDS rows are BK bytes; 16-byte chunks are XOR-swizzled by row so that the
-//    16 lanes reading one fragment column, and the lanes writing one row, touch
-//    distinct banks.
+//  * LDS rows are BK bytes; 16-byte chunks are XOR-swizzled by row (chunk ^ ((row >> 1)
+//    & 7) for 128-byte rows). Measured on gfx950 with SQ_LDS_BANK_CONFLICT: this
+//    fragment-read pattern (16 rows x one logical chunk per 16 lanes) runs at the
+//    full 4 cycles per ds_read_b128, where an unswizzled layout takes 16.
 //  * Two LDS stages: global loads for tile k+1 are issued into registers before the
 //    MFMAs of tile k and written to the other stage afterwards; one barrier per
 //    K-tile.
@@ -347,6 +348,408 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmProblem p, Til
     }
 }
 
+// ---- direct-to-LDS multi-stage pipeline (per-channel / raw int32) -------------------
+//
+// BN x BM output tile (BN weight rows, BM token rows), 128-byte K-tiles, STAGES LDS
+// stages of (BN + BM) x 128 bytes. Tiles are copied L2 -> LDS with
+// global_load_lds_dwordx4 (no VGPR staging): one instruction moves 1 KiB = 8 rows x 128
+// bytes, lane i writing LDS bytes [16 i, 16 i + 16) of that block, so the chunk swizzle
+// is applied on the global side (lane i fetches logical chunk (i % 8) ^ ((row >> 1) & 7)
+// of its row). 128-byte row segments matter: measured on gfx950, DMA of 128-byte row
+// segments streams at ~58 B/clk per CU, 64-byte segments at ~39.
+// Each wave keeps the fragments of one 64-byte K-step in registers while the MFMAs of
+// the other run:
+//
+//   loop kt:  DMA stage kt+STAGES-1 into the buffer freed by stage kt-1
+//             read frags(kt, ks1);  MFMAs(ks0)
+//             retire own LDS reads and own DMA of stage kt+1; barrier
+//             read frags(kt+1, ks0); MFMAs(ks1); retire those reads
+//
+// With 3 stages the DMA of a stage has about 1.5 K-tiles of MFMA time to land.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+__device__ __forceinline__ void dma_16B(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)l, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+// Workgroup barrier that the compiler may not move memory operations across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BN_, int BM_, int STAGES_, int WGN_, int WGM_>
+struct MsShape {
+    static constexpr int BN = BN_, BM = BM_, BK = 128, STAGES = STAGES_, WGN = WGN_, WGM = WGM_;
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int FM = WM / 16, FN = WN / 16;
+    static constexpr int W_TILE = BN * BK, STAGE = (BM + BN) * BK;
+    static constexpr int GROUPS = (BM + BN) / 8;          // 1 KiB row groups per stage
+    static constexpr int GPW = (GROUPS + NW - 1) / NW;    // DMA instructions per wave (max)
+    static constexpr int FULL_WAVES = GROUPS - (GPW - 1) * NW;  // waves that issue GPW, others GPW-1
+    static_assert(BN % 8 == 0 && BM % 8 == 0 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
+    static_assert(STAGES * STAGE <= 163840, "LDS");
+};
+
+template <class S>
+__device__ __forceinline__ void ms_issue(const int8_t *const (&src)[S::GPW], int koff, int8_t *stage_base,
+                                         int wave) {
+#pragma unroll
+    for (int j = 0; j < S::GPW; ++j) {
+        if (j < S::GPW - 1 || wave < S::FULL_WAVES)
+            dma_16B(src[j] + koff, stage_base + (wave + j * S::NW) * 1024);
+    }
+}
+
+// vmcnt wait for "all but the last `stages_after` stages of this wave's DMA".
+template <class S>
+__device__ __forceinline__ void ms_wait_dma(int stages_after, int wave) {
+    constexpr int G = S::GPW, g = S::GPW - 1;
+    const bool full = wave < S::FULL_WAVES;
+    if (stages_after <= 0) {
+        wait_vmcnt<0>();
+    } else if (stages_after == 1) {
+        if (full) wait_vmcnt<G>(); else wait_vmcnt<g>();
+    } else {
+        if (full) wait_vmcnt<(2 * G < 63 ? 2 * G : 63)>(); else wait_vmcnt<(2 * g < 63 ? 2 * g : 63)>();
+    }
+}
+
+template <class S>
+__device__ __forceinline__ void ms_frags(const int8_t *st, int ks, int wm, int wn, int frow, int fchunk,
+                                         v4i (&a)[S::FN], v4i (&b)[S::FM]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn)
+        a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(wn * S::WN + fn * 16 + frow, ks * 4 + fchunk));
+#pragma unroll
+    for (int fm = 0; fm < S::FM; ++fm)
+        b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE +
+                                               swz<128>(wm * S::WM + fm * 16 + frow, ks * 4 + fchunk));
+}
+
+template <class S>
+__device__ __forceinline__ void ms_mma(v4i (&acc)[S::FN][S::FM], const v4i (&a)[S::FN], const v4i (&b)[S::FM]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < S::FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+}
+
+template <int BN, int BM, int STAGES, int WGN, int WGM>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_ms_kernel(GemmProblem p, TileMap tmap) {
+    using S = MsShape<BN, BM, STAGES, WGN, WGM>;
+    constexpr int FM = S::FM, FN = S::FN, GPW = S::GPW;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * S::STAGE];
+
+    int tm, tn;
+    map_tile(tmap, tm, tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WGN, wm = wave / WGN;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    // Loader: wave w issues row groups g = w + j * NW of each stage (groups below BN / 8
+    // are weight rows, the rest token rows); lane i covers row 8 g + i / 8 of the stage.
+    const int8_t *src[GPW];
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int g = min(wave + j * S::NW, S::GROUPS - 1);
+        const bool is_w = g < BN / 8;
+        const int lrow = (is_w ? g : g - BN / 8) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((lrow >> 1) & 7);
+        const int grow = is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
+        src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + 16 * c);
+    }
+
+    v4i acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int KT = K / S::BK;
+    // prologue: stages 0 .. STAGES-2 in flight, wait for stage 0
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) ms_issue<S>(src, s * S::BK, smem + s * S::STAGE, wave);
+    ms_wait_dma<S>(min(STAGES - 2, KT - 1), wave);
+    lds_barrier();
+
+    v4i a0[FN], b0[FM], a1[FN], b1[FM];
+    ms_frags<S>(smem, 0, wm, wn, frow, fchunk, a0, b0);
+    wait_lgkmcnt0();
+    int cur = 0;  // buffer of stage kt
+    for (int kt = 0; kt < KT; ++kt) {
+        // the buffer of stage kt-1 was released by the barrier of the previous iteration
+        const int fill = kt + STAGES - 1;
+        if (fill < KT) {
+            int fb = cur + STAGES - 1;
+            fb -= fb >= STAGES ? STAGES : 0;
+            ms_issue<S>(src, fill * S::BK, smem + fb * S::STAGE, wave);
+        }
+        const int8_t *st = smem + cur * S::STAGE;
+        ms_frags<S>(st, 1, wm, wn, frow, fchunk, a1, b1);
+        ms_mma<S>(acc, a0, b0);
+        wait_lgkmcnt0();
+        if (kt + 1 < KT) {
+            // DMA issued after stage kt+1: stages kt+2 .. min(kt+STAGES-1, KT-1)
+            ms_wait_dma<S>(min(STAGES - 2, KT - 2 - kt), wave);
+            lds_barrier();
+            int nb = cur + 1;
+            nb -= nb >= STAGES ? STAGES : 0;
+            ms_frags<S>(smem + nb * S::STAGE, 0, wm, wn, frow, fchunk, a0, b0);
+            cur = nb;
+        }
+        ms_mma<S>(acc, a1, b1);
+        wait_lgkmcnt0();
+    }
+
+    // ---- epilogue (per-channel dequant or raw int32) ----
+    // All scale loads are issued before the first store: y may alias nothing the
+    // compiler can see, so loads placed between stores would each be serialized
+    // behind the previous store.
+    const float *__restrict__ sxp = p.sx;
+    const float *__restrict__ swp = p.sw;
+    float sxm[FM];
+    float4 s4[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sxm[fm] = sxp[min(m0 + wm * S::WM + fm * 16 + frow, M - 1)];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        s4[fn] = *reinterpret_cast<const float4 *>(swp + min(n0 + wn * S::WN + fn * 16 + 4 * fchunk, N - 4));
+    const int out = p.out;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm * S::WM + fm * 16 + frow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+            if (n >= N) continue;
+            const int64_t off = (int64_t)m * p.ldy + n;
+            const v4i v = acc[fn][fm];
+            if (out == OUT_I32) {
+                *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = make_int4(v[0], v[1], v[2], v[3]);
+            } else {
+                store4(p.y, off, out, ((float)v[0] * sxm[fm]) * s4[fn].x, ((float)v[1] * sxm[fm]) * s4[fn].y,
+                       ((float)v[2] * sxm[fm]) * s4[fn].z, ((float)v[3] * sxm[fm]) * s4[fn].w);
+            }
+        }
+    }
+}
+
+// ---- weights through LDS, activations direct to registers ----------------------------
+//
+// Measured on gfx950: LDS serves about 128 B/clk per CU for ds_read_b128 and DMA writes
+// combined. A tile that stages both operands in LDS spends most of that on operand
+// re-reads, so here only the weight tile goes through LDS; activation fragments are
+// loaded straight from L2 into VGPRs, where the MFMA B operand wants them.
+//
+// Tile: 256 weight rows (n) x 256 tokens (m), 128-byte K-tiles, 4 * WGN waves; wave
+// (wn, wm) covers n in [wn * 256 / WGN, ...) and tokens [64 wm, 64 wm + 64). With WGN = 2
+// (8 waves, two per SIMD) a wave holds 8 x 4 MFMA 16x16x64 accumulators (128 VGPRs).
+// Weight K-tiles stream through a 4-deep LDS ring (32 KiB each) by global_load_lds.
+// A K-tile is 2 * FN weight fragments per wave (FN n-blocks x 2 K-steps); every
+// fragment feeds 4 MFMAs and is read from LDS WIN fragments ahead of its use. Per K-tile t:
+//
+//   top:  load x fragments of K-tile t+1 (VGPR double buffer)
+//   fragments of K-step 0 and 1, each: 4 MFMAs, read fragment f + WIN
+//   mid (after the last read of stage t was issued):
+//         wait own weight DMA of stage t+1; barrier; DMA weight stage t+3 into the
+//         buffer of stage t-1 (free: every wave passed this barrier after finishing it)
+//   the reads that run past the K-tile fetch stage t+1
+//   end:  wait x of K-tile t+1
+//
+// VMEM issue order is x(t+1) at the top, weights(t+3) at mid; global loads return in
+// order, so the vmcnt limits below count exactly the loads issued after the one needed.
+// LDS traffic per K-tile: 32 KiB DMA + 128 KiB fragment reads over 2048 MFMA cycles/SIMD.
+template <int WGN_>
+struct XdShape {
+    static constexpr int WGN = WGN_;
+    static constexpr int BN = 256, BM = 256, BK = 128, STAGES = 4, NW = 4 * WGN;
+    static constexpr int WM = 64, FM = 4, WN = BN / WGN, FN = WN / 16, NFRAG = 2 * FN, WIN = 4;
+    static constexpr int STAGE = BN * BK;      // 32 KiB of weights
+    static constexpr int GPW = (BN / 8) / NW;  // weight DMA instructions per wave per stage
+    static constexpr int XL = FM * 2;          // x load instructions per wave per K-tile (8)
+    static constexpr int MID = NFRAG - 1 - WIN;  // last fragment index whose prefetch is in stage t
+};
+
+template <class S>
+__device__ __forceinline__ const v4i *xd_frag_ptr(const int8_t *st, int f, int wn, int frow, int fchunk) {
+    // fragment f: n-block f % FN of this wave, K-step f / FN
+    return reinterpret_cast<const v4i *>(
+        st + swz<128>(wn * S::WN + (f % S::FN) * 16 + frow, (f / S::FN) * 4 + fchunk));
+}
+
+template <class S>
+__device__ __forceinline__ void xd_load_x(const int8_t *const (&xrow)[S::FM], int k0, int fchunk,
+                                          v4i (&x)[S::FM][2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int fm = 0; fm < S::FM; ++fm)
+            x[fm][ks] = *reinterpret_cast<const v4i *>(xrow[fm] + k0 + ks * 64 + fchunk * 16);
+}
+
+template <class S>
+__device__ __forceinline__ void xd_issue_w(const int8_t *const (&wsrc)[S::GPW], int k0, int8_t *dst, int wave) {
+#pragma unroll
+    for (int j = 0; j < S::GPW; ++j) dma_16B(wsrc[j] + k0, dst + (wave + j * S::NW) * 1024);
+}
+
+// One K-tile of the main loop (X = x fragments of this K-tile, XN = buffer for the next).
+// STEADY: t + 3 < KT is known, so the body has no data-dependent branches.
+template <class S, bool STEADY>
+__device__ __forceinline__ void xd_ktile(int t, int KT, int8_t *smem, const int8_t *const (&wsrc)[S::GPW],
+                                         const int8_t *const (&xrow)[S::FM], int wave, int wn, int frow,
+                                         int fchunk, v4i (&win)[S::WIN], v4i (&acc)[S::FN][S::FM],
+                                         const v4i (&X)[S::FM][2], v4i (&XN)[S::FM][2]) {
+    if (STEADY || t + 1 < KT) xd_load_x<S>(xrow, (t + 1) * S::BK, fchunk, XN);
+    const int8_t *st = smem + (t & 3) * S::STAGE;
+    const int8_t *st_next = smem + ((t + 1) & 3) * S::STAGE;
+#pragma unroll
+    for (int f = 0; f < S::NFRAG; ++f) {
+        const v4i a = win[f % S::WIN];
+        const int fr = f + S::WIN;  // fragment to prefetch into this window slot
+        if (fr < S::NFRAG)
+            win[f % S::WIN] = *xd_frag_ptr<S>(st, fr, wn, frow, fchunk);
+        else if (STEADY || t + 1 < KT)
+            win[f % S::WIN] = *xd_frag_ptr<S>(st_next, fr - S::NFRAG, wn, frow, fchunk);
+        const int ks = f / S::FN, fn = f % S::FN;
+#pragma unroll
+        for (int fm = 0; fm < S::FM; ++fm) acc[fn][fm] = mfma_i8(a, X[fm][ks], acc[fn][fm]);
+        if (f == S::MID) {
+            // every read issued so far is of stage t; the next one is of stage t+1
+            if (STEADY) {
+                // loads issued after weight stage t+1: x(t), w(t+2), x(t+1)
+                wait_vmcnt<S::GPW + 2 * S::XL>();
+                lds_barrier();
+                xd_issue_w<S>(wsrc, (t + 3) * S::BK, smem + ((t + 3) & 3) * S::STAGE, wave);
+            } else {
+                if (t + 1 < KT) {
+                    if (t + 2 < KT) wait_vmcnt<S::GPW + 2 * S::XL>();
+                    else wait_vmcnt<2 * S::XL>();
+                    lds_barrier();
+                }
+                if (t + 3 < KT) xd_issue_w<S>(wsrc, (t + 3) * S::BK, smem + ((t + 3) & 3) * S::STAGE, wave);
+            }
+        }
+    }
+    // x(t+1) must be complete before the next K-tile; only weights(t+3) may still fly
+    if (STEADY || t + 3 < KT) wait_vmcnt<S::GPW>();
+    else wait_vmcnt<0>();
+}
+
+template <int WGN>
+__global__ __launch_bounds__(256 * WGN) void gemm_xd_kernel(GemmProblem p, TileMap tmap) {
+    using S = XdShape<WGN>;
+    constexpr int FM = S::FM, FN = S::FN, GPW = S::GPW;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[S::STAGES * S::STAGE];
+
+    int tm, tn;
+    map_tile(tmap, tm, tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WGN, wm = wave / WGN;
+    const int m0 = tm * S::BM, n0 = tn * S::BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int frow = lane & 15, fchunk = lane >> 4;
+
+    // weight DMA: wave w issues row groups g = w + NW j (8 rows x 128 B each) of every stage
+    const int8_t *wsrc[GPW];
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int lrow = (wave + j * S::NW) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((lrow >> 1) & 7);
+        wsrc[j] = static_cast<const int8_t *>(p.wq) + ((int64_t)min(n0 + lrow, N - 1) * K + 16 * c);
+    }
+    // activation rows of this wave's fragments
+    const int8_t *xrow[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+        xrow[fm] = p.xq + (int64_t)min(m0 + wm * S::WM + fm * 16 + frow, M - 1) * K;
+
+    v4i acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    const int KT = K / S::BK;
+    // prologue: x(0), weight stages 0..2; everything waited
+    v4i xa[FM][2], xb[FM][2];
+    xd_load_x<S>(xrow, 0, fchunk, xa);
+#pragma unroll
+    for (int s = 0; s < S::STAGES - 1; ++s)
+        if (s < KT) xd_issue_w<S>(wsrc, s * S::BK, smem + s * S::STAGE, wave);
+    wait_vmcnt<0>();
+    lds_barrier();
+    v4i win[S::WIN];
+#pragma unroll
+    for (int i = 0; i < S::WIN; ++i) win[i] = *xd_frag_ptr<S>(smem, i, wn, frow, fchunk);
+
+    // steady state, two K-tiles per trip so the x buffers alternate statically
+    int t = 0;
+    for (; t + 4 < KT; t += 2) {
+        xd_ktile<S, true>(t, KT, smem, wsrc, xrow, wave, wn, frow, fchunk, win, acc, xa, xb);
+        xd_ktile<S, true>(t + 1, KT, smem, wsrc, xrow, wave, wn, frow, fchunk, win, acc, xb, xa);
+    }
+    // last K-tiles (at most 4)
+    for (; t < KT; t += 2) {
+        xd_ktile<S, false>(t, KT, smem, wsrc, xrow, wave, wn, frow, fchunk, win, acc, xa, xb);
+        if (t + 1 < KT) xd_ktile<S, false>(t + 1, KT, smem, wsrc, xrow, wave, wn, frow, fchunk, win, acc, xb, xa);
+    }
+
+    // ---- epilogue (per-channel dequant or raw int32) ----
+    const float *__restrict__ sxp = p.sx;
+    const float *__restrict__ swp = p.sw;
+    float sxm[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sxm[fm] = sxp[min(m0 + wm * S::WM + fm * 16 + frow, M - 1)];
+    const int out = p.out;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+        const float4 s4 = *reinterpret_cast<const float4 *>(swp + min(n, N - 4));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + wm * S::WM + fm * 16 + frow;
+            if (m >= M || n >= N) continue;
+            const int64_t off = (int64_t)m * p.ldy + n;
+            const v4i v = acc[fn][fm];
+            if (out == OUT_I32) {
+                *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = make_int4(v[0], v[1], v[2], v[3]);
+            } else {
+                store4(p.y, off, out, ((float)v[0] * sxm[fm]) * s4.x, ((float)v[1] * sxm[fm]) * s4.y,
+                       ((float)v[2] * sxm[fm]) * s4.z, ((float)v[3] * sxm[fm]) * s4.w);
+            }
+        }
+    }
+}
+
+template <int WGN>
+hipError_t launch_xd(const GemmProblem &p, int group_m, hipStream_t stream) {
+    TileMap t;
+    t.tiles_m = (p.M + 255) / 256;
+    t.tiles_n = (p.N + 255) / 256;
+    t.group_m = group_m;
+    dim3 grid(t.tiles_m * t.tiles_n), block(256 * WGN);
+    hipLaunchKernelGGL(gemm_xd_kernel<WGN>, grid, block, 0, stream, p, t);
+    return hipGetLastError();
+}
+
+
 // ---- configuration table ------------------------------------------------------------
 
 struct Config {
@@ -360,6 +763,11 @@ constexpr Config kConfigs[] = {
     {256, 128, 4},  // 2: 4 waves, 128x64 per wave
     {128, 256, 4},  // 3: 4 waves, 64x128 per wave
     {64, 64, 4},    // 4: 4 waves, 32x32 per wave (small M / narrow N)
+    {256, 256, 4},  // 5: direct-to-LDS, BN=256 BM=256, 2 stages, 8 waves (64 n x 128 m each)
+    {256, 160, 4},  // 6: direct-to-LDS, BN=160 BM=256, 3 stages, 8 waves (80 n x 64 m each)
+    {256, 128, 4},  // 7: direct-to-LDS, BN=128 BM=256, 3 stages, 8 waves (64 n x 64 m each)
+    {256, 256, 4},  // 8: weights via 4-stage LDS ring, activations direct, 4 waves (256 n x 64 m each)
+    {256, 256, 4},  // 9: weights via 4-stage LDS ring, activations direct, 8 waves (128 n x 64 m each)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -393,11 +801,27 @@ hipError_t launch_grouped(const GemmProblem &p, int group_m, hipStream_t stream)
     return launch_cfg<BM, BN, WGM, WGN, 128, W_INT8>(p, group_m, stream);
 }
 
+template <int BN, int BM, int STAGES, int WGN, int WGM>
+hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
+    TileMap t;
+    t.tiles_m = (p.M + BM - 1) / BM;
+    t.tiles_n = (p.N + BN - 1) / BN;
+    t.group_m = group_m;
+    dim3 grid(t.tiles_m * t.tiles_n), block(64 * WGM * WGN);
+    hipLaunchKernelGGL((gemm_ms_kernel<BN, BM, STAGES, WGN, WGM>), grid, block, 0, stream, p, t);
+    return hipGetLastError();
+}
+
 int choose_config(const GemmProblem &p) {
-    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel is
+    // fastest when it fills the chip; the 128 x 256 variant next; small M uses 64 x 64 tiles.
     if (p.M <= 128) return 4;
-    if (big_tiles >= 256) return 1;
-    return 0;
+    if (p.K % 128 != 0 || p.wkind != W_INT8) return 1;
+    const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
+    if (t6 >= 256) return 6;
+    const int64_t t7 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
+    if (t7 >= 48) return 7;
+    return 4;
 }
 
 }  // namespace
@@ -414,7 +838,14 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         return launch_grouped<128, 128, 2, 2>(p, gm, stream);
     }
     const int gm = kConfigs[id].group_m;
+    const bool dma_ok = p.K % 128 == 0 && p.wkind == W_INT8;
+    if (id >= 5 && !dma_ok) id = 1;
     switch (id) {
+        case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
+        case 6: return launch_ms<160, 256, 3, 2, 4>(p, gm, stream);
+        case 7: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
+        case 8: return launch_xd<1>(p, gm, stream);
+        case 9: return launch_xd<2>(p, gm, stream);
         case 0: return launch_shape<128, 128, 2, 2>(p, gm, stream);
         case 1: return launch_shape<256, 256, 2, 4>(p, gm, stream);
         case 2: return launch_shape<256, 128, 2, 2>(p, gm, stream);
