@@ -293,3 +293,24 @@ def test_qwen3_block_sampled(w8a8):
             owq, osw = oracle.quantize_weight(W, 8, 0)
             r = oracle.linear_pc(x[rows], owq, osw)
             check_output(y[rows], "bf16", r["y"], np.abs(r["y"]), 1, f"qwen3 {name}")
+
+
+def test_quantize_all_fp16_values_sampled_maxima(w8a8):
+    """For 96 row maxima (extremes + random), a row holding every fp16 value of magnitude
+    <= the maximum, both signs: codes and scales bit-exact against the oracle's IEEE
+    division (covers every quotient the per-row reciprocal path can meet for those rows)."""
+    note("quantize: all fp16 element values under sampled maxima")
+    rng = np.random.default_rng(31)
+    maxima = np.concatenate([[1, 2, 0x3C00, 0x7BFF, 0x7BFE, 0x0400, 0x03FF, 0x5BF0],
+                             rng.integers(1, 0x7C00, 88)]).astype(np.uint16)
+    K = 2 * 0x7C00  # room for every magnitude of both signs
+    rows = np.zeros((len(maxima), K), np.uint16)
+    for i, mb in enumerate(maxima):
+        mags = np.arange(0, int(mb) + 1, dtype=np.uint16)
+        vals = np.concatenate([mags, mags | 0x8000])
+        rows[i, :len(vals)] = vals
+    x = rows.view(np.float16)
+    xq, sx = gpu_quantize(w8a8, x)
+    rq, rs = oracle.quantize_per_token(x)
+    assert (sx.view(np.uint32) == rs.view(np.uint32)).all()
+    assert (xq == rq).all()
