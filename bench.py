@@ -14,13 +14,20 @@ the timed region) and a cpu_baseline object (the CPU oracle timed on a bounded
 sample of the same workload on the host cores).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1]
+       [--workload pc|pg64|pg128|w4|m1] [--copy-ref-mb MB]
+
+roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
+WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
+counters measured on a plain copy of known size; it is reported only while the GEMM
+source still has the hash recorded there, else null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +35,8 @@ import numpy as np
 
 PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E, 8 TB/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "w8a8_activation_quantized_amd", "csrc", "gemm.hip")
 
 # name -> (M, N, K, weight bits, group size)
 WORKLOADS = {
@@ -48,7 +57,29 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle sample")
+    ap.add_argument("--copy-ref-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a counter reference)")
     return ap.parse_args()
+
+
+def gemm_source_sha():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^\s*-?\s*(\w+)\s*=\s*(\S+)\s*$", text, flags=re.M))
+    if fields.get("gemm_source_sha256") != gemm_source_sha():
+        return None
+    try:
+        return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(x, W, bits, gs, budget_s):
@@ -98,6 +129,13 @@ def main():
         print("no gfx950 GPU available: " + w8a8.w8a8_last_error(), file=sys.stderr)
         return 1
 
+    if args.copy_ref_mb:
+        src = torch.empty(args.copy_ref_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     M, N, K, bits, gs = WORKLOADS[args.workload]
     x_np, W_np = linear_inputs(M, N, K, seed=0)
     x = torch.from_numpy(x_np).cuda()
@@ -120,19 +158,20 @@ def main():
             w8a8.w8a8_gemm_pc(xq, sx, wq, sw, y=y, stream=stream)
 
     def step(ev=None):
-        w8a8.quantize_per_token(x, xq, sx, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        gemm()
+        w8a8.quantize_per_token(x, xq, sx, stream=stream)
         if ev is not None:
             ev[1].record(stream)
+        gemm()
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -141,7 +180,8 @@ def main():
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in events]))
+    gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in events]))
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
 
@@ -150,11 +190,12 @@ def main():
         alg_bytes = wbytes + K * 1 + 4 + N * 2  # weights + scales, x_q + s_x in, y out
         achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
     else:
         achieved = ops / (gemm_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                    "frac": achieved / PEAK_INT8_TOPS, "traffic": None}
+                    "frac": achieved / PEAK_INT8_TOPS, "traffic": measured_traffic(args.workload),
+                    "kernel": "gemm (int8 MFMA, fused per-channel dequant)", "launch_ms": gemm_ms}
 
     result = {
         "metric": f"INT8 TOPS & % MFMA peak of fused quant-GEMM-dequant, M={M} N={N} K={K}",
@@ -174,6 +215,8 @@ def main():
                    "parallelism": "single GPU"},
         "frac_of_peak_step": value / PEAK_INT8_TOPS,
         "gemm_ms": gemm_ms,
+        "quantize_ms": quant_ms,
+        "quantize_gbs": (3.0 * M * K + 4 * M) / (quant_ms * 1e-3) / 1e9,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
