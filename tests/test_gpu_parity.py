@@ -180,7 +180,8 @@ def compare(yt, r, what):
     check_output(host(yt), OUT_FMT[yt.dtype], r["y"], r["mag"], r["G"], what)
 
 
-SHAPES = [(37, 272, 384), (300, 1040, 2560), (128, 512, 640), (1, 16, 128), (65, 48, 256), (513, 272, 1280)]
+SHAPES = [(37, 272, 384), (300, 1040, 2560), (128, 512, 640), (1, 16, 128), (65, 48, 256), (513, 272, 1280),
+          (16, 272, 1280), (7, 1040, 640), (2, 48, 10240)]
 
 
 @pytest.mark.parametrize("mode", MODES)

@@ -374,17 +374,28 @@ __device__ __forceinline__ void dma_16B(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)l, 16, 0, 0);
 }
 
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding). The waits and
+// the barrier are fenced with sched_barrier(0): the instruction scheduler otherwise moves
+// MFMAs (which touch no memory) across them, so a wait meant to trail a run of MFMAs ends
+// up ahead of it and exposes the latency it was placed to hide.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+    __builtin_amdgcn_sched_barrier(0);
 }
 // Workgroup barrier that the compiler may not move memory operations across.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int BN_, int BM_, int STAGES_, int WGN_, int WGM_>
 struct MsShape {
@@ -750,6 +761,148 @@ hipError_t launch_xd(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 
+// ---- small-M path: weight-streaming GEMV on matrix cores ------------------------------
+//
+// For M <= 16 the layer is bound by streaming the weights once from HBM. A workgroup owns
+// 16 output rows; its S waves split K into S contiguous segments (whole groups for the
+// per-group path). Each lane loads its MFMA fragments straight from global memory (16
+// bytes of a weight row, 8 for int4; the token fragment from the small x_q), so no LDS is
+// needed on the way in. Tokens m >= M read row M-1 and their results are discarded. The
+// S partial tiles are summed through LDS in segment order by wave 0 (int32 for
+// per-channel: exact; fp32 for per-group), which also applies the dequant and stores.
+template <int GS, int WK, int S>
+__global__ __launch_bounds__(64 * S) void gemv_kernel(GemmProblem p, int seg_steps) {
+    constexpr bool GROUPED = GS > 0;
+    constexpr int CH = 8;  // K-steps (64 bytes each) loaded per batch
+    __shared__ __attribute__((aligned(16))) float redf[GROUPED ? S : 1][64][4];
+    __shared__ __attribute__((aligned(16))) int redi[GROUPED ? 1 : S][64][4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int M = p.M, N = p.N, K = p.K;
+    const int G = GROUPED ? K / GS : 1;
+    const int KS = K / 64;
+    const int ks0 = wave * seg_steps, ks1 = min(KS, ks0 + seg_steps);
+
+    const int8_t *xrow = p.xq + (int64_t)min(frow, M - 1) * K;
+    const int nrow = min(n0 + frow, N - 1);
+    const int8_t *wrow8 = static_cast<const int8_t *>(p.wq) + (int64_t)nrow * K;
+    const uint8_t *wrow4 = static_cast<const uint8_t *>(p.wq) + (int64_t)nrow * (K / 2);
+
+    v4i acc = {0, 0, 0, 0};
+    float facc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = ks0; kb < ks1; kb += CH) {
+        v4i a[CH], b[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ks = min(kb + c, ks1 - 1);
+            if constexpr (WK == W_INT4) {
+                const uint2 w = *reinterpret_cast<const uint2 *>(wrow4 + ks * 32 + fchunk * 8);
+                a[c] = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
+            } else {
+                a[c] = *reinterpret_cast<const v4i *>(wrow8 + ks * 64 + fchunk * 16);
+            }
+            b[c] = *reinterpret_cast<const v4i *>(xrow + ks * 64 + fchunk * 16);
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ks = kb + c;
+            if (ks >= ks1) break;
+            if constexpr (GROUPED) {
+                constexpr int SPG = GS / 64;  // K-steps per group
+                acc = mfma_i8(a[c], b[c], (ks % SPG) == 0 ? v4i{0, 0, 0, 0} : acc);
+                if ((ks % SPG) == SPG - 1) {
+                    const int g = ks / SPG;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int n = min(n0 + 4 * fchunk + e, N - 1);
+                        facc[e] = __builtin_fmaf((float)acc[e], p.sw[(int64_t)n * G + g], facc[e]);
+                    }
+                }
+            } else {
+                acc = mfma_i8(a[c], b[c], acc);
+            }
+        }
+    }
+    // partials -> LDS, summed in segment order by wave 0 (int32 for per-channel: exact)
+    if constexpr (GROUPED) {
+        *reinterpret_cast<float4 *>(&redf[wave][lane][0]) = make_float4(facc[0], facc[1], facc[2], facc[3]);
+    } else {
+        *reinterpret_cast<int4 *>(&redi[wave][lane][0]) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int m = frow;
+    const int n = n0 + 4 * fchunk;
+    if (m >= M || n >= N) return;
+    const int64_t off = (int64_t)m * p.ldy + n;
+    if constexpr (GROUPED) {
+        float4 t = *reinterpret_cast<const float4 *>(&redf[0][lane][0]);
+#pragma unroll
+        for (int w = 1; w < S; ++w) {
+            const float4 u = *reinterpret_cast<const float4 *>(&redf[w][lane][0]);
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        const float sxm = p.sx[m];
+        store4(p.y, off, p.out, t.x * sxm, t.y * sxm, t.z * sxm, t.w * sxm);
+    } else {
+        int4 t = *reinterpret_cast<const int4 *>(&redi[0][lane][0]);
+#pragma unroll
+        for (int w = 1; w < S; ++w) {
+            const int4 u = *reinterpret_cast<const int4 *>(&redi[w][lane][0]);
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        if (p.out == OUT_I32) {
+            *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = t;
+            return;
+        }
+        const float sxm = p.sx[m];
+        const float4 s4 = *reinterpret_cast<const float4 *>(p.sw + n);
+        store4(p.y, off, p.out, ((float)t.x * sxm) * s4.x, ((float)t.y * sxm) * s4.y, ((float)t.z * sxm) * s4.z,
+               ((float)t.w * sxm) * s4.w);
+    }
+}
+
+template <int GS, int WK>
+hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream) {
+    const int KS = p.K / 64;
+    const int blocks = (p.N + 15) / 16;
+    // enough waves in flight: about 2560 in total, segments in whole groups
+    int S = 4;
+    if ((int64_t)blocks * 4 < 1280) S = 8;
+    if ((int64_t)blocks * 8 < 1280) S = 16;
+    const int unit = GS > 0 ? GS / 64 : 1;  // K-steps per group
+    int seg = (KS + S - 1) / S;
+    seg = (seg + unit - 1) / unit * unit;
+    dim3 grid(blocks);
+    switch (S) {
+        case 4: hipLaunchKernelGGL((gemv_kernel<GS, WK, 4>), grid, dim3(256), 0, stream, p, seg); break;
+        case 8: hipLaunchKernelGGL((gemv_kernel<GS, WK, 8>), grid, dim3(512), 0, stream, p, seg); break;
+        default: hipLaunchKernelGGL((gemv_kernel<GS, WK, 16>), grid, dim3(1024), 0, stream, p, seg); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t dispatch_gemv(const GemmProblem &p, hipStream_t stream) {
+    const int gs = p.out == OUT_I32 ? 0 : p.gs;
+    if (p.wkind == W_INT4) {
+        if (gs == 64) return launch_gemv<64, W_INT4>(p, stream);
+        if (gs == 128) return launch_gemv<128, W_INT4>(p, stream);
+        return launch_gemv<0, W_INT4>(p, stream);
+    }
+    if (gs == 64) return launch_gemv<64, W_INT8>(p, stream);
+    if (gs == 128) return launch_gemv<128, W_INT8>(p, stream);
+    return launch_gemv<0, W_INT8>(p, stream);
+}
+
 // ---- configuration table ------------------------------------------------------------
 
 struct Config {
@@ -768,6 +921,7 @@ constexpr Config kConfigs[] = {
     {256, 128, 4},  // 7: direct-to-LDS, BN=128 BM=256, 3 stages, 8 waves (64 n x 64 m each)
     {256, 256, 4},  // 8: weights via 4-stage LDS ring, activations direct, 4 waves (256 n x 64 m each)
     {256, 256, 4},  // 9: weights via 4-stage LDS ring, activations direct, 8 waves (128 n x 64 m each)
+    {16, 16, 1},    // 10: small-M weight-streaming GEMV (M <= 16)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -815,6 +969,7 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
 int choose_config(const GemmProblem &p) {
     // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel is
     // fastest when it fills the chip; the 128 x 256 variant next; small M uses 64 x 64 tiles.
+    if (p.M <= 16) return 10;
     if (p.M <= 128) return 4;
     if (p.K % 128 != 0 || p.wkind != W_INT8) return 1;
     const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
@@ -830,6 +985,10 @@ int gemm_num_configs() { return kNumConfigs; }
 
 hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) {
     int id = (force_cfg >= 0 && force_cfg < kNumConfigs) ? force_cfg : choose_config(p);
+    if (id == 10) {
+        if (p.M <= 16) return dispatch_gemv(p, stream);
+        id = 4;
+    }
     const bool grouped = p.gs > 0 && p.out != OUT_I32;
     if (grouped) {
         if (id != 4) id = 0;
