@@ -203,6 +203,21 @@ def test_gemm_strided_output_and_empty(w8a8):
     got = host(ybig)
     check_output(got[:, :272], "f16", r["y"], r["mag"], 1, "strided y")
     assert (got[:, 272:] == np.float16(7.0)).all()  # padding columns untouched
+    # row strides of 304 (16-byte rows: staged stores) and 276 (8-byte rows: direct
+    # stores), both 16-bit types, in the automatic choice and the DMA-pipeline kernels
+    try:
+        for cfg in (-1, 6, 7):
+            w8a8.w8a8_debug_force_config(cfg)
+            for ldy in (304, 276):
+                for out, fmt in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
+                    note(f"gemm strided y: config {cfg} ldy={ldy} {fmt}")
+                    ybig = torch.zeros((50, ldy), dtype=out, device="cuda")
+                    run_mode(w8a8, "pc", x, W, out, y=ybig[:, :272])
+                    got = host(ybig)
+                    check_output(got[:, :272], fmt, r["y"], r["mag"], 1, f"cfg {cfg} ldy={ldy} {fmt}")
+                    assert (got[:, 272:] == 0).all()
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
     xq = torch.zeros((0, 512), dtype=torch.int8, device="cuda")
     sx = torch.zeros((0,), dtype=torch.float32, device="cuda")
     wq = torch.zeros((272, 512), dtype=torch.int8, device="cuda")
@@ -274,6 +289,39 @@ def test_full_size_sampled(w8a8, mode, M, N, K):
             assert (y[rows] == r["acc"]).all(), "int32 accumulators differ"
         else:
             check_output(y[rows], "f16", r["y"], r["mag"], r["G"], f"{mode} {M}x{N}x{K}")
+
+
+def _bf16_rne_bits(f32: np.ndarray) -> np.ndarray:
+    u = f32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K,cfgs", [(300, 528, 1280, (-1, 0, 1, 4, 5, 6, 7)), (9, 1040, 640, (-1, 10, 4)),
+                                        (2000, 5280, 384, (-1, 6, 7))])
+def test_pc_epilogue_rounding_exact(w8a8, M, N, K, cfgs):
+    """Per-channel outputs are RNE of the fp32 value ((fp32)acc * s_x) * s_w, two fp32
+    roundings and then one to fp16/bf16, in every tile configuration: checked exactly
+    (not to a tolerance) from the GPU's own int32 accumulators and scales, which the
+    other tests hold bit-exact against the oracle. Catches a multiply fused into the
+    fp16 conversion (one rounding), which differs at fp16 ties only."""
+    x, W = linear_inputs(M, N, K, seed=17)
+    xq, sx = w8a8.quantize_per_token(dev(x))
+    wq, sw = w8a8.quantize_weight(dev(W), 8, 0)
+    try:
+        for cfg in cfgs:
+            w8a8.w8a8_debug_force_config(cfg)
+            note(f"epilogue rounding: config {cfg} M={M} N={N} K={K}")
+            acc = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.int32))
+            y32 = (acc.astype(np.float32) * host(sx)[:, None]) * host(sw)[None, :]
+            y16 = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.float16))
+            bad = np.argwhere(y16.view(np.uint16) != y32.astype(np.float16).view(np.uint16))
+            assert len(bad) == 0, f"config {cfg}: fp16 rounding differs at {bad[:4].tolist()}"
+            yb = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.bfloat16))
+            assert (yb == _bf16_rne_bits(y32)).all(), f"config {cfg}: bf16 rounding differs"
+            yf = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.float32))
+            assert (yf.view(np.uint32) == y32.view(np.uint32)).all(), f"config {cfg}: fp32 output differs"
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
 
 
 def test_qwen3_block_sampled(w8a8):

@@ -126,6 +126,10 @@ int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w,
     p.gs = gs;
     p.wkind = wkind;
     p.out = y_dtype;
+    {
+        const int64_t esize = (y_dtype == W8A8_F16 || y_dtype == W8A8_BF16) ? 2 : 4;
+        p.y_rows16 = ((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ((ldy * esize) & 15) == 0) ? 1 : 0;
+    }
     return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed),
                                       static_cast<hipStream_t>(stream)),
                     fn);

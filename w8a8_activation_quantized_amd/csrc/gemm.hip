@@ -37,6 +37,8 @@
 //    but not of the 128-byte K-tile ends in a half tile whose missing chunks are
 //    loaded from a clamped address and replaced by zero codes (int4: nibble 8),
 //    which add nothing to the integer sums.
+#include <atomic>
+
 #include "internal.h"
 
 namespace w8a8 {
@@ -85,7 +87,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return u >> 16;
 }
 
+// fp32 -> fp16 bits, RNE, of an fp32 value that has been rounded to fp32 first. The empty
+// asm pins the fp32 value in a register: without it the compiler may fold a preceding
+// fp32 multiply and this conversion into one v_fma_mixlo_f16, which rounds the exact
+// product once, straight to fp16, and differs from the two roundings at fp16 ties.
 __device__ __forceinline__ uint32_t f16_bits(float f) {
+    asm volatile("" : "+v"(f));
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
@@ -107,13 +114,9 @@ struct TileMap {
     int tiles_m, tiles_n, group_m;
 };
 
-// XCD-aware block -> (tile_m, tile_n).
-__device__ __forceinline__ void map_tile(const TileMap &t, int &tm, int &tn) {
-    const int T = t.tiles_m * t.tiles_n;
-    const int b = blockIdx.x;
-    const int x = b & 7, i = b >> 3;
-    const int q = T >> 3, r = T & 7;
-    const int logical = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+// Logical tile index -> (tile_m, tile_n): group_m M-tiles side by side, N-tiles in order
+// within a group, so consecutive logical tiles share activation and weight panels.
+__device__ __forceinline__ void logical_tile(const TileMap &t, int logical, int &tm, int &tn) {
     const int per_group = t.group_m * t.tiles_n;
     const int grp = logical / per_group;
     const int first_m = grp * t.group_m;
@@ -121,6 +124,17 @@ __device__ __forceinline__ void map_tile(const TileMap &t, int &tm, int &tn) {
     const int in_grp = logical - grp * per_group;
     tm = first_m + in_grp % gsize;
     tn = in_grp / gsize;
+}
+
+// XCD-aware block -> (tile_m, tile_n). Workgroups are dealt to the 8 XCDs round-robin
+// (block b runs on XCD b % 8), so XCD x is given one contiguous run of logical tiles and
+// its L2 sees the panels of that run only.
+__device__ __forceinline__ void map_tile(const TileMap &t, int &tm, int &tn) {
+    const int T = t.tiles_m * t.tiles_n;
+    const int b = blockIdx.x;
+    const int x = b & 7, i = b >> 3;
+    const int q = T >> 3, r = T & 7;
+    logical_tile(t, x * q + min(x, r) + i, tm, tn);
 }
 
 // Compile-time shape of one kernel instantiation.
@@ -447,6 +461,15 @@ __device__ __forceinline__ void ms_frags(const int8_t *st, int ks, int wm, int w
                                                swz<128>(wm * S::WM + fm * 16 + frow, ks * 4 + fchunk));
 }
 
+// Byte stride of a 16-bit output row staged in LDS: 16 bytes of padding against bank
+// conflicts between the 16 rows one MFMA fragment writes, when the pipeline buffers
+// have room for it.
+template <class S>
+constexpr int ms_out_row_stride() {
+    static_assert(S::BM * S::BN * 2 <= S::STAGES * S::STAGE, "staged output tile must fit the LDS buffers");
+    return S::BM * (S::BN * 2 + 16) <= S::STAGES * S::STAGE ? S::BN * 2 + 16 : S::BN * 2;
+}
+
 template <class S>
 __device__ __forceinline__ void ms_mma(v4i (&acc)[S::FN][S::FM], const v4i (&a)[S::FN], const v4i (&b)[S::FM]) {
 #pragma unroll
@@ -540,6 +563,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_ms_kernel(GemmProblem p, 
     for (int fn = 0; fn < FN; ++fn)
         s4[fn] = *reinterpret_cast<const float4 *>(swp + min(n0 + wn * S::WN + fn * 16 + 4 * fchunk, N - 4));
     const int out = p.out;
+    if ((out == OUT_F16 || out == OUT_BF16) && p.y_rows16) {
+        // 16-bit outputs go through LDS (the pipeline buffers are free once every wave has
+        // passed the barrier below) so that global stores are whole 16-byte pieces of
+        // output rows: lane-contiguous runs of a row instead of the MFMA layout's 8-byte
+        // pieces of 16 different rows, which store at about 60% of the rate.
+        constexpr int RS = ms_out_row_stride<S>();
+        lds_barrier();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int lr = wm * S::WM + fm * 16 + frow;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const v4i v = acc[fn][fm];
+                const float y0 = ((float)v[0] * sxm[fm]) * s4[fn].x, y1 = ((float)v[1] * sxm[fm]) * s4[fn].y;
+                const float y2 = ((float)v[2] * sxm[fm]) * s4[fn].z, y3 = ((float)v[3] * sxm[fm]) * s4[fn].w;
+                const uint2 w = out == OUT_F16 ? make_uint2(f16_bits(y0) | (f16_bits(y1) << 16), f16_bits(y2) | (f16_bits(y3) << 16))
+                                               : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
+                *reinterpret_cast<uint2 *>(smem + lr * RS + 2 * (wn * S::WN + fn * 16 + 4 * fchunk)) = w;
+            }
+        }
+        lds_barrier();
+        constexpr int CPR = S::BN / 8;  // 16-byte chunks per output row
+        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
+#pragma unroll 4
+        for (int c = tid; c < S::BM * CPR; c += S::NT) {
+            const int r = c / CPR, cc = c - r * CPR;
+            if (r < rows && cc * 8 < cols) {
+                const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
+                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int m = m0 + wm * S::WM + fm * 16 + frow;
@@ -966,17 +1022,31 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
     return hipGetLastError();
 }
 
+int num_cus() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cached.store(n, std::memory_order_relaxed);
+    return n;
+}
+
 int choose_config(const GemmProblem &p) {
-    // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel is
-    // fastest when it fills the chip; the 128 x 256 variant next; small M uses 64 x 64 tiles.
+    // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel (6)
+    // does the most work per unit time, the 128 x 256 one (7) about 0.9 of that per tile
+    // area. Pick the one with fewer chip-wide rounds of tiles times tile area (partial
+    // tiles cost a whole tile); small M uses 64 x 64 tiles.
     if (p.M <= 16) return 10;
     if (p.M <= 128) return 4;
     if (p.K % 128 != 0 || p.wkind != W_INT8) return 1;
-    const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
-    if (t6 >= 256) return 6;
-    const int64_t t7 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
-    if (t7 >= 48) return 7;
-    return 4;
+    const int64_t cus = num_cus();
+    const int64_t tm = (p.M + 255) / 256;
+    const int64_t t6 = tm * ((p.N + 159) / 160), t7 = tm * ((p.N + 127) / 128);
+    if (t7 < 48) return 4;
+    const int64_t cost6 = (t6 + cus - 1) / cus * 160 * 10, cost7 = (t7 + cus - 1) / cus * 128 * 11;
+    return cost6 <= cost7 ? 6 : 7;
 }
 
 }  // namespace

@@ -21,6 +21,7 @@ struct GemmProblem {
     int gs;            // 0 = per-channel, else 64 | 128
     int wkind;         // WeightKind
     int out;           // OutType
+    int y_rows16;      // 1 if y and the start of every output row are 16-byte aligned
 };
 
 // Activation quantization (fp16 / bf16 rows -> int8 + fp32 scale).
