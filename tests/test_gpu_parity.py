@@ -181,7 +181,7 @@ def compare(yt, r, what):
 
 
 SHAPES = [(37, 272, 384), (300, 1040, 2560), (128, 512, 640), (1, 16, 128), (65, 48, 256), (513, 272, 1280),
-          (16, 272, 1280), (7, 1040, 640), (2, 48, 10240)]
+          (16, 272, 1280), (7, 1040, 640), (2, 48, 10240), (9, 16, 12288), (3, 32, 4096)]
 
 
 @pytest.mark.parametrize("mode", MODES)

@@ -46,6 +46,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -113,6 +114,18 @@ __device__ __forceinline__ void store4(void *y, int64_t off, int out, float v0, 
 struct TileMap {
     int tiles_m, tiles_n, group_m;
 };
+
+// Compute units of the current device (cached after the first call).
+int num_cus() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cached.store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // Logical tile index -> (tile_m, tile_n): group_m M-tiles side by side, N-tiles in order
 // within a group, so consecutive logical tiles share activation and weight panels.
@@ -386,6 +399,10 @@ typedef const __attribute__((address_space(1))) void gbl_void_t;
 
 __device__ __forceinline__ void dma_16B(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)l, 16, 0, 0);
+}
+// 4-byte form: lane i writes LDS bytes [4 i, 4 i + 4) of the block at l.
+__device__ __forceinline__ void dma_4B(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)l, 4, 0, 0);
 }
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding). The waits and
@@ -820,21 +837,29 @@ hipError_t launch_xd(const GemmProblem &p, int group_m, hipStream_t stream) {
 // ---- small-M path: weight-streaming GEMV on matrix cores ------------------------------
 //
 // For M <= 16 the layer is bound by streaming the weights once from HBM. A workgroup owns
-// 16 output rows; its S waves split K into S contiguous segments (whole groups for the
-// per-group path). Each lane loads its MFMA fragments straight from global memory (16
-// bytes of a weight row, 8 for int4; the token fragment from the small x_q), so no LDS is
-// needed on the way in. Tokens m >= M read row M-1 and their results are discarded. The
-// S partial tiles are summed through LDS in segment order by wave 0 (int32 for
-// per-channel: exact; fp32 for per-group), which also applies the dequant and stores.
-template <int GS, int WK, int S>
-__global__ __launch_bounds__(64 * S) void gemv_kernel(GemmProblem p, int seg_steps) {
-    constexpr bool GROUPED = GS > 0;
-    constexpr int CH = 8;  // K-steps (64 bytes each) loaded per batch
-    __shared__ __attribute__((aligned(16))) float redf[GROUPED ? S : 1][64][4];
-    __shared__ __attribute__((aligned(16))) int redi[GROUPED ? 1 : S][64][4];
+// 16 output rows; its S waves (S = blockDim / 64, at most 8) split K into S contiguous
+// segments (whole groups for the per-group path) of at most CH K-steps, so that each
+// wave issues every weight load of its segment before its first MFMA: one HBM round
+// trip, with all waves of the grid resident at once. Each lane loads its MFMA fragments
+// straight from global memory (16 bytes of a weight row, 8 for int4; the token fragment
+// from the small x_q), so no LDS is needed on the way in. Tokens m >= M read row M-1 and
+// their results are discarded. The S partial tiles are summed through LDS in segment
+// order by wave 0 (int32 for per-channel: exact; fp32 for per-group), which also applies
+// the dequant and stores.
+constexpr int GEMV_MAX_WAVES = 8;
 
+template <int GS, int WK, int CH>
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(GemmProblem p, int seg_steps) {
+    constexpr bool GROUPED = GS > 0;
+    constexpr int SPG = GROUPED ? GS / 64 : 1;  // K-steps per group
+    constexpr int GPB = GROUPED ? CH / SPG : 1;  // groups per batch
+    static_assert(!GROUPED || CH % SPG == 0, "a batch holds whole groups");
+    __shared__ __attribute__((aligned(16))) float redf[GROUPED ? GEMV_MAX_WAVES : 1][64][4];
+    __shared__ __attribute__((aligned(16))) int redi[GROUPED ? 1 : GEMV_MAX_WAVES][64][4];
+
+    const int S = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int frow = lane & 15, fchunk = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int M = p.M, N = p.N, K = p.K;
@@ -850,35 +875,48 @@ __global__ __launch_bounds__(64 * S) void gemv_kernel(GemmProblem p, int seg_ste
     v4i acc = {0, 0, 0, 0};
     float facc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int kb = ks0; kb < ks1; kb += CH) {
-        v4i a[CH], b[CH];
+        // every load of the batch first (weights, then tokens, then group scales)
+        v4i a8[CH];
+        v2u a4[CH];
+        v4i b[CH];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int ks = min(kb + c, ks1 - 1);
-            if constexpr (WK == W_INT4) {
-                const uint2 w = *reinterpret_cast<const uint2 *>(wrow4 + ks * 32 + fchunk * 8);
-                a[c] = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
-            } else {
-                a[c] = *reinterpret_cast<const v4i *>(wrow8 + ks * 64 + fchunk * 16);
-            }
-            b[c] = *reinterpret_cast<const v4i *>(xrow + ks * 64 + fchunk * 16);
+            if constexpr (WK == W_INT4)
+                a4[c] = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(wrow4 + ks * 32 + fchunk * 8));
+            else
+                a8[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wrow8 + ks * 64 + fchunk * 16));
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int ks = kb + c;
-            if (ks >= ks1) break;
-            if constexpr (GROUPED) {
-                constexpr int SPG = GS / 64;  // K-steps per group
-                acc = mfma_i8(a[c], b[c], (ks % SPG) == 0 ? v4i{0, 0, 0, 0} : acc);
-                if ((ks % SPG) == SPG - 1) {
-                    const int g = ks / SPG;
+            const int ks = min(kb + c, ks1 - 1);
+            b[c] = *reinterpret_cast<const v4i *>(xrow + ks * 64 + fchunk * 16);
+        }
+        float sw[GROUPED ? GPB : 1][4];
+        if constexpr (GROUPED) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int n = min(n0 + 4 * fchunk + e, N - 1);
-                        facc[e] = __builtin_fmaf((float)acc[e], p.sw[(int64_t)n * G + g], facc[e]);
-                    }
+            for (int j = 0; j < GPB; ++j) {
+                const int g = min(kb / SPG + j, G - 1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sw[j][e] = p.sw[(int64_t)min(n0 + 4 * fchunk + e, N - 1) * G + g];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (kb + c >= ks1) continue;  // uniform; no early exit, so the loop unrolls fully
+            v4i a;
+            if constexpr (WK == W_INT4)
+                a = __builtin_bit_cast(v4i, unpack_nibbles(a4[c].x, a4[c].y));
+            else
+                a = a8[c];
+            if constexpr (GROUPED) {
+                acc = mfma_i8(a, b[c], (c % SPG) == 0 ? v4i{0, 0, 0, 0} : acc);
+                if ((c % SPG) == SPG - 1) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) facc[e] = __builtin_fmaf((float)acc[e], sw[c / SPG][e], facc[e]);
                 }
             } else {
-                acc = mfma_i8(a[c], b[c], acc);
+                acc = mfma_i8(a, b[c], acc);
             }
         }
     }
@@ -931,32 +969,333 @@ template <int GS, int WK>
 hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream) {
     const int KS = p.K / 64;
     const int blocks = (p.N + 15) / 16;
-    // enough waves in flight: about 2560 in total, segments in whole groups
-    int S = 4;
-    if ((int64_t)blocks * 4 < 1280) S = 8;
-    if ((int64_t)blocks * 8 < 1280) S = 16;
     const int unit = GS > 0 ? GS / 64 : 1;  // K-steps per group
+    // Waves per workgroup: segments of at most 16 K-steps (whole groups), and at least
+    // about 2048 waves in the grid while segments stay at 4 K-steps or more.
+    int S = (KS + 15) / 16;
+    while (S < GEMV_MAX_WAVES && (int64_t)blocks * S < 2048 && (KS + S) / (S + 1) >= 4) ++S;
+    S = min(S, GEMV_MAX_WAVES);
     int seg = (KS + S - 1) / S;
     seg = (seg + unit - 1) / unit * unit;
-    dim3 grid(blocks);
-    switch (S) {
-        case 4: hipLaunchKernelGGL((gemv_kernel<GS, WK, 4>), grid, dim3(256), 0, stream, p, seg); break;
-        case 8: hipLaunchKernelGGL((gemv_kernel<GS, WK, 8>), grid, dim3(512), 0, stream, p, seg); break;
-        default: hipLaunchKernelGGL((gemv_kernel<GS, WK, 16>), grid, dim3(1024), 0, stream, p, seg); break;
-    }
+    S = (KS + seg - 1) / seg;
+    dim3 grid(blocks), block(64 * S);
+    if (seg <= 8)
+        hipLaunchKernelGGL((gemv_kernel<GS, WK, 8>), grid, block, 0, stream, p, seg);
+    else
+        hipLaunchKernelGGL((gemv_kernel<GS, WK, 16>), grid, block, 0, stream, p, seg);
     return hipGetLastError();
+}
+
+// ---- small-M path with the weights staged through LDS --------------------------------
+//
+// Measured on MI355X: global loads in the MFMA operand layout (64 lanes taking 64 bytes
+// from each of 16 rows) stream from HBM at about 3.2 TB/s, while loads that take 128
+// contiguous bytes or more of each row run at the rate of a plain linear read (~4.1 TB/s
+// for a 26 MB matrix in one launch). So the weights go to LDS with global_load_lds in
+// pieces of 8 rows x 128 bytes and the fragments are read from there.
+//
+// A workgroup owns 16 output rows; its S waves split the row's 128-byte chunks into S
+// contiguous segments (whole groups for per-group scales). Each wave streams its segment
+// through a private ring of up to RING chunk slots (16 rows x 128 bytes, 2 KiB each), so
+// no data is shared between waves and no barrier is needed before the final reduction.
+// Within a slot, row r's 16-byte piece c sits at position c ^ ((r >> 1) & 7) (the swizzle
+// is applied to the DMA source addresses), which keeps the fragment reads free of bank
+// conflicts. With XL (when it fits in LDS) the wave's segment of the x_q rows is copied to LDS once,
+// up front, and the token fragments are read from there; otherwise (x_q is small and
+// stays in L2) they are loaded with each chunk's DMA. Loads that return little data still
+// hold a place in the CU's memory queue and retire in order behind the weight stream, so
+// at M = 1 half of the queue would carry 16 bytes of useful data per instruction. The
+// per-group scales of the wave's segment are put in an LDS table first.
+template <int GS, int WK, bool XL>
+struct GvShape {
+    static constexpr bool GROUPED = GS > 0;
+    static constexpr int KPC = WK == W_INT4 ? 256 : 128;  // k values per 128-byte chunk
+    static constexpr int SPC = KPC / 64;                  // K-steps per chunk
+    static constexpr int RING = WK == W_INT4 ? 4 : 8;     // slots per wave
+    static constexpr int OPS = XL ? 2 : 2 + SPC;          // vector-memory ops per chunk
+    static constexpr int SPG = GROUPED ? GS / 64 : 1;     // K-steps per group
+    static constexpr int GPC = GROUPED ? (SPC >= SPG ? SPC / SPG : 1) : 1;  // groups per chunk
+    static constexpr int CPG = GROUPED ? (SPG > SPC ? SPG / SPC : 1) : 1;   // chunks per group
+};
+
+template <class S, int N>
+__device__ __forceinline__ void gv_wait_tail(int after) {
+    // vmcnt wait allowing `after` chunks (S::OPS ops each) issued after the one needed
+    if constexpr (N > 0) {
+        if (after >= N) {
+            wait_vmcnt<S::OPS * N>();
+            return;
+        }
+        gv_wait_tail<S, N - 1>(after);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+template <int GS, int WK, bool XL>
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProblem p, int seg_chunks, int slots,
+                                                                        int table_groups) {
+    using S = GvShape<GS, WK, XL>;
+    constexpr int RING = S::RING, SPC = S::SPC;
+    extern __shared__ __attribute__((aligned(1024))) int8_t gv_lds[];
+
+    const int NW = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int M = p.M, N = p.N, K = p.K;
+    const int G = S::GROUPED ? K / GS : 1;
+    const int NCH = K / S::KPC;
+    const int c0 = wave * seg_chunks, nch = max(min(NCH, c0 + seg_chunks) - c0, 0);
+    const int RB = WK == W_INT4 ? K / 2 : K;  // bytes per weight row
+
+    int8_t *my_ring = gv_lds + wave * slots * 2048;
+    float *table = reinterpret_cast<float *>(gv_lds + NW * slots * 2048) + wave * table_groups * 16;
+    // XL region of this wave: room for M rows of seg_chunks * KPC bytes (rounded up to 1 KiB)
+    const int xl_bytes = (M * seg_chunks * S::KPC + 1023) & ~1023;
+    int8_t *xl = gv_lds + NW * slots * 2048 + NW * table_groups * 64 + wave * xl_bytes;
+
+    // the epilogue's scales, fetched first so that they arrive with the weight stream
+    // (retired by the first chunk wait: they precede every DMA)
+    const int em = min(frow, M - 1), en = min(n0 + 4 * fchunk, N - 4);
+    float e_sx = 0.f;
+    float4 e_sw = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (wave == 0) {
+        e_sx = p.sx[em];
+        if constexpr (!S::GROUPED) e_sw = *reinterpret_cast<const float4 *>(p.sw + en);
+    }
+
+    // per-group scales of this wave's segment: table[(g - g0) * 16 + r] = s_w[n0 + r, g],
+    // copied with 4-byte DMA (64 entries per instruction; table_groups is a multiple of 4)
+    // so that no register waits on them: the first chunk wait retires them
+    const int g0 = S::GROUPED ? (c0 * SPC) / S::SPG : 0;
+    if constexpr (S::GROUPED) {
+        const int ng = min(G - g0, table_groups);
+        for (int b = 0; b * 64 < ng * 16; ++b) {
+            const int e = b * 64 + lane;
+            const int gg = min(e >> 4, ng - 1), r = e & 15;
+            dma_4B(p.sw + (int64_t)min(n0 + r, N - 1) * G + g0 + gg, table + b * 64);
+        }
+    }
+
+    // DMA roles: lane i of a piece covers row (half * 8 + i / 8), slot position i % 8,
+    // which holds the row's logical 16-byte piece (i % 8) ^ ((row >> 1) & 7)
+    const int dr = lane >> 3, dpos = lane & 7;
+    const uint8_t *W = static_cast<const uint8_t *>(p.wq);
+    const uint8_t *src_lo = W + (int64_t)min(n0 + dr, N - 1) * RB + 16 * (dpos ^ ((dr >> 1) & 7));
+    const uint8_t *src_hi = W + (int64_t)min(n0 + 8 + dr, N - 1) * RB + 16 * (dpos ^ (((8 + dr) >> 1) & 7));
+    const int8_t *xrow = p.xq + (int64_t)min(frow, M - 1) * K;
+
+    v4i xf[RING][SPC];  // token fragments of the chunks in flight, by slot
+
+    // XL: rows 0..M-1 of x_q, bytes [c0 KPC, (c0 + nch) KPC) (this wave's chunks only, so
+    // never past the row end), stored flat with row stride xlr; 1 KiB per DMA, lane i
+    // taking flat byte 1024 b + 16 i (clamped to the last row's end)
+    const int xlr = nch * S::KPC;
+    if constexpr (XL) {
+        const int total = M * xlr;
+        for (int b = 0; b * 1024 < total; ++b) {
+            const int flat = min(b * 1024 + 16 * lane, total - 16);
+            const int r = flat / xlr, col = flat - r * xlr;
+            dma_16B(p.xq + (int64_t)r * K + c0 * S::KPC + col, xl + b * 1024);
+        }
+    }
+    const int8_t *xl_row = xl + min(frow, M - 1) * xlr;
+
+    v4i acc = {0, 0, 0, 0};
+    float facc[4] = {0.f, 0.f, 0.f, 0.f};
+    // One chunk's MFMAs from ring slot `slot` (token fragments from xl_row, or xf[s]).
+    auto chunk_mma = [&](int j, const int8_t *slot, const v4i *xfs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < SPC; ++t) {
+            v4i a;
+            if constexpr (WK == W_INT4) {
+                // K-step t: bytes 32 t + 8 fchunk of the row's 128
+                const int byte = t * 32 + fchunk * 8;
+                const uint2 w = *reinterpret_cast<const uint2 *>(
+                    slot + frow * 128 + (((byte >> 4) ^ ((frow >> 1) & 7)) << 4) + (byte & 15));
+                a = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
+            } else {
+                a = *reinterpret_cast<const v4i *>(slot + frow * 128 + (((t * 4 + fchunk) ^ ((frow >> 1) & 7)) << 4));
+            }
+            const v4i bx = XL ? *reinterpret_cast<const v4i *>(xl_row + j * S::KPC + t * 64 + fchunk * 16) : xfs[t];
+            if constexpr (S::GROUPED) {
+                const int ks = (c0 + j) * SPC + t;  // global K-step
+                acc = mfma_i8(a, bx, (ks % S::SPG) == 0 ? v4i{0, 0, 0, 0} : acc);
+                if ((ks % S::SPG) == S::SPG - 1) {
+                    const float4 sw = *reinterpret_cast<const float4 *>(table + (ks / S::SPG - g0) * 16 + 4 * fchunk);
+                    facc[0] = __builtin_fmaf((float)acc[0], sw.x, facc[0]);
+                    facc[1] = __builtin_fmaf((float)acc[1], sw.y, facc[1]);
+                    facc[2] = __builtin_fmaf((float)acc[2], sw.z, facc[2]);
+                    facc[3] = __builtin_fmaf((float)acc[3], sw.w, facc[3]);
+                }
+            } else {
+                acc = mfma_i8(a, bx, acc);
+            }
+        }
+    };
+    if constexpr (XL) {
+        // ring of `slots` slots (any depth <= RING), chunk j in slot j % slots
+        const int R = min(slots, nch);
+        for (int j = 0; j < R; ++j) {
+            dma_16B(src_lo + (c0 + j) * 128, my_ring + j * 2048);
+            dma_16B(src_hi + (c0 + j) * 128, my_ring + j * 2048 + 1024);
+        }
+        int sl = 0;
+        for (int j = 0; j < nch; ++j) {
+            // chunks issued so far: min(nch, j + R); those after chunk j may be in flight
+            gv_wait_tail<S, RING - 1>(min(nch, j + R) - j - 1);
+            chunk_mma(j, my_ring + sl * 2048, nullptr);
+            if (j + R < nch) {
+                wait_lgkmcnt0();  // the slot's fragment reads are done before it is refilled
+                dma_16B(src_lo + (c0 + j + R) * 128, my_ring + sl * 2048);
+                dma_16B(src_hi + (c0 + j + R) * 128, my_ring + sl * 2048 + 1024);
+            }
+            sl = sl + 1 == R ? 0 : sl + 1;
+        }
+    } else {
+        // ring of RING slots (the launcher gives min(RING, seg_chunks)), chunk j in slot
+        // j % RING; the token fragments of a slot live in registers, so slots are constants
+#pragma unroll
+        for (int s = 0; s < RING; ++s)
+            if (s < nch) {
+                const int ck = c0 + s;
+                dma_16B(src_lo + ck * 128, my_ring + s * 2048);
+                dma_16B(src_hi + ck * 128, my_ring + s * 2048 + 1024);
+#pragma unroll
+                for (int t = 0; t < SPC; ++t)
+                    xf[s][t] = *reinterpret_cast<const v4i *>(xrow + ck * S::KPC + t * 64 + fchunk * 16);
+            }
+        for (int j0 = 0; j0 < nch; j0 += RING) {
+#pragma unroll
+            for (int s = 0; s < RING; ++s) {
+                const int j = j0 + s;
+                if (j < nch) {
+                    gv_wait_tail<S, RING - 1>(min(nch, j + RING) - j - 1);
+                    chunk_mma(j, my_ring + s * 2048, xf[s]);
+                    if (j + RING < nch) {
+                        wait_lgkmcnt0();
+                        const int ck = c0 + j + RING;
+                        dma_16B(src_lo + ck * 128, my_ring + s * 2048);
+                        dma_16B(src_hi + ck * 128, my_ring + s * 2048 + 1024);
+#pragma unroll
+                        for (int t = 0; t < SPC; ++t)
+                            xf[s][t] = *reinterpret_cast<const v4i *>(xrow + ck * S::KPC + t * 64 + fchunk * 16);
+                    }
+                }
+            }
+        }
+    }
+
+    // partials -> LDS (the ring space, once every wave is done with it), summed in
+    // segment order by wave 0 (int32 for per-channel: exact)
+    __syncthreads();
+    if constexpr (S::GROUPED) {
+        float4 *red = reinterpret_cast<float4 *>(gv_lds);
+        red[wave * 64 + lane] = make_float4(facc[0], facc[1], facc[2], facc[3]);
+    } else {
+        int4 *red = reinterpret_cast<int4 *>(gv_lds);
+        red[wave * 64 + lane] = make_int4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int m = frow;
+    const int n = n0 + 4 * fchunk;
+    if (m >= M || n >= N) return;
+    const int64_t off = (int64_t)m * p.ldy + n;
+    if constexpr (S::GROUPED) {
+        const float4 *red = reinterpret_cast<const float4 *>(gv_lds);
+        float4 t = red[lane];
+        for (int w = 1; w < NW; ++w) {
+            const float4 u = red[w * 64 + lane];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        store4(p.y, off, p.out, t.x * e_sx, t.y * e_sx, t.z * e_sx, t.w * e_sx);
+    } else {
+        const int4 *red = reinterpret_cast<const int4 *>(gv_lds);
+        int4 t = red[lane];
+        for (int w = 1; w < NW; ++w) {
+            const int4 u = red[w * 64 + lane];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        if (p.out == OUT_I32) {
+            *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = t;
+            return;
+        }
+        store4(p.y, off, p.out, ((float)t.x * e_sx) * e_sw.x, ((float)t.y * e_sx) * e_sw.y,
+               ((float)t.z * e_sx) * e_sw.z, ((float)t.w * e_sx) * e_sw.w);
+    }
+}
+
+// Launch of the LDS-staged GEMV; returns hipErrorInvalidValue (without launching) when the
+// shape does not fit it, and the caller then uses the direct-load GEMV.
+template <int GS, int WK, bool XL>
+hipError_t launch_gemv_dma_x(const GemmProblem &p, hipStream_t stream) {
+    using S = GvShape<GS, WK, XL>;
+    const int RB = WK == W_INT4 ? p.K / 2 : p.K;
+    if (RB % 128 != 0) return hipErrorInvalidValue;
+    const int NCH = p.K / S::KPC;
+    const int blocks = (p.N + 15) / 16;
+    // waves per workgroup: segments of at most RING chunks where possible, at least about
+    // 2048 waves in the grid while each wave keeps 2 chunks or more; whole groups
+    const int unit = S::GROUPED ? S::CPG : 1;
+    int NW = min(GEMV_MAX_WAVES, max(1, (NCH + S::RING - 1) / S::RING));
+    while (NW < GEMV_MAX_WAVES && (int64_t)blocks * NW < 2048 && NCH / (NW + 1) >= 2) ++NW;
+    int seg = (NCH + NW - 1) / NW;
+    seg = (seg + unit - 1) / unit * unit;
+    NW = (NCH + seg - 1) / seg;
+    const int table_groups = S::GROUPED ? ((seg * S::SPC + S::SPG - 1) / S::SPG + 1 + 3) & ~3 : 0;
+    const size_t xl = XL ? (size_t)((p.M * seg * S::KPC + 1023) & ~1023) : 0;
+    // ring slots: as many as fit while every workgroup of the grid is resident at once
+    const int per_cu = (blocks + num_cus() - 1) / num_cus();
+    const size_t budget = (size_t)160 * 1024 / per_cu;
+    const size_t fixed = (size_t)NW * (table_groups * 16 * sizeof(float) + xl);
+    if (budget <= fixed) return hipErrorInvalidValue;
+    const int fit = (int)((budget - fixed) / ((size_t)NW * 2048));
+    const int slots = min(min(S::RING, seg), fit);
+    // the register-token variant cycles through min(RING, seg) slots; the LDS-token one
+    // through `slots`, of which it needs 2 unless the segment is a single chunk
+    if (!XL && slots < min(S::RING, seg)) return hipErrorInvalidValue;
+    if (slots < 2 && slots < seg) return hipErrorInvalidValue;
+    const size_t lds = (size_t)NW * slots * 2048 + fixed;
+    if (lds > 160 * 1024 || slots < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_dma_kernel<GS, WK, XL>), dim3(blocks), dim3(64 * NW), lds, stream, p, seg, slots,
+                       table_groups);
+    return hipGetLastError();
+}
+
+template <int GS, int WK>
+hipError_t launch_gemv_dma(const GemmProblem &p, hipStream_t stream) {
+    {
+        const hipError_t e = launch_gemv_dma_x<GS, WK, true>(p, stream);
+        if (e != hipErrorInvalidValue) return e;
+    }
+    return launch_gemv_dma_x<GS, WK, false>(p, stream);
+}
+
+template <int GS, int WK>
+hipError_t launch_gemv_any(const GemmProblem &p, hipStream_t stream) {
+    const hipError_t e = launch_gemv_dma<GS, WK>(p, stream);
+    return e == hipErrorInvalidValue ? launch_gemv<GS, WK>(p, stream) : e;
 }
 
 hipError_t dispatch_gemv(const GemmProblem &p, hipStream_t stream) {
     const int gs = p.out == OUT_I32 ? 0 : p.gs;
     if (p.wkind == W_INT4) {
-        if (gs == 64) return launch_gemv<64, W_INT4>(p, stream);
-        if (gs == 128) return launch_gemv<128, W_INT4>(p, stream);
-        return launch_gemv<0, W_INT4>(p, stream);
+        if (gs == 64) return launch_gemv_any<64, W_INT4>(p, stream);
+        if (gs == 128) return launch_gemv_any<128, W_INT4>(p, stream);
+        return launch_gemv_any<0, W_INT4>(p, stream);
     }
-    if (gs == 64) return launch_gemv<64, W_INT8>(p, stream);
-    if (gs == 128) return launch_gemv<128, W_INT8>(p, stream);
-    return launch_gemv<0, W_INT8>(p, stream);
+    if (gs == 64) return launch_gemv_any<64, W_INT8>(p, stream);
+    if (gs == 128) return launch_gemv_any<128, W_INT8>(p, stream);
+    return launch_gemv_any<0, W_INT8>(p, stream);
 }
 
 // ---- configuration table ------------------------------------------------------------
@@ -1022,16 +1361,6 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int num_cus() {
-    static std::atomic<int> cached{0};
-    int v = cached.load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        n = 256;
-    cached.store(n, std::memory_order_relaxed);
-    return n;
-}
 
 int choose_config(const GemmProblem &p) {
     // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel (6)
