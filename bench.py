@@ -3,10 +3,12 @@
 
 One step = one pass of the hot path over one batch: per-token activation
 quantization (fp16 x -> int8 x_q + fp32 s_x) followed by the int8 GEMM with the
-per-channel dequantization fused into its store (fp16 y). Workload: M=4096 tokens,
-N=10240 output channels, K=2560 input channels, seeded synthetic inputs (weights
-quantized once, offline, outside the timed region). Inputs are resident in HBM
-before timing starts.
+per-channel dequantization fused into its store (fp16 y). Default workload: M=4096
+tokens, N=10240 output channels, K=2560 input channels, seeded synthetic inputs
+(weights quantized once, offline, outside the timed region). Inputs are resident in HBM
+before timing starts. For M <= 16 the step is one w8a8_linear call (quantization inside
+the GEMV kernel); for M <= 128 the weights rotate over copies totalling more than
+512 MB, so that no step finds them in the 256 MB Infinity Cache.
 
 Prints ONE JSON line: metric/value (INT8 TOPS = 2*M*N*K / step time), a roofline
 object for the dominant kernel (the GEMM, timed with HIP events on its stream over
@@ -14,7 +16,7 @@ the timed region) and a cpu_baseline object (the CPU oracle timed on a bounded
 sample of the same workload on the host cores).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1] [--copy-ref-mb MB]
+       [--workload pc|pg64|pg128|w4|m1|m1w4] [--copy-ref-mb MB]
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
@@ -45,6 +47,7 @@ WORKLOADS = {
     "pg64": (4096, 10240, 2560, 8, 64),
     "w4": (4096, 10240, 2560, 4, 128),
     "m1": (1, 10240, 2560, 8, 0),
+    "m1w4": (1, 10240, 2560, 4, 128),
 }
 
 
@@ -142,55 +145,86 @@ def main():
     Wd = torch.from_numpy(W_np).cuda()
     wq, sw = w8a8.quantize_weight(Wd, bits, gs)  # offline: not timed
     del Wd
+    # small M is bound by streaming the weights: rotate over copies larger than the MALL
+    wbytes = wq.numel() * wq.element_size()
+    copies = [wq] + ([wq.clone() for _ in range((512 << 20) // wbytes)] if M <= 128 else [])
     xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
     sx = torch.empty((M,), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
+    fused = M <= 16
 
     if bits == 4:
-        def gemm():
-            w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, y=y, stream=stream)
+        def gemm(w):
+            w8a8.w4a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=stream)
     elif gs:
-        def gemm():
-            w8a8.w8a8_gemm_pg(xq, sx, wq, sw, gs, y=y, stream=stream)
+        def gemm(w):
+            w8a8.w8a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=stream)
     else:
-        def gemm():
-            w8a8.w8a8_gemm_pc(xq, sx, wq, sw, y=y, stream=stream)
+        def gemm(w):
+            w8a8.w8a8_gemm_pc(xq, sx, w, sw, y=y, stream=stream)
 
-    def step(ev=None):
+    def step(i, ev=None):
+        w = copies[i % len(copies)]
+        if fused:
+            w8a8.w8a8_linear(x, w, sw, bits, gs, y=y, x_q=xq, s_x=sx, stream=torch.cuda.current_stream())
+            return
         if ev is not None:
             ev[0].record(stream)
         w8a8.quantize_per_token(x, xq, sx, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        gemm()
+        gemm(w)
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if fused:
+        # A step is one short kernel (a few microseconds), shorter than the host's time to
+        # issue it, so the timed steps are replayed as one captured graph: the kernels then
+        # run back to back and the events around the replay measure them, not the host.
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record()
+            graph.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        quant_ms = gemm_ms = e0.elapsed_time(e1) / args.steps
+    else:
+        events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i, events[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in events]))
+        gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in events]))
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in events]))
-    gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in events]))
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
 
-    if M == 1:
-        wbytes = N * K * bits // 8 + sw.numel() * 4
-        alg_bytes = wbytes + K * 1 + 4 + N * 2  # weights + scales, x_q + s_x in, y out
-        achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
+    if fused:
+        # one kernel per step: quantization + GEMV + dequant; HBM-bound on the weight stream
+        kernel_ms = quant_ms
+        alg_bytes = wbytes + sw.numel() * 4 + M * K * 2 + M * N * 2  # weights + scales, x in, y out
+        achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload)}
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
+                    "kernel": "fused quantize + GEMV + dequant (w8a8_linear, M <= 16)",
+                    "launch_ms": kernel_ms, "alg_bytes": alg_bytes}
     else:
         achieved = ops / (gemm_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
@@ -210,13 +244,16 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": f"w8a8 linear ({args.workload}): per-token quantize + int8 GEMM + fused dequant",
+        "config": {"workload": f"w8a8 linear ({args.workload}): per-token quantize + int8 GEMM + fused dequant"
+                               + (" in one kernel" if fused else ""),
                    "M": M, "N": N, "K": K, "weight_bits": bits, "group_size": gs, "out": "fp16",
                    "parallelism": "single GPU"},
         "frac_of_peak_step": value / PEAK_INT8_TOPS,
-        "gemm_ms": gemm_ms,
-        "quantize_ms": quant_ms,
-        "quantize_gbs": (3.0 * M * K + 4 * M) / (quant_ms * 1e-3) / 1e9,
+        "gemm_ms": None if fused else gemm_ms,
+        "quantize_ms": None if fused else quant_ms,
+        "fused_ms": quant_ms if fused else None,
+        "quantize_gbs": None if fused else (3.0 * M * K + 4 * M) / (quant_ms * 1e-3) / 1e9,
+        "weight_copies": len(copies),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

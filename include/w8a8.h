@@ -136,6 +136,27 @@ int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, c
                  int64_t ldy, void *stream);
 
 /*
+ * w8a8_linear -- the whole layer in one call: per-token activation quantization of x
+ * followed by the int8 GEMM with fused dequant (juejin post, "INT8 TensorOps 内核设计":
+ * quantize_per_token, then matmul_fused_dequant). The weight arguments select the GEMM:
+ *   weight_bits 8, group_size 0      -> w8a8_gemm_pc (w = w_q [N, K] int8, s_w [N])
+ *   weight_bits 8, group_size 64|128 -> w8a8_gemm_pg (s_w [N, K/group_size])
+ *   weight_bits 4, group_size 64|128 -> w4a8_gemm_pg (w = w_packed [N, K/2])
+ *   x [M, K] fp16 or bf16 (x_dtype), row stride ldx elements (ldx >= K, ldx % 8 == 0).
+ *   x_q [M, K] int8 and s_x [M] fp32 (caller-owned) receive the codes and scales exactly as
+ *   quantize_per_token writes them; y [M, N] as for the GEMM calls (not W8A8_I32).
+ * Results are bit-identical to quantize_per_token followed by the matching GEMM call for
+ * per-channel weights. For M <= 16 one kernel does both steps (each workgroup quantizes
+ * the rows it needs, saving the second launch); the per-group sum over a row's K range
+ * may then be split differently, within the GEMM's fp32 tolerance. Larger M, or a
+ * configuration forced with w8a8_debug_force_config, runs the two launches.
+ * Constraints: those of quantize_per_token and of the selected GEMM call.
+ */
+int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const float *s_w,
+                int weight_bits, int group_size, int8_t *x_q, float *s_x, void *y, int y_dtype,
+                int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream);
+
+/*
  * Debug knob: force the GEMM tile configuration (-1 = automatic choice by shape).
  * Every configuration computes identical results; tests use this to run each one.
  * Returns the number of configurations, or W8A8_ERR_INVALID_ARGUMENT (negated)

@@ -38,7 +38,8 @@ def unavailable(monkeypatch):
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for required in ("quantize_per_token", "quantize_weight", "w8a8_gemm_pc", "w8a8_gemm_pg",
-                     "w4a8_gemm_pg", "w8a8_is_available", "w8a8_last_error", "w8a8_status_string"):
+                     "w4a8_gemm_pg", "w8a8_linear", "w8a8_is_available", "w8a8_last_error",
+                     "w8a8_status_string"):
         assert required in names, names
 
 
@@ -133,3 +134,34 @@ def test_binding_raises_on_bad_input(w8a8):
     x = torch.zeros((4, 64), dtype=torch.float32)
     with pytest.raises(TypeError):
         w8a8.quantize_per_token(x)
+
+
+def _linear(lib, x=FAKE, x_dtype=F16, ldx=256, bits=8, gs=0, x_q=FAKE, y_dtype=F16, M=8, N=256, K=256, ldy=256):
+    return lib.w8a8_linear(x, x_dtype, ldx, FAKE, FAKE, bits, gs, x_q, FAKE, FAKE, y_dtype, M, N, K, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x_dtype=F32), INVALID, "x_dtype"),
+    (dict(bits=2), INVALID, "weight_bits"),
+    (dict(gs=32), INVALID, "group_size"),
+    (dict(bits=4, gs=0), INVALID, "int4"),
+    (dict(y_dtype=I32), INVALID, "y_dtype"),
+    (dict(ldx=200), INVALID, "ldx"),
+    (dict(ldx=260), INVALID, "ldx"),
+    (dict(N=250), UNSUPPORTED_SHAPE, "N"),
+    (dict(K=100, ldx=104), UNSUPPORTED_SHAPE, "K"),
+    (dict(gs=128, K=192, ldx=192), UNSUPPORTED_SHAPE, "group_size"),
+    (dict(ldy=250), INVALID, "ldy"),
+    (dict(x=None), INVALID, "x"),
+    (dict(x=ctypes.c_void_p(0x100008)), INVALID, "x"),
+    (dict(x_q=None), INVALID, "null"),
+])
+def test_linear_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _linear(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_linear_forced_unavailable(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert _linear(lib) == UNSUPPORTED_DEVICE

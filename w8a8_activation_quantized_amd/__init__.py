@@ -37,6 +37,8 @@ _SIGNATURES = {
     "w8a8_gemm_pc": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w8a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w4a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
+    "w8a8_linear": ([_vp, _int, _i64, _vp, _vp, _int, _int, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp],
+                    _int),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -158,3 +160,27 @@ def w4a8_gemm_pg(x_q, s_x, w_packed, s_w, group_size, out_dtype=torch.float16, y
     _check(_lib.w4a8_gemm_pg(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(s_w), group_size, _ptr(y),
                              _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
     return y
+
+
+def w8a8_linear(x, w, s_w, weight_bits=8, group_size=0, out_dtype=torch.float16, y=None, x_q=None, s_x=None,
+                stream=None):
+    """The whole layer: y = dequant(quantize_per_token(x) . w^T) in one call.
+
+    x [M, K] fp16/bf16; w int8 [N, K] (weight_bits 8) or packed uint8 [N, K/2] (4);
+    s_w [N] (group_size 0) or [N, K/group_size]. Returns (y, x_q, s_x); x_q and s_x hold
+    the activation codes and scales as quantize_per_token computes them."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last dimension")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    M, K = x.shape
+    N = w.shape[0]
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty((M,), dtype=torch.float32, device=x.device)
+    y = _out(y, M, N, out_dtype, x.device)
+    _check(_lib.w8a8_linear(_ptr(x), _DTYPE_CODE[x.dtype], x.stride(0), _ptr(w), _ptr(s_w), weight_bits,
+                            group_size, _ptr(x_q), _ptr(s_x), _ptr(y), _DTYPE_CODE[y.dtype], M, N, K,
+                            y.stride(0), _stream(stream)))
+    return y, x_q, s_x

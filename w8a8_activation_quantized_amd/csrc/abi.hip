@@ -106,13 +106,8 @@ int check_gemm(const char *fn, const void *x_q, const float *s_x, const void *w,
     return W8A8_OK;
 }
 
-int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w, const float *s_w,
-             int gs, int wkind, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
-             void *stream) {
-    int rc = check_gemm(fn, x_q, s_x, w, s_w, gs, y, y_dtype, M, N, K, ldy, gs != 0 || wkind == w8a8::W_INT4);
-    if (rc != W8A8_OK) return rc;
-    if ((rc = check_device()) != W8A8_OK) return rc;
-    if (M == 0) return ok();
+w8a8::GemmProblem make_problem(const int8_t *x_q, const float *s_x, const void *w, const float *s_w, int gs,
+                               int wkind, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy) {
     w8a8::GemmProblem p;
     p.xq = x_q;
     p.sx = s_x;
@@ -130,6 +125,22 @@ int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w,
         const int64_t esize = (y_dtype == W8A8_F16 || y_dtype == W8A8_BF16) ? 2 : 4;
         p.y_rows16 = ((reinterpret_cast<uintptr_t>(y) & 15) == 0 && ((ldy * esize) & 15) == 0) ? 1 : 0;
     }
+    p.x = nullptr;
+    p.ldx = 0;
+    p.x_bf16 = 0;
+    p.xq_out = nullptr;
+    p.sx_out = nullptr;
+    return p;
+}
+
+int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w, const float *s_w,
+             int gs, int wkind, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+             void *stream) {
+    int rc = check_gemm(fn, x_q, s_x, w, s_w, gs, y, y_dtype, M, N, K, ldy, gs != 0 || wkind == w8a8::W_INT4);
+    if (rc != W8A8_OK) return rc;
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    const w8a8::GemmProblem p = make_problem(x_q, s_x, w, s_w, gs, wkind, y, y_dtype, M, N, K, ldy);
     return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed),
                                       static_cast<hipStream_t>(stream)),
                     fn);
@@ -239,6 +250,51 @@ int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, c
         return fail(W8A8_ERR_INVALID_ARGUMENT, "w4a8_gemm_pg: group_size must be 64 or 128");
     return run_gemm("w4a8_gemm_pg", x_q, s_x, w_packed, s_w, group_size, w8a8::W_INT4, y, y_dtype, M, N,
                     K, ldy, stream);
+}
+
+int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const float *s_w, int weight_bits,
+                int group_size, int8_t *x_q, float *s_x, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                int64_t ldy, void *stream) {
+    const char *fn = "w8a8_linear";
+    if (x_dtype != W8A8_F16 && x_dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: x_dtype must be F16 or BF16", fn);
+    if (weight_bits != 8 && weight_bits != 4)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: weight_bits must be 8 or 4", fn);
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
+    if (weight_bits == 4 && group_size == 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
+    if (y_dtype == W8A8_I32)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: y_dtype must be F16, BF16 or F32", fn);
+    if (ldx < K || ldx % 8 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldx = %lld must be >= K and a multiple of 8", fn,
+                    (long long)ldx);
+    int rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy,
+                        group_size != 0 || weight_bits == 4);
+    if (rc != W8A8_OK) return rc;
+    if (M > 0 && (!x || !aligned16(x)))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: x must be a non-null 16-byte aligned pointer", fn);
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    const int wkind = weight_bits == 4 ? w8a8::W_INT4 : w8a8::W_INT8;
+    w8a8::GemmProblem p = make_problem(x_q, s_x, w, s_w, group_size, wkind, y, y_dtype, M, N, K, ldy);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int force = g_force_cfg.load(std::memory_order_relaxed);
+    if (force < 0) {
+        p.x = x;
+        p.ldx = ldx;
+        p.x_bf16 = x_dtype == W8A8_BF16 ? 1 : 0;
+        p.xq_out = x_q;
+        p.sx_out = s_x;
+        const hipError_t e = w8a8::launch_linear_small(p, st);
+        if (e != hipErrorNotSupported) return launched(e, fn);
+        p.x = nullptr;
+        p.xq_out = nullptr;
+        p.sx_out = nullptr;
+    }
+    hipError_t e = w8a8::launch_quantize_per_token(x, x_dtype == W8A8_BF16, ldx, (int)M, (int)K, x_q, s_x, st);
+    if (e != hipSuccess) return launched(e, fn);
+    return launched(w8a8::launch_gemm(p, force, st), fn);
 }
 
 }  // extern "C"

@@ -39,6 +39,7 @@
 //    which add nothing to the integer sums.
 #include <atomic>
 
+#include "act_quant.h"
 #include "internal.h"
 
 namespace w8a8 {
@@ -1032,10 +1033,13 @@ __device__ __forceinline__ void gv_wait_tail(int after) {
     }
 }
 
-template <int GS, int WK, bool XL>
+template <int GS, int WK, bool XL, int FQ>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProblem p, int seg_chunks, int slots,
                                                                         int table_groups) {
     using S = GvShape<GS, WK, XL>;
+    // FQ: 0 = x_q given; 1 / 2 = quantize fp16 / bf16 rows of p.x here (needs XL)
+    static_assert(FQ == 0 || XL, "in-kernel quantization writes the codes to the LDS token region");
+    constexpr bool BF16X = FQ == 2;
     constexpr int RING = S::RING, SPC = S::SPC;
     extern __shared__ __attribute__((aligned(1024))) int8_t gv_lds[];
 
@@ -1055,6 +1059,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
     // XL region of this wave: room for M rows of seg_chunks * KPC bytes (rounded up to 1 KiB)
     const int xl_bytes = (M * seg_chunks * S::KPC + 1023) & ~1023;
     int8_t *xl = gv_lds + NW * slots * 2048 + NW * table_groups * 64 + wave * xl_bytes;
+    // FQ: this wave's fp16 / bf16 x segment (twice the code bytes), then row maxima [NW][16]
+    const int xh_bytes = FQ ? (2 * M * seg_chunks * S::KPC + 1023) & ~1023 : 0;
+    int8_t *xh = gv_lds + NW * slots * 2048 + NW * table_groups * 64 + NW * xl_bytes + wave * xh_bytes;
+    uint32_t *pmax = reinterpret_cast<uint32_t *>(gv_lds + NW * slots * 2048 + NW * table_groups * 64 +
+                                                  NW * xl_bytes + NW * xh_bytes);
 
     // the epilogue's scales, fetched first so that they arrive with the weight stream
     // (retired by the first chunk wait: they precede every DMA)
@@ -1062,7 +1071,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
     float e_sx = 0.f;
     float4 e_sw = make_float4(0.f, 0.f, 0.f, 0.f);
     if (wave == 0) {
-        e_sx = p.sx[em];
+        if constexpr (FQ == 0) e_sx = p.sx[em];
         if constexpr (!S::GROUPED) e_sw = *reinterpret_cast<const float4 *>(p.sw + en);
     }
 
@@ -1093,7 +1102,15 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
     // never past the row end), stored flat with row stride xlr; 1 KiB per DMA, lane i
     // taking flat byte 1024 b + 16 i (clamped to the last row's end)
     const int xlr = nch * S::KPC;
-    if constexpr (XL) {
+    if constexpr (FQ != 0) {
+        // the same rows of x (2 bytes per element), flat with row stride 2 xlr
+        const int total = 2 * M * xlr;
+        for (int b = 0; b * 1024 < total; ++b) {
+            const int flat = min(b * 1024 + 16 * lane, total - 16);
+            const int r = flat / (2 * xlr), col = flat - r * (2 * xlr);
+            dma_16B(static_cast<const int8_t *>(p.x) + 2 * ((int64_t)r * p.ldx + c0 * S::KPC) + col, xh + b * 1024);
+        }
+    } else if constexpr (XL) {
         const int total = M * xlr;
         for (int b = 0; b * 1024 < total; ++b) {
             const int flat = min(b * 1024 + 16 * lane, total - 16);
@@ -1138,9 +1155,61 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
     if constexpr (XL) {
         // ring of `slots` slots (any depth <= RING), chunk j in slot j % slots
         const int R = min(slots, nch);
-        for (int j = 0; j < R; ++j) {
+        // With in-kernel quantization only the first chunks go out before it: a wave blocks
+        // while issuing into a full memory queue, and the quantization should run while the
+        // first weights are in flight, not after the whole prologue has been issued.
+        const int R0 = FQ != 0 ? min(R, 2) : R;
+        for (int j = 0; j < R0; ++j) {
             dma_16B(src_lo + (c0 + j) * 128, my_ring + j * 2048);
             dma_16B(src_hi + (c0 + j) * 128, my_ring + j * 2048 + 1024);
+        }
+        if constexpr (FQ != 0) {
+            // In-kernel activation quantization, with the arithmetic of the quantize kernel.
+            // The x copy and the scale table precede the R0 chunk DMAs (2 ops each).
+            gv_wait_tail<S, 2>(R0);
+            const int nc8 = xlr / 8;  // 16-byte pieces (8 elements) of a row segment
+            for (int m = 0; m < M; ++m) {
+                act::u16x2 mm = {0, 0};
+                for (int c = lane; c < nc8; c += 64)
+                    mm = act::absmax8(*reinterpret_cast<const uint4 *>(xh + m * 2 * xlr + 16 * c), mm);
+                const uint32_t a = act::wave_max_u32(mm.x > mm.y ? mm.x : mm.y);
+                if (lane == 0) pmax[wave * 16 + m] = a;
+            }
+            __syncthreads();
+            const bool out0 = blockIdx.x == 0;
+            for (int m = 0; m < M; ++m) {
+                uint32_t a = 0;
+                for (int w = 0; w < NW; ++w) a = max(a, pmax[w * 16 + m]);
+                const float sc = act::row_scale<BF16X>(a);
+                if (em == m) e_sx = sc;
+                if (out0 && wave == 0 && lane == 0) p.sx_out[m] = sc;
+                const int8_t *hrow = xh + m * 2 * xlr;
+                int8_t *crow = xl + m * xlr;
+                int8_t *grow = p.xq_out + (int64_t)m * K + c0 * S::KPC;
+                if (sc == 0.0f) {
+                    for (int c = lane; c < nc8; c += 64) {
+                        *reinterpret_cast<uint2 *>(crow + 8 * c) = make_uint2(0, 0);
+                        if (out0) *reinterpret_cast<uint2 *>(grow + 8 * c) = make_uint2(0, 0);
+                    }
+                } else if (sc >= act::kMinFastScale) {
+                    const float rc = 1.0f / sc;
+                    for (int c = lane; c < nc8; c += 64) {
+                        const uint2 q = act::quant8<BF16X, true>(*reinterpret_cast<const uint4 *>(hrow + 16 * c), sc, rc);
+                        *reinterpret_cast<uint2 *>(crow + 8 * c) = q;
+                        if (out0) *reinterpret_cast<uint2 *>(grow + 8 * c) = q;
+                    }
+                } else {
+                    for (int c = lane; c < nc8; c += 64) {
+                        const uint2 q = act::quant8<BF16X, false>(*reinterpret_cast<const uint4 *>(hrow + 16 * c), sc, 0.f);
+                        *reinterpret_cast<uint2 *>(crow + 8 * c) = q;
+                        if (out0) *reinterpret_cast<uint2 *>(grow + 8 * c) = q;
+                    }
+                }
+            }
+            for (int j = R0; j < R; ++j) {
+                dma_16B(src_lo + (c0 + j) * 128, my_ring + j * 2048);
+                dma_16B(src_hi + (c0 + j) * 128, my_ring + j * 2048 + 1024);
+            }
         }
         int sl = 0;
         for (int j = 0; j < nch; ++j) {
@@ -1234,13 +1303,15 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
     }
 }
 
-// Launch of the LDS-staged GEMV; returns hipErrorInvalidValue (without launching) when the
+// Launch of the LDS-staged GEMV; returns hipErrorNotSupported (without launching) when the
 // shape does not fit it, and the caller then uses the direct-load GEMV.
-template <int GS, int WK, bool XL>
+template <int GS, int WK, bool XL, int FQ = 0>
 hipError_t launch_gemv_dma_x(const GemmProblem &p, hipStream_t stream) {
     using S = GvShape<GS, WK, XL>;
     const int RB = WK == W_INT4 ? p.K / 2 : p.K;
-    if (RB % 128 != 0) return hipErrorInvalidValue;
+    if (RB % 128 != 0 || p.M > 16) return hipErrorNotSupported;
+    // in-kernel quantization copies x rows with 16-byte DMA: rows must start 16-byte aligned
+    if (FQ && ((reinterpret_cast<uintptr_t>(p.x) & 15) != 0 || (p.ldx * 2) % 16 != 0)) return hipErrorNotSupported;
     const int NCH = p.K / S::KPC;
     const int blocks = (p.N + 15) / 16;
     // waves per workgroup: segments of at most RING chunks where possible, at least about
@@ -1253,20 +1324,21 @@ hipError_t launch_gemv_dma_x(const GemmProblem &p, hipStream_t stream) {
     NW = (NCH + seg - 1) / seg;
     const int table_groups = S::GROUPED ? ((seg * S::SPC + S::SPG - 1) / S::SPG + 1 + 3) & ~3 : 0;
     const size_t xl = XL ? (size_t)((p.M * seg * S::KPC + 1023) & ~1023) : 0;
+    const size_t xh = FQ ? (size_t)((2 * p.M * seg * S::KPC + 1023) & ~1023) : 0;
     // ring slots: as many as fit while every workgroup of the grid is resident at once
     const int per_cu = (blocks + num_cus() - 1) / num_cus();
     const size_t budget = (size_t)160 * 1024 / per_cu;
-    const size_t fixed = (size_t)NW * (table_groups * 16 * sizeof(float) + xl);
-    if (budget <= fixed) return hipErrorInvalidValue;
+    const size_t fixed = (size_t)NW * (table_groups * 16 * sizeof(float) + xl + xh) + (FQ ? (size_t)NW * 16 * 4 : 0);
+    if (budget <= fixed) return hipErrorNotSupported;
     const int fit = (int)((budget - fixed) / ((size_t)NW * 2048));
     const int slots = min(min(S::RING, seg), fit);
     // the register-token variant cycles through min(RING, seg) slots; the LDS-token one
     // through `slots`, of which it needs 2 unless the segment is a single chunk
-    if (!XL && slots < min(S::RING, seg)) return hipErrorInvalidValue;
-    if (slots < 2 && slots < seg) return hipErrorInvalidValue;
+    if (!XL && slots < min(S::RING, seg)) return hipErrorNotSupported;
+    if (slots < 2 && slots < seg) return hipErrorNotSupported;
     const size_t lds = (size_t)NW * slots * 2048 + fixed;
-    if (lds > 160 * 1024 || slots < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemv_dma_kernel<GS, WK, XL>), dim3(blocks), dim3(64 * NW), lds, stream, p, seg, slots,
+    if (lds > 160 * 1024 || slots < 1) return hipErrorNotSupported;
+    hipLaunchKernelGGL((gemv_dma_kernel<GS, WK, XL, FQ>), dim3(blocks), dim3(64 * NW), lds, stream, p, seg, slots,
                        table_groups);
     return hipGetLastError();
 }
@@ -1275,7 +1347,7 @@ template <int GS, int WK>
 hipError_t launch_gemv_dma(const GemmProblem &p, hipStream_t stream) {
     {
         const hipError_t e = launch_gemv_dma_x<GS, WK, true>(p, stream);
-        if (e != hipErrorInvalidValue) return e;
+        if (e != hipErrorNotSupported) return e;
     }
     return launch_gemv_dma_x<GS, WK, false>(p, stream);
 }
@@ -1283,7 +1355,7 @@ hipError_t launch_gemv_dma(const GemmProblem &p, hipStream_t stream) {
 template <int GS, int WK>
 hipError_t launch_gemv_any(const GemmProblem &p, hipStream_t stream) {
     const hipError_t e = launch_gemv_dma<GS, WK>(p, stream);
-    return e == hipErrorInvalidValue ? launch_gemv<GS, WK>(p, stream) : e;
+    return e == hipErrorNotSupported ? launch_gemv<GS, WK>(p, stream) : e;
 }
 
 hipError_t dispatch_gemv(const GemmProblem &p, hipStream_t stream) {
@@ -1296,6 +1368,19 @@ hipError_t dispatch_gemv(const GemmProblem &p, hipStream_t stream) {
     if (gs == 64) return launch_gemv_any<64, W_INT8>(p, stream);
     if (gs == 128) return launch_gemv_any<128, W_INT8>(p, stream);
     return launch_gemv_any<0, W_INT8>(p, stream);
+}
+
+template <int FQ>
+hipError_t linear_small_fq(const GemmProblem &p, hipStream_t stream) {
+    const int gs = p.gs;
+    if (p.wkind == W_INT4) {
+        if (gs == 64) return launch_gemv_dma_x<64, W_INT4, true, FQ>(p, stream);
+        if (gs == 128) return launch_gemv_dma_x<128, W_INT4, true, FQ>(p, stream);
+        return hipErrorNotSupported;
+    }
+    if (gs == 64) return launch_gemv_dma_x<64, W_INT8, true, FQ>(p, stream);
+    if (gs == 128) return launch_gemv_dma_x<128, W_INT8, true, FQ>(p, stream);
+    return launch_gemv_dma_x<0, W_INT8, true, FQ>(p, stream);
 }
 
 // ---- configuration table ------------------------------------------------------------
@@ -1381,6 +1466,11 @@ int choose_config(const GemmProblem &p) {
 }  // namespace
 
 int gemm_num_configs() { return kNumConfigs; }
+
+hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream) {
+    if (p.x == nullptr || p.M < 1 || p.M > 16 || p.out == OUT_I32) return hipErrorNotSupported;
+    return p.x_bf16 ? linear_small_fq<2>(p, stream) : linear_small_fq<1>(p, stream);
+}
 
 hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) {
     int id = (force_cfg >= 0 && force_cfg < kNumConfigs) ? force_cfg : choose_config(p);

@@ -22,6 +22,13 @@ struct GemmProblem {
     int wkind;         // WeightKind
     int out;           // OutType
     int y_rows16;      // 1 if y and the start of every output row are 16-byte aligned
+    // fused small-M layer (activation quantization inside the GEMV kernel): x is read in
+    // place of xq / sx, and workgroup 0 writes the codes and scales it computes
+    const void *x;     // [M, K] fp16 / bf16, row stride ldx elements; null when unfused
+    int64_t ldx;
+    int x_bf16;
+    int8_t *xq_out;    // [M, K]
+    float *sx_out;     // [M]
 };
 
 // Activation quantization (fp16 / bf16 rows -> int8 + fp32 scale).
@@ -34,6 +41,9 @@ hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs
 
 // GEMM + fused dequant. `force_cfg` < 0 lets the launcher choose by shape.
 hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream);
+// The whole layer for small M in one kernel (p.x set). Returns hipErrorNotSupported without
+// launching when the shape does not fit it; the caller then quantizes and runs launch_gemm.
+hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream);
 
 // Number of GEMM tile configurations selectable via force_cfg.
 int gemm_num_configs();
