@@ -16,7 +16,7 @@ the timed region) and a cpu_baseline object (the CPU oracle timed on a bounded
 sample of the same workload on the host cores).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1|m1w4] [--copy-ref-mb MB]
+       [--workload pc|pg64|pg128|w4|m1|m1w4] [--copy-ref-mb MB] [--no-graph]
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
@@ -62,6 +62,9 @@ def parse():
                     help="time budget of the CPU-oracle sample")
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a counter reference)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="issue small-M steps one by one instead of as a graph replay (for counter "
+                         "collection; the timing then includes the host's issue time)")
     return ap.parse_args()
 
 
@@ -167,7 +170,13 @@ def main():
     def step(i, ev=None):
         w = copies[i % len(copies)]
         if fused:
-            w8a8.w8a8_linear(x, w, sw, bits, gs, y=y, x_q=xq, s_x=sx, stream=torch.cuda.current_stream())
+            cur = torch.cuda.current_stream()
+            if ev is not None:
+                ev[0].record(cur)
+            w8a8.w8a8_linear(x, w, sw, bits, gs, y=y, x_q=xq, s_x=sx, stream=cur)
+            if ev is not None:
+                ev[1].record(cur)
+                ev[2].record(cur)
             return
         if ev is not None:
             ev[0].record(stream)
@@ -178,11 +187,15 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    # setup, not a step: touch every weight copy once (page tables warm, as in a serving
+    # loop), then the warmup steps
+    for i in range(len(copies) if len(copies) > 1 else 0):
+        step(i)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    if fused:
+    if fused and not args.no_graph:
         # A step is one short kernel (a few microseconds), shorter than the host's time to
         # issue it, so the timed steps are replayed as one captured graph: the kernels then
         # run back to back and the events around the replay measure them, not the host.
@@ -209,8 +222,9 @@ def main():
             step(args.warmup + i, events[i])
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in events]))
-        gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in events]))
+        # medians: a few steps absorb host hiccups that are not kernel time
+        quant_ms = float(np.median([a.elapsed_time(b) for a, b, _ in events]))
+        gemm_ms = float(np.median([b.elapsed_time(c) for _, b, c in events]))
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ops = 2.0 * M * N * K
