@@ -363,3 +363,14 @@ def test_quantize_all_fp16_values_sampled_maxima(w8a8):
     rq, rs = oracle.quantize_per_token(x)
     assert (sx.view(np.uint32) == rs.view(np.uint32)).all()
     assert (xq == rq).all()
+
+
+@pytest.mark.parametrize("mode", ["pg64", "w4_64"])
+@pytest.mark.parametrize("M,N,K", [(300, 272, 320), (257, 48, 64)])
+def test_grouped_k_not_multiple_of_128(w8a8, mode, M, N, K):
+    """Per-group shapes whose K is a multiple of 64 but not 128 (the register-staged kernel)."""
+    note(f"grouped K%128 != 0 {mode} M={M} N={N} K={K}")
+    x, W = linear_inputs(M, N, K, seed=M + K)
+    r = oracle_mode(mode, x, W)
+    for out in (torch.float16, torch.float32, torch.int32):
+        compare(run_mode(w8a8, mode, x, W, out), r, f"{mode} {M}x{N}x{K} {out}")

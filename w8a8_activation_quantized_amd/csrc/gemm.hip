@@ -634,6 +634,276 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_ms_kernel(GemmProblem p, 
     }
 }
 
+// ---- per-group and W4A8 on the direct-to-LDS pipeline ---------------------------------
+//
+// The structure of gemm_ms_kernel (BN x BM tile, 128-value K-tiles, STAGES LDS stages filled
+// by global_load_lds, one barrier per K-tile) with the per-group dequantization of the
+// pages' segmented form: per group g, acc_g (int32, started by an MFMA on a zero
+// accumulator) is folded into an fp32 accumulator, t = fma(fp32(acc_g), s_w[n, g], t), g
+// ascending; at the end y = t * s_x[m]. Each stage also carries the K-tile's group scales of
+// the tile's BN output channels ([group][n] floats, 4-byte DMA gathers from s_w [N, G]); a
+// wave reads them into registers before the stage's barrier, together with the next
+// K-step's fragments, so the buffer can be refilled as soon as every wave passed it.
+//
+// int4 weights (WK = W_INT4) are 64 bytes per row per K-tile; a DMA instruction moves 16
+// rows x 64 bytes and the 16-byte pieces of row r sit at position piece ^ ((r >> 2) & 3),
+// which keeps the 8-byte fragment reads conflict-free; fragments are unpacked to int8
+// after the LDS read (nibble split, byte interleave, u - 8).
+template <int BN_, int BM_, int STAGES_, int WGN_, int WGM_, int GS_, int WK_>
+struct MgShape {
+    static constexpr int BN = BN_, BM = BM_, BK = 128, STAGES = STAGES_, WGN = WGN_, WGM = WGM_, GS = GS_, WK = WK_;
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int FM = WM / 16, FN = WN / 16;
+    static constexpr int WB = WK == W_INT4 ? 64 : 128;        // weight bytes per row per K-tile
+    static constexpr int W_TILE = BN * WB, X_TILE = BM * BK;
+    static constexpr int GPK = BK / GS;                         // groups per K-tile (1 or 2)
+    static constexpr int SCALES = GPK * BN * 4;
+    static constexpr int STAGE = W_TILE + X_TILE + SCALES;
+    static constexpr int WG = W_TILE / 1024, XG = X_TILE / 1024;  // 1 KiB DMA pieces per stage
+    static constexpr int NG = WG + XG;
+    static constexpr int NSD = GPK * BN / 64;                   // 4-byte scale DMAs per stage
+    static constexpr int GPW = (NG + NW - 1) / NW;              // tile DMAs per wave (max)
+    static_assert(GS == 64 || GS == 128, "group size");
+    static_assert(BN % 64 == 0 && BM % 8 == 0 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
+    static_assert(W_TILE % 1024 == 0 && NSD <= NW, "loader shape");
+    static_assert(STAGES * STAGE <= 163840, "LDS");
+};
+
+// s_waitcnt vmcnt(n) for a uniform n known only at run time (n clamped to 40; a smaller
+// count only waits longer).
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+    switch (n) {
+#define W8A8_VM_CASE(k) case k: wait_vmcnt<k>(); break;
+        W8A8_VM_CASE(0) W8A8_VM_CASE(1) W8A8_VM_CASE(2) W8A8_VM_CASE(3) W8A8_VM_CASE(4) W8A8_VM_CASE(5)
+        W8A8_VM_CASE(6) W8A8_VM_CASE(7) W8A8_VM_CASE(8) W8A8_VM_CASE(9) W8A8_VM_CASE(10) W8A8_VM_CASE(11)
+        W8A8_VM_CASE(12) W8A8_VM_CASE(13) W8A8_VM_CASE(14) W8A8_VM_CASE(15) W8A8_VM_CASE(16) W8A8_VM_CASE(17)
+        W8A8_VM_CASE(18) W8A8_VM_CASE(19) W8A8_VM_CASE(20) W8A8_VM_CASE(21) W8A8_VM_CASE(22) W8A8_VM_CASE(23)
+        W8A8_VM_CASE(24) W8A8_VM_CASE(25) W8A8_VM_CASE(26) W8A8_VM_CASE(27) W8A8_VM_CASE(28) W8A8_VM_CASE(29)
+        W8A8_VM_CASE(30) W8A8_VM_CASE(31) W8A8_VM_CASE(32) W8A8_VM_CASE(33) W8A8_VM_CASE(34) W8A8_VM_CASE(35)
+        W8A8_VM_CASE(36) W8A8_VM_CASE(37) W8A8_VM_CASE(38) W8A8_VM_CASE(39)
+#undef W8A8_VM_CASE
+        default: wait_vmcnt<40>(); break;
+    }
+}
+
+// DMA of K-tile kt of the tile (m0, n0) into one stage. Wave w issues pieces g = w + j NW
+// (weight pieces first, then token pieces) and, if w < NSD, scale gather w.
+template <class S>
+__device__ __forceinline__ void mg_issue(const GemmProblem &p, int m0, int n0, int kt, int8_t *st, int wave,
+                                         int lane) {
+    const int G = p.K / S::GS;
+#pragma unroll
+    for (int j = 0; j < S::GPW; ++j) {
+        const int g = wave + j * S::NW;
+        if (g < S::NG) {
+            if (g < S::WG) {
+                // weight piece: WB = 128 -> 8 rows x 128 B; WB = 64 -> 16 rows x 64 B
+                constexpr int LPR = S::WB / 16;  // lanes per row
+                const int lrow = g * (64 / LPR) + lane / LPR, pos = lane % LPR;
+                const int c = S::WB == 128 ? pos ^ ((lrow >> 1) & 7) : pos ^ ((lrow >> 2) & 3);
+                const int grow = min(n0 + lrow, p.N - 1);
+                const int8_t *w = static_cast<const int8_t *>(p.wq) + (int64_t)grow * (S::WK == W_INT4 ? p.K / 2 : p.K);
+                dma_16B(w + kt * S::WB + 16 * c, st + g * 1024);
+            } else {
+                const int xg = g - S::WG;
+                const int lrow = xg * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ ((lrow >> 1) & 7);
+                const int grow = min(m0 + lrow, p.M - 1);
+                dma_16B(p.xq + (int64_t)grow * p.K + kt * S::BK + 16 * c, st + S::W_TILE + xg * 1024);
+            }
+        }
+    }
+    if (wave < S::NSD) {
+        // scales [gi][n] of this K-tile: gather gi = wave / (BN / 64), n block wave % (BN / 64)
+        const int gi = wave / (S::BN / 64), nb = wave % (S::BN / 64);
+        const int n = min(n0 + nb * 64 + lane, p.N - 1);
+        dma_4B(p.sw + (int64_t)n * G + kt * S::GPK + gi, st + S::W_TILE + S::X_TILE + (gi * S::BN + nb * 64) * 4);
+    }
+}
+
+template <class S>
+__device__ __forceinline__ int mg_ops_per_stage(int wave) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < S::GPW; ++j) n += (wave + j * S::NW < S::NG) ? 1 : 0;
+    return n + (wave < S::NSD ? 1 : 0);
+}
+
+template <class S>
+__device__ __forceinline__ void mg_frags(const int8_t *st, int ks, int wm, int wn, int frow, int fchunk,
+                                         v4i (&a)[S::FN], v4i (&b)[S::FM]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn) {
+        const int r = wn * S::WN + fn * 16 + frow;
+        if constexpr (S::WK == W_INT4) {
+            const int byte = ks * 32 + fchunk * 8;  // 16 int4 values of this lane
+            const uint2 w = *reinterpret_cast<const uint2 *>(st + r * 64 + (((byte >> 4) ^ ((r >> 2) & 3)) << 4) +
+                                                             (byte & 15));
+            a[fn] = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
+        } else {
+            a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(r, ks * 4 + fchunk));
+        }
+    }
+#pragma unroll
+    for (int fm = 0; fm < S::FM; ++fm)
+        b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<128>(wm * S::WM + fm * 16 + frow, ks * 4 + fchunk));
+}
+
+// MFMAs of one K-step; FIRST: the step opens a group (accumulate from zero).
+template <class S, bool FIRST>
+__device__ __forceinline__ void mg_mma(v4i (&acc)[S::FN][S::FM], const v4i (&a)[S::FN], const v4i (&b)[S::FM]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < S::FM; ++fm)
+            acc[fn][fm] = mfma_i8(a[fn], b[fm], FIRST ? v4i{0, 0, 0, 0} : acc[fn][fm]);
+}
+
+// t = fma(fp32(acc_g), s_w[n, g], t) for the group that just closed.
+template <class S>
+__device__ __forceinline__ void mg_fold(const v4i (&acc)[S::FN][S::FM], const float4 (&sw)[S::FN],
+                                        float4 (&t)[S::FN][S::FM]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < S::FM; ++fm) {
+            t[fn][fm].x = __builtin_fmaf((float)acc[fn][fm][0], sw[fn].x, t[fn][fm].x);
+            t[fn][fm].y = __builtin_fmaf((float)acc[fn][fm][1], sw[fn].y, t[fn][fm].y);
+            t[fn][fm].z = __builtin_fmaf((float)acc[fn][fm][2], sw[fn].z, t[fn][fm].z);
+            t[fn][fm].w = __builtin_fmaf((float)acc[fn][fm][3], sw[fn].w, t[fn][fm].w);
+        }
+}
+
+template <class S>
+__device__ __forceinline__ void mg_scales(const int8_t *st, int gi, int wn, int fchunk, float4 (&sw)[S::FN]) {
+    const float *sc = reinterpret_cast<const float *>(st + S::W_TILE + S::X_TILE) + gi * S::BN;
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn) sw[fn] = *reinterpret_cast<const float4 *>(sc + wn * S::WN + fn * 16 + 4 * fchunk);
+}
+
+template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mg_kernel(GemmProblem p, TileMap tmap) {
+    using S = MgShape<BN, BM, STAGES, WGN, WGM, GS, WK>;
+    constexpr int FM = S::FM, FN = S::FN;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * S::STAGE];
+
+    int tm, tn;
+    map_tile(tmap, tm, tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WGN, wm = wave / WGN;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N;
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int KT = p.K / S::BK;
+    const int OPS = mg_ops_per_stage<S>(wave);
+
+    v4i acc[FN][FM];
+    float4 t[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            acc[i][j] = v4i{0, 0, 0, 0};
+            t[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+
+    // prologue: stages 0 .. STAGES-2 in flight, wait for stage 0
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) mg_issue<S>(p, m0, n0, s, smem + s * S::STAGE, wave, lane);
+    wait_vmcnt_rt(OPS * min(STAGES - 2, KT - 1));
+    lds_barrier();
+
+    v4i a0[FN], b0[FM], a1[FN], b1[FM];
+    float4 sw0[FN], sw1[FN];
+    mg_frags<S>(smem, 0, wm, wn, frow, fchunk, a0, b0);
+    wait_lgkmcnt0();
+    int cur = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int fill = kt + STAGES - 1;
+        if (fill < KT) {
+            int fb = cur + STAGES - 1;
+            fb -= fb >= STAGES ? STAGES : 0;
+            mg_issue<S>(p, m0, n0, fill, smem + fb * S::STAGE, wave, lane);
+        }
+        const int8_t *st = smem + cur * S::STAGE;
+        // everything this wave still needs from stage kt is read before its barrier
+        mg_frags<S>(st, 1, wm, wn, frow, fchunk, a1, b1);
+        mg_scales<S>(st, 0, wn, fchunk, sw0);
+        if constexpr (S::GPK == 2) mg_scales<S>(st, 1, wn, fchunk, sw1);
+        mg_mma<S, true>(acc, a0, b0);  // K-step 0 opens group kt (or 2 kt)
+        wait_lgkmcnt0();
+        if constexpr (S::GPK == 2) mg_fold<S>(acc, sw0, t);
+        if (kt + 1 < KT) {
+            wait_vmcnt_rt(OPS * min(STAGES - 2, KT - 2 - kt));
+            lds_barrier();
+            int nb = cur + 1;
+            nb -= nb >= STAGES ? STAGES : 0;
+            mg_frags<S>(smem + nb * S::STAGE, 0, wm, wn, frow, fchunk, a0, b0);
+            cur = nb;
+        }
+        if constexpr (S::GPK == 2) {
+            mg_mma<S, true>(acc, a1, b1);  // K-step 1 is group 2 kt + 1
+            wait_lgkmcnt0();
+            mg_fold<S>(acc, sw1, t);
+        } else {
+            mg_mma<S, false>(acc, a1, b1);  // K-step 1 closes group kt
+            wait_lgkmcnt0();
+            mg_fold<S>(acc, sw0, t);
+        }
+    }
+
+    // ---- epilogue: y = t * s_x[m] ----
+    const float *__restrict__ sxp = p.sx;
+    float sxm[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sxm[fm] = sxp[min(m0 + wm * S::WM + fm * 16 + frow, M - 1)];
+    const int out = p.out;
+    if ((out == OUT_F16 || out == OUT_BF16) && p.y_rows16) {
+        constexpr int RS = S::BM * (S::BN * 2 + 16) <= S::STAGES * S::STAGE ? S::BN * 2 + 16 : S::BN * 2;
+        static_assert(S::BM * S::BN * 2 <= S::STAGES * S::STAGE, "staged output tile must fit the LDS buffers");
+        lds_barrier();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int lr = wm * S::WM + fm * 16 + frow;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const float4 v = t[fn][fm];
+                const float y0 = v.x * sxm[fm], y1 = v.y * sxm[fm], y2 = v.z * sxm[fm], y3 = v.w * sxm[fm];
+                const uint2 w = out == OUT_F16 ? make_uint2(f16_bits(y0) | (f16_bits(y1) << 16), f16_bits(y2) | (f16_bits(y3) << 16))
+                                               : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
+                *reinterpret_cast<uint2 *>(smem + lr * RS + 2 * (wn * S::WN + fn * 16 + 4 * fchunk)) = w;
+            }
+        }
+        lds_barrier();
+        constexpr int CPR = S::BN / 8;
+        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
+#pragma unroll 4
+        for (int c = tid; c < S::BM * CPR; c += S::NT) {
+            const int r = c / CPR, cc = c - r * CPR;
+            if (r < rows && cc * 8 < cols) {
+                const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
+                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm * S::WM + fm * 16 + frow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+            if (n >= N) continue;
+            const float4 v = t[fn][fm];
+            store4(p.y, (int64_t)m * p.ldy + n, out, v.x * sxm[fm], v.y * sxm[fm], v.z * sxm[fm], v.w * sxm[fm]);
+        }
+    }
+}
+
 // ---- weights through LDS, activations direct to registers ----------------------------
 //
 // Measured on gfx950: LDS serves about 128 B/clk per CU for ds_read_b128 and DMA writes
@@ -1402,6 +1672,7 @@ constexpr Config kConfigs[] = {
     {256, 256, 4},  // 8: weights via 4-stage LDS ring, activations direct, 4 waves (256 n x 64 m each)
     {256, 256, 4},  // 9: weights via 4-stage LDS ring, activations direct, 8 waves (128 n x 64 m each)
     {16, 16, 1},    // 10: small-M weight-streaming GEMV (M <= 16)
+    {256, 128, 4},  // 11: per-group / W4A8 on the direct-to-LDS pipeline, BN=128 BM=256 (per-channel: 7)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1447,6 +1718,26 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 
+template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK>
+hipError_t launch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
+    TileMap t;
+    t.tiles_m = (p.M + BM - 1) / BM;
+    t.tiles_n = (p.N + BN - 1) / BN;
+    t.group_m = group_m;
+    dim3 grid(t.tiles_m * t.tiles_n), block(64 * WGM * WGN);
+    hipLaunchKernelGGL((gemm_mg_kernel<BN, BM, STAGES, WGN, WGM, GS, WK>), grid, block, 0, stream, p, t);
+    return hipGetLastError();
+}
+
+hipError_t dispatch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
+    if (p.wkind == W_INT4) {
+        if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT4>(p, group_m, stream);
+        return launch_mg<128, 256, 3, 2, 4, 128, W_INT4>(p, group_m, stream);
+    }
+    if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT8>(p, group_m, stream);
+    return launch_mg<128, 256, 3, 2, 4, 128, W_INT8>(p, group_m, stream);
+}
+
 int choose_config(const GemmProblem &p) {
     // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel (6)
     // does the most work per unit time, the 128 x 256 one (7) about 0.9 of that per tile
@@ -1454,6 +1745,7 @@ int choose_config(const GemmProblem &p) {
     // tiles cost a whole tile); small M uses 64 x 64 tiles.
     if (p.M <= 16) return 10;
     if (p.M <= 128) return 4;
+    if (p.gs > 0 && p.out != OUT_I32) return p.K % 128 == 0 ? 11 : 0;
     if (p.K % 128 != 0 || p.wkind != W_INT8) return 1;
     const int64_t cus = num_cus();
     const int64_t tm = (p.M + 255) / 256;
@@ -1479,6 +1771,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         id = 4;
     }
     const bool grouped = p.gs > 0 && p.out != OUT_I32;
+    if (grouped && id == 11 && p.K % 128 == 0) return dispatch_mg(p, kConfigs[11].group_m, stream);
     if (grouped) {
         if (id != 4) id = 0;
         const int gm = kConfigs[id].group_m;
@@ -1489,6 +1782,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
     const bool dma_ok = p.K % 128 == 0 && p.wkind == W_INT8;
     if (id >= 5 && !dma_ok) id = 1;
     switch (id) {
+        case 11: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
         case 6: return launch_ms<160, 256, 3, 2, 4>(p, gm, stream);
         case 7: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
