@@ -497,7 +497,11 @@ __device__ __forceinline__ void ms_mma(v4i (&acc)[S::FN][S::FM], const v4i (&a)[
 }
 
 template <int BN, int BM, int STAGES, int WGN, int WGM>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_ms_kernel(GemmProblem p, TileMap tmap) {
+// Declared for 512 threads even when launched with 4 waves: at that bound the compiler
+// budgets 256 registers per wave and keeps the MFMA accumulators in arch VGPRs, each MFMA
+// accumulating in place. With a 256-thread bound it moves them to AGPRs without tying
+// source and destination, and copies every accumulator back at the loop edge.
+__global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tmap) {
     using S = MsShape<BN, BM, STAGES, WGN, WGM>;
     constexpr int FM = S::FM, FN = S::FN, GPW = S::GPW;
     __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * S::STAGE];
@@ -783,7 +787,7 @@ __device__ __forceinline__ void mg_scales(const int8_t *st, int gi, int wn, int 
 }
 
 template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mg_kernel(GemmProblem p, TileMap tmap) {
+__global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tmap) {  // see gemm_ms_kernel
     using S = MgShape<BN, BM, STAGES, WGN, WGM, GS, WK>;
     constexpr int FM = S::FM, FN = S::FN;
     __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * S::STAGE];
@@ -1673,6 +1677,7 @@ constexpr Config kConfigs[] = {
     {256, 256, 4},  // 9: weights via 4-stage LDS ring, activations direct, 8 waves (128 n x 64 m each)
     {16, 16, 1},    // 10: small-M weight-streaming GEMV (M <= 16)
     {256, 128, 4},  // 11: per-group / W4A8 on the direct-to-LDS pipeline, BN=128 BM=256 (per-channel: 7)
+    {64, 64, 4},    // 12: direct-to-LDS, BN=64 BM=64, 4 stages, 4 waves (32 n x 32 m each); small M
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1729,7 +1734,15 @@ hipError_t launch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t dispatch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
+// Per-group / W4A8 on the DMA pipeline: 128 x 256 tiles, or 64 x 64 for small M.
+hipError_t dispatch_mg(const GemmProblem &p, bool small, int group_m, hipStream_t stream) {
+    if (small) {
+        if (p.wkind == W_INT4)
+            return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT4>(p, group_m, stream)
+                              : launch_mg<64, 64, 4, 2, 2, 128, W_INT4>(p, group_m, stream);
+        return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT8>(p, group_m, stream)
+                          : launch_mg<64, 64, 4, 2, 2, 128, W_INT8>(p, group_m, stream);
+    }
     if (p.wkind == W_INT4) {
         if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT4>(p, group_m, stream);
         return launch_mg<128, 256, 3, 2, 4, 128, W_INT4>(p, group_m, stream);
@@ -1739,20 +1752,31 @@ hipError_t dispatch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 int choose_config(const GemmProblem &p) {
-    // Measured on MI355X (per-channel, fp16 out): the 160 x 256 three-stage DMA kernel (6)
-    // does the most work per unit time, the 128 x 256 one (7) about 0.9 of that per tile
-    // area. Pick the one with fewer chip-wide rounds of tiles times tile area (partial
-    // tiles cost a whole tile); small M uses 64 x 64 tiles.
-    if (p.M <= 16) return 10;
-    if (p.M <= 128) return 4;
-    if (p.gs > 0 && p.out != OUT_I32) return p.K % 128 == 0 ? 11 : 0;
-    if (p.K % 128 != 0 || p.wkind != W_INT8) return 1;
+    // Measured on MI355X (fp16 out, M = 32 .. 8192, N = 2560 .. 12288, K = 2560 .. 12288).
+    if (p.M <= 16) return 10;  // weight-streaming GEMV
+    const bool dma = p.K % 128 == 0;
     const int64_t cus = num_cus();
-    const int64_t tm = (p.M + 255) / 256;
-    const int64_t t6 = tm * ((p.N + 159) / 160), t7 = tm * ((p.N + 127) / 128);
-    if (t7 < 48) return 4;
-    const int64_t cost6 = (t6 + cus - 1) / cus * 160 * 10, cost7 = (t7 + cus - 1) / cus * 128 * 11;
-    return cost6 <= cost7 ? 6 : 7;
+    if (p.gs > 0 && p.out != OUT_I32) {
+        // per-group: the 128 x 256 DMA kernel once it has enough tiles to spread over the
+        // chip (the group fold is VALU work it does not overlap); below that the
+        // register-staged 64 x 64 kernel, except int8 at M <= 128 (64 x 64 DMA tiles)
+        if (!dma) return p.M <= 128 ? 4 : 0;
+        const int64_t t11 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
+        if (t11 >= (p.wkind == W_INT4 ? cus : cus / 2)) return 11;
+        return p.wkind == W_INT8 && p.M <= 128 ? 12 : 4;
+    }
+    if (!dma || p.wkind != W_INT8) return p.M <= 128 ? 4 : 1;
+    // per-channel: among the DMA kernels, the fewest chip-wide rounds of tiles times tile
+    // area over the kernel's work rate per unit area (160 x 256: 1.0, 128 x 256: 0.9,
+    // 64 x 64: 0.4); partial tiles and a partly filled last round cost whole ones
+    const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
+    const int64_t t7 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
+    const int64_t t12 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+    const double c6 = (double)((t6 + cus - 1) / cus) * 160 * 256 / 1.0;
+    const double c7 = (double)((t7 + cus - 1) / cus) * 128 * 256 / 0.9;
+    const double c12 = (double)((t12 + cus - 1) / cus) * 64 * 64 / 0.4;
+    if (c12 < c6 && c12 < c7) return 12;
+    return c6 <= c7 ? 6 : 7;
 }
 
 }  // namespace
@@ -1771,7 +1795,8 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         id = 4;
     }
     const bool grouped = p.gs > 0 && p.out != OUT_I32;
-    if (grouped && id == 11 && p.K % 128 == 0) return dispatch_mg(p, kConfigs[11].group_m, stream);
+    if (grouped && (id == 11 || id == 12) && p.K % 128 == 0)
+        return dispatch_mg(p, id == 12, kConfigs[id].group_m, stream);
     if (grouped) {
         if (id != 4) id = 0;
         const int gm = kConfigs[id].group_m;
@@ -1783,6 +1808,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
     if (id >= 5 && !dma_ok) id = 1;
     switch (id) {
         case 11: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
+        case 12: return launch_ms<64, 64, 4, 2, 2>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
         case 6: return launch_ms<160, 256, 3, 2, 4>(p, gm, stream);
         case 7: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
