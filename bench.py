@@ -11,8 +11,9 @@ the GEMV kernel); for M <= 128 the weights rotate over copies totalling more tha
 512 MB, so that no step finds them in the 256 MB Infinity Cache.
 
 Prints ONE JSON line: metric/value (INT8 TOPS = 2*M*N*K / step time), a roofline
-object for the dominant kernel (the GEMM, timed with HIP events on its stream over
-the timed region) and a cpu_baseline object (the CPU oracle timed on a bounded
+object for the dominant kernel (the GEMM; its launch duration is timed with HIP events
+on its stream around as many back-to-back launches as there are timed steps, right after
+them, with no event between launches) and a cpu_baseline object (the CPU oracle timed on a bounded
 sample of the same workload on the host cores).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
@@ -63,7 +64,7 @@ def parse():
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a counter reference)")
     ap.add_argument("--no-graph", action="store_true",
-                    help="issue small-M steps one by one instead of as a graph replay (for counter "
+                    help="issue the steps one by one instead of as a graph replay (for counter "
                          "collection; the timing then includes the host's issue time)")
     return ap.parse_args()
 
@@ -167,25 +168,27 @@ def main():
         def gemm(w):
             w8a8.w8a8_gemm_pc(xq, sx, w, sw, y=y, stream=stream)
 
-    def step(i, ev=None):
+    def step(i):
         w = copies[i % len(copies)]
         if fused:
             cur = torch.cuda.current_stream()
-            if ev is not None:
-                ev[0].record(cur)
             w8a8.w8a8_linear(x, w, sw, bits, gs, y=y, x_q=xq, s_x=sx, stream=cur)
-            if ev is not None:
-                ev[1].record(cur)
-                ev[2].record(cur)
             return
-        if ev is not None:
-            ev[0].record(stream)
         w8a8.quantize_per_token(x, xq, sx, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         gemm(w)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def launch_ms(launch, stream):
+        """Average duration of one launch: args.steps launches issued back to back on the
+        stream the kernel runs on, between two events on that stream. Events between the
+        launches themselves would add their own time to every kernel they bracket."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            launch(args.warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
     # setup, not a step: touch every weight copy once (page tables warm, as in a serving
     # loop), then the warmup steps
@@ -195,10 +198,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    if fused and not args.no_graph:
-        # A step is one short kernel (a few microseconds), shorter than the host's time to
-        # issue it, so the timed steps are replayed as one captured graph: the kernels then
-        # run back to back and the events around the replay measure them, not the host.
+    if not args.no_graph:
+        # The timed steps are replayed as one captured graph: the kernels then run back to
+        # back (a fused step is a few microseconds, shorter than the host's time to issue
+        # it) and the events around the replay measure them, not the host.
         stream = torch.cuda.Stream()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
@@ -213,18 +216,26 @@ def main():
             e1.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        quant_ms = gemm_ms = e0.elapsed_time(e1) / args.steps
+        step_event_ms = e0.elapsed_time(e1) / args.steps
+        stream = torch.cuda.current_stream()
     else:
-        events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(args.warmup + i, events[i])
+            step(args.warmup + i)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        # medians: a few steps absorb host hiccups that are not kernel time
-        quant_ms = float(np.median([a.elapsed_time(b) for a, b, _ in events]))
-        gemm_ms = float(np.median([b.elapsed_time(c) for _, b, c in events]))
+        step_event_ms = None
+    if fused:
+        quant_ms = gemm_ms = step_event_ms if step_event_ms is not None else launch_ms(step, stream)
+    else:
+        # per-kernel durations on the same stream, right after the timed steps; the
+        # quantization rotates over copies of x larger than the Infinity Cache, since in a
+        # step the GEMM's traffic evicts x between two quantizations
+        xs = [x] + [x.clone() for _ in range((512 << 20) // (x.numel() * x.element_size()))]
+        quant_ms = launch_ms(lambda i: w8a8.quantize_per_token(xs[i % len(xs)], xq, sx, stream=stream), stream)
+        gemm_ms = launch_ms(lambda i: gemm(copies[i % len(copies)]), stream)
+        del xs
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ops = 2.0 * M * N * K

@@ -206,7 +206,7 @@ def test_gemm_strided_output_and_empty(w8a8):
     # row strides of 304 (16-byte rows: staged stores) and 276 (8-byte rows: direct
     # stores), both 16-bit types, in the automatic choice and the DMA-pipeline kernels
     try:
-        for cfg in (-1, 6, 7):
+        for cfg in (-1, 6, 7, 13):
             w8a8.w8a8_debug_force_config(cfg)
             for ldy in (304, 276):
                 for out, fmt in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
@@ -296,8 +296,8 @@ def _bf16_rne_bits(f32: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("M,N,K,cfgs", [(300, 528, 1280, (-1, 0, 1, 4, 5, 6, 7)), (9, 1040, 640, (-1, 10, 4)),
-                                        (2000, 5280, 384, (-1, 6, 7))])
+@pytest.mark.parametrize("M,N,K,cfgs", [(300, 528, 1280, (-1, 0, 1, 4, 5, 6, 7, 13)), (9, 1040, 640, (-1, 10, 4)),
+                                        (2000, 5280, 384, (-1, 6, 7, 13))])
 def test_pc_epilogue_rounding_exact(w8a8, M, N, K, cfgs):
     """Per-channel outputs are RNE of the fp32 value ((fp32)acc * s_x) * s_w, two fp32
     roundings and then one to fp16/bf16, in every tile configuration: checked exactly

@@ -638,6 +638,194 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
     }
 }
 
+// ---- per-channel, two wave groups in alternation ("ping-pong") -----------------------
+//
+// BN x BM tile (weights x tokens), 64-value K-steps, STAGES LDS stages filled by
+// global_load_lds, eight waves in two groups of four. Group g owns tokens
+// [g BM/2, (g+1) BM/2) of the tile and wave q of a group owns weight rows [q BN/4,
+// (q+1) BN/4), so each SIMD holds one wave of each group. Every K-step has two phases
+// separated by workgroup barriers; group 1 starts one phase late (one extra barrier),
+// so while one group issues its MFMAs the other reads its next fragments from LDS and
+// issues its share of the DMA for a later stage. The matrix pipe of each SIMD then
+// alternates between the two waves instead of idling while both wait on LDS at once,
+// which is what a single barrier per K-tile with all waves in step leaves it doing.
+//
+// Stage j is read by group 0 in phase 2j and by group 1 in phase 2j+1. Each wave waits
+// for its own DMA of stage j+1 at the end of its memory phase of K-step j, so both
+// groups' parts of a stage have landed by the barrier before its first reader; the
+// buffer of stage j-1 is refilled (with stage j+STAGES-1) only in memory phases that
+// follow both groups' reads of it.
+template <int BN_, int BM_, int STAGES_>
+struct PpShape {
+    static constexpr int BN = BN_, BM = BM_, BK = 64, STAGES = STAGES_;
+    static constexpr int NW = 8, NT = 512;
+    static constexpr int WN = BN / 4, WM = BM / 2;
+    static constexpr int FN = WN / 16, FM = WM / 16;
+    static constexpr int W_TILE = BN * BK, STAGE = (BN + BM) * BK;
+    static constexpr int PIECES = (BN + BM) / 16;        // 1 KiB DMA pieces (16 rows) per stage
+    static constexpr int PPW = (PIECES + NW - 1) / NW;   // pieces per wave (max)
+    static constexpr int FULL_WAVES = PIECES - (PPW - 1) * NW;
+    static constexpr int LDS = 163840;
+    static constexpr int CPR = BN / 8;                   // 16-byte output chunks per staged row
+    static_assert(BN % 64 == 0 && BM % 32 == 0, "tile shape");
+    static_assert(STAGES >= 2 && STAGES <= 4 && STAGES * STAGE <= LDS, "stages");
+    static_assert(BM * BN * 2 <= LDS, "staged output tile");
+    static_assert(2 * PPW < 64, "vmcnt range");
+};
+
+template <class S>
+__device__ __forceinline__ void pp_issue(const int8_t *const (&src)[S::PPW], int koff, int8_t *stage, int wave) {
+#pragma unroll
+    for (int j = 0; j < S::PPW; ++j)
+        if (j < S::PPW - 1 || wave < S::FULL_WAVES) dma_16B(src[j] + koff, stage + (wave + j * S::NW) * 1024);
+}
+
+// Wait until at most `after` stages of this wave's DMA are still in flight.
+template <class S>
+__device__ __forceinline__ void pp_wait(int after, bool full) {
+    constexpr int G = S::PPW, g = S::PPW - 1;
+    if (after <= 0) {
+        wait_vmcnt<0>();
+    } else if (after == 1) {
+        if (full) wait_vmcnt<G>(); else wait_vmcnt<g>();
+    } else {
+        if (full) wait_vmcnt<2 * G>(); else wait_vmcnt<2 * g>();
+    }
+}
+
+template <int BN, int BM, int STAGES>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tmap) {
+    using S = PpShape<BN, BM, STAGES>;
+    constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[S::LDS];
+
+    int tm, tn;
+    map_tile(tmap, tm, tn);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;
+    const bool full = wave < S::FULL_WAVES;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    // Loader: wave w issues pieces g = w + j * NW of each stage (pieces below BN / 16 are
+    // weight rows, the rest token rows); lane i covers row 16 g + i / 4 of the stage and
+    // loads its 16-byte chunk (i & 3) ^ ((row >> 2) & 3), which is where the fragment
+    // reads look for it.
+    const int8_t *src[PPW];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+        const int g = min(wave + j * S::NW, S::PIECES - 1);
+        const bool is_w = g < BN / 16;
+        const int lrow = (is_w ? g : g - BN / 16) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((lrow >> 2) & 3);
+        const int grow = is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
+        src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + 16 * c);
+    }
+
+    v4i acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int KT = K / S::BK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) pp_issue<S>(src, s * S::BK, smem + s * S::STAGE, wave);
+    pp_wait<S>(min(STAGES - 2, KT - 1), full);
+    lds_barrier();
+    if (grp == 1) lds_barrier();  // group 1 runs one phase behind group 0
+
+    v4i a[FN], b[FM];
+    int cur = 0, fb = STAGES - 1;  // buffers of stage j and of stage j + STAGES - 1
+    for (int j = 0; j < KT; ++j) {
+        // memory phase
+        if (j + STAGES - 1 < KT) pp_issue<S>(src, (j + STAGES - 1) * S::BK, smem + fb * S::STAGE, wave);
+        const int8_t *st = smem + cur * S::STAGE;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            a[fn] = *reinterpret_cast<const v4i *>(st + swz<64>(wq * S::WN + fn * 16 + frow, fchunk));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<64>(grp * S::WM + fm * 16 + frow, fchunk));
+        wait_lgkmcnt0();
+        if (j + 1 < KT) pp_wait<S>(min(STAGES - 2, KT - 2 - j), full);
+        lds_barrier();
+        // compute phase
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+        lds_barrier();
+        cur = cur + 1 == STAGES ? 0 : cur + 1;
+        fb = fb + 1 == STAGES ? 0 : fb + 1;
+    }
+    if (grp == 0) lds_barrier();  // pairs with group 1's last compute barrier: LDS is free
+
+    // ---- epilogue (per-channel dequant or raw int32) ----
+    const float *__restrict__ sxp = p.sx;
+    const float *__restrict__ swp = p.sw;
+    float sxm[FM];
+    float4 s4[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sxm[fm] = sxp[min(m0 + grp * S::WM + fm * 16 + frow, M - 1)];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        s4[fn] = *reinterpret_cast<const float4 *>(swp + min(n0 + wq * S::WN + fn * 16 + 4 * fchunk, N - 4));
+    const int out = p.out;
+    if ((out == OUT_F16 || out == OUT_BF16) && p.y_rows16) {
+        // staged through LDS as [BM][BN] 16-bit rows with the 16-byte chunk index XOR-ed
+        // with (row & 7): the MFMA layout's 8-byte writes (16 rows per instruction) and
+        // the row-contiguous 16-byte reads both stay free of bank conflicts
+        constexpr int RS = S::BN * 2;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int lr = grp * S::WM + fm * 16 + frow;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const v4i v = acc[fn][fm];
+                const float y0 = ((float)v[0] * sxm[fm]) * s4[fn].x, y1 = ((float)v[1] * sxm[fm]) * s4[fn].y;
+                const float y2 = ((float)v[2] * sxm[fm]) * s4[fn].z, y3 = ((float)v[3] * sxm[fm]) * s4[fn].w;
+                const uint2 w = out == OUT_F16 ? make_uint2(f16_bits(y0) | (f16_bits(y1) << 16), f16_bits(y2) | (f16_bits(y3) << 16))
+                                               : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
+                const int nl = wq * S::WN + fn * 16 + 4 * fchunk;
+                *reinterpret_cast<uint2 *>(smem + lr * RS + (((nl >> 3) ^ (lr & 7)) << 4) + ((nl & 4) << 1)) = w;
+            }
+        }
+        lds_barrier();
+        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
+#pragma unroll 4
+        for (int c = tid; c < S::BM * S::CPR; c += S::NT) {
+            const int r = c / S::CPR, cc = c - r * S::CPR;
+            if (r < rows && cc * 8 < cols) {
+                const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + ((cc ^ (r & 7)) << 4));
+                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + grp * S::WM + fm * 16 + frow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + wq * S::WN + fn * 16 + 4 * fchunk;
+            if (n >= N) continue;
+            const int64_t off = (int64_t)m * p.ldy + n;
+            const v4i v = acc[fn][fm];
+            if (out == OUT_I32) {
+                *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = make_int4(v[0], v[1], v[2], v[3]);
+            } else {
+                store4(p.y, off, out, ((float)v[0] * sxm[fm]) * s4[fn].x, ((float)v[1] * sxm[fm]) * s4[fn].y,
+                       ((float)v[2] * sxm[fm]) * s4[fn].z, ((float)v[3] * sxm[fm]) * s4[fn].w);
+            }
+        }
+    }
+}
+
 // ---- per-group and W4A8 on the direct-to-LDS pipeline ---------------------------------
 //
 // The structure of gemm_ms_kernel (BN x BM tile, 128-value K-tiles, STAGES LDS stages filled
@@ -1678,6 +1866,7 @@ constexpr Config kConfigs[] = {
     {16, 16, 1},    // 10: small-M weight-streaming GEMV (M <= 16)
     {256, 128, 4},  // 11: per-group / W4A8 on the direct-to-LDS pipeline, BN=128 BM=256 (per-channel: 7)
     {64, 64, 4},    // 12: direct-to-LDS, BN=64 BM=64, 4 stages, 4 waves (32 n x 32 m each); small M
+    {256, 320, 4},  // 13: direct-to-LDS, BN=320 BM=256, 4 stages of 64, two wave groups in alternation
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1722,6 +1911,17 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
     return hipGetLastError();
 }
 
+
+template <int BN, int BM, int STAGES>
+hipError_t launch_pp(const GemmProblem &p, int group_m, hipStream_t stream) {
+    TileMap t;
+    t.tiles_m = (p.M + BM - 1) / BM;
+    t.tiles_n = (p.N + BN - 1) / BN;
+    t.group_m = group_m;
+    dim3 grid(t.tiles_m * t.tiles_n), block(512);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES>), grid, block, 0, stream, p, t);
+    return hipGetLastError();
+}
 
 template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK>
 hipError_t launch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
@@ -1804,11 +2004,12 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         return launch_grouped<128, 128, 2, 2>(p, gm, stream);
     }
     const int gm = kConfigs[id].group_m;
-    const bool dma_ok = p.K % 128 == 0 && p.wkind == W_INT8;
+    const bool dma_ok = p.K % (id == 13 ? 64 : 128) == 0 && p.wkind == W_INT8;
     if (id >= 5 && !dma_ok) id = 1;
     switch (id) {
         case 11: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
         case 12: return launch_ms<64, 64, 4, 2, 2>(p, gm, stream);
+        case 13: return launch_pp<320, 256, 4>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
         case 6: return launch_ms<160, 256, 3, 2, 4>(p, gm, stream);
         case 7: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
