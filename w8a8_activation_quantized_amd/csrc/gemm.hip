@@ -422,9 +422,14 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
     __builtin_amdgcn_sched_barrier(0);
 }
-// Workgroup barrier that the compiler may not move memory operations across.
+// Workgroup barrier that the compiler may not move memory operations across. The
+// s_barrier is written as asm, so the compiler adds no wait before it: this wave's LDS
+// writes (and reads) are waited for here, else another wave may pass the barrier and
+// read LDS that a write of this wave has not reached yet. DMA into LDS is counted by
+// vmcnt and waited for separately.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -645,16 +650,16 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
 // [g BM/2, (g+1) BM/2) of the tile and wave q of a group owns weight rows [q BN/4,
 // (q+1) BN/4), so each SIMD holds one wave of each group. Every K-step has two phases
 // separated by workgroup barriers; group 1 starts one phase late (one extra barrier),
-// so while one group issues its MFMAs the other reads its next fragments from LDS and
-// issues its share of the DMA for a later stage. The matrix pipe of each SIMD then
-// alternates between the two waves instead of idling while both wait on LDS at once,
-// which is what a single barrier per K-tile with all waves in step leaves it doing.
+// so while one group issues its MFMAs (and, between them, its share of the DMA for a
+// later stage) the other reads its next fragments from LDS. The matrix pipe of each SIMD
+// then alternates between the two waves instead of idling while both wait on LDS at
+// once, which is what a single barrier per K-tile with all waves in step leaves it doing.
 //
 // Stage j is read by group 0 in phase 2j and by group 1 in phase 2j+1. Each wave waits
 // for its own DMA of stage j+1 at the end of its memory phase of K-step j, so both
 // groups' parts of a stage have landed by the barrier before its first reader; the
-// buffer of stage j-1 is refilled (with stage j+STAGES-1) only in memory phases that
-// follow both groups' reads of it.
+// buffer of stage j-1 is refilled (with stage j+STAGES-1) in the compute phase of K-step
+// j, which follows both groups' reads of it.
 template <int BN_, int BM_, int STAGES_>
 struct PpShape {
     static constexpr int BN = BN_, BM = BM_, BK = 64, STAGES = STAGES_;
@@ -667,8 +672,10 @@ struct PpShape {
     static constexpr int FULL_WAVES = PIECES - (PPW - 1) * NW;
     static constexpr int LDS = 163840;
     static constexpr int CPR = BN / 8;                   // 16-byte output chunks per staged row
+    static constexpr int SP = FN * FM / PPW;             // MFMAs between a wave's DMA pieces
+    static_assert(SP >= 8, "DMA slots SP i + 2 Q of the four waves of a group");
     static_assert(BN % 64 == 0 && BM % 32 == 0, "tile shape");
-    static_assert(STAGES >= 2 && STAGES <= 4 && STAGES * STAGE <= LDS, "stages");
+    static_assert(STAGES >= 3 && STAGES <= 4 && STAGES * STAGE <= LDS, "stages");
     static_assert(BM * BN * 2 <= LDS, "staged output tile");
     static_assert(2 * PPW < 64, "vmcnt range");
 };
@@ -690,6 +697,51 @@ __device__ __forceinline__ void pp_wait(int after, bool full) {
         if (full) wait_vmcnt<G>(); else wait_vmcnt<g>();
     } else {
         if (full) wait_vmcnt<2 * G>(); else wait_vmcnt<2 * g>();
+    }
+}
+
+// The K loop of one wave; Q = the wave's index in its group, a template parameter so that
+// each wave's DMA slots are fixed in its own copy of the code (no branches between the
+// MFMAs). A DMA instruction holds the CU's address unit for about one MFMA's time and a
+// wave cannot issue past one that waits for it; piece i of wave Q goes after MFMA
+// SP i + 2 Q, so the four waves of a group, released by the same barrier, do not queue
+// behind each other and the MFMA stream of each is not held up.
+template <class S, int Q>
+__device__ __forceinline__ void pp_loop(v4i (&acc)[S::FN][S::FM], const int8_t *const (&src)[S::PPW], int8_t *smem,
+                                        int KT, int grp, int wave, bool full, int frow, int fchunk) {
+    constexpr int FN = S::FN, FM = S::FM, PPW = S::PPW, STAGES = S::STAGES;
+    v4i a[FN], b[FM];
+    int cur = 0, fb = STAGES - 1;  // buffers of stage j and of stage j + STAGES - 1
+    for (int j = 0; j < KT; ++j) {
+        // memory phase: this K-step's fragments; this wave's part of stage j + 1 landed
+        const int8_t *st = smem + cur * S::STAGE;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            a[fn] = *reinterpret_cast<const v4i *>(st + swz<64>(Q * S::WN + fn * 16 + frow, fchunk));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<64>(grp * S::WM + fm * 16 + frow, fchunk));
+        wait_lgkmcnt0();
+        if (j + 1 < KT) pp_wait<S>(min(STAGES - 3, KT - 2 - j), full);
+        lds_barrier();
+        // compute phase, with this wave's DMA for stage j + STAGES - 1 in its slots
+        const bool fill = j + STAGES - 1 < KT, fill_last = fill && full;
+        const int koff = (j + STAGES - 1) * S::BK;
+        int8_t *fdst = smem + fb * S::STAGE + wave * 1024;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+                const int t = fn * FM + fm;
+                if (t % S::SP == 2 * Q && t / S::SP < PPW) {
+                    const int piece = t / S::SP;
+                    if (piece < PPW - 1 ? fill : fill_last) dma_16B(src[piece] + koff, fdst + piece * S::NW * 1024);
+                }
+            }
+        lds_barrier();
+        cur = cur + 1 == STAGES ? 0 : cur + 1;
+        fb = fb + 1 == STAGES ? 0 : fb + 1;
     }
 }
 
@@ -738,29 +790,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
     lds_barrier();
     if (grp == 1) lds_barrier();  // group 1 runs one phase behind group 0
 
-    v4i a[FN], b[FM];
-    int cur = 0, fb = STAGES - 1;  // buffers of stage j and of stage j + STAGES - 1
-    for (int j = 0; j < KT; ++j) {
-        // memory phase
-        if (j + STAGES - 1 < KT) pp_issue<S>(src, (j + STAGES - 1) * S::BK, smem + fb * S::STAGE, wave);
-        const int8_t *st = smem + cur * S::STAGE;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            a[fn] = *reinterpret_cast<const v4i *>(st + swz<64>(wq * S::WN + fn * 16 + frow, fchunk));
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-            b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<64>(grp * S::WM + fm * 16 + frow, fchunk));
-        wait_lgkmcnt0();
-        if (j + 1 < KT) pp_wait<S>(min(STAGES - 2, KT - 2 - j), full);
-        lds_barrier();
-        // compute phase
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
-        lds_barrier();
-        cur = cur + 1 == STAGES ? 0 : cur + 1;
-        fb = fb + 1 == STAGES ? 0 : fb + 1;
+    switch (wq) {
+        case 0: pp_loop<S, 0>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+        case 1: pp_loop<S, 1>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+        case 2: pp_loop<S, 2>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+        default: pp_loop<S, 3>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
     }
     if (grp == 0) lds_barrier();  // pairs with group 1's last compute barrier: LDS is free
 
@@ -1967,15 +2001,19 @@ int choose_config(const GemmProblem &p) {
     }
     if (!dma || p.wkind != W_INT8) return p.M <= 128 ? 4 : 1;
     // per-channel: among the DMA kernels, the fewest chip-wide rounds of tiles times tile
-    // area over the kernel's work rate per unit area (160 x 256: 1.0, 128 x 256: 0.9,
-    // 64 x 64: 0.4); partial tiles and a partly filled last round cost whole ones
+    // area over the kernel's work rate per unit area (320 x 256 in alternating wave
+    // groups: 1.05, 160 x 256: 1.0, 128 x 256: 0.9, 64 x 64: 0.4); partial tiles and a
+    // partly filled last round cost whole ones
+    const int64_t t13 = (int64_t)((p.M + 255) / 256) * ((p.N + 319) / 320);
     const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
     const int64_t t7 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
     const int64_t t12 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+    const double c13 = (double)((t13 + cus - 1) / cus) * 320 * 256 / 1.05;
     const double c6 = (double)((t6 + cus - 1) / cus) * 160 * 256 / 1.0;
     const double c7 = (double)((t7 + cus - 1) / cus) * 128 * 256 / 0.9;
     const double c12 = (double)((t12 + cus - 1) / cus) * 64 * 64 / 0.4;
-    if (c12 < c6 && c12 < c7) return 12;
+    if (c12 < c6 && c12 < c7 && c12 < c13) return 12;
+    if (c13 < c6 && c13 < c7) return 13;
     return c6 <= c7 ? 6 : 7;
 }
 
