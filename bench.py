@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle sample")
@@ -120,6 +120,125 @@ def cpu_baseline(x, W, bits, gs, budget_s):
                       f"per-token quantize + int GEMM + fp64 dequant; {dt:.2f} s"}
 
 
+def timed_steps(args, torch, step):
+    """Warmup, then args.steps steps replayed as one captured graph (or issued one by one
+    with --no-graph). Returns (ms per step by the host clock, ms per step by events or
+    None)."""
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.no_graph:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, None
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(side):
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / args.steps, e0.elapsed_time(e1) / args.steps
+
+
+def qwen3_block(args, torch, w8a8):
+    """One Qwen3-8B-shaped decoder block's seven linears at prefill (M=2048 tokens), W8A8
+    per-channel, bf16 out: each of the four block inputs is quantized once per step; q, k,
+    v share one GEMM over their concatenated weights (N = 6144) and gate, up another
+    (N = 24576): exact, since per-channel weight scales belong to output rows."""
+    from synth_inputs import qwen3_8b_block_inputs, QWEN3_8B_BLOCK
+
+    M = 2048
+    inputs, weights = qwen3_8b_block_inputs(M=M, seed=0)
+    groups = (("attn_in", ("q", "k", "v")), ("o_in", ("o",)), ("mlp_in", ("gate", "up")), ("down_in", ("down",)))
+    ops = sum(2.0 * M * N * K for _, K, N in QWEN3_8B_BLOCK)
+    stages = []
+    for in_name, projs in groups:
+        x = torch.from_numpy(inputs[in_name]).cuda()
+        W_host = np.concatenate([weights[n] for n in projs])
+        wq, sw = w8a8.quantize_weight(torch.from_numpy(W_host).cuda(), 8, 0)  # offline: not timed
+        K, N = x.shape[1], wq.shape[0]
+        stages.append({"name": "+".join(projs), "x": x, "wq": wq, "sw": sw, "N": N, "K": K,
+                       "x_host": inputs[in_name], "W_host": W_host,
+                       "xq": torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                       "sx": torch.empty((M,), dtype=torch.float32, device="cuda"),
+                       "y": torch.empty((M, N), dtype=torch.bfloat16, device="cuda")})
+    del inputs, weights
+
+    def run(st, stream):
+        w8a8.quantize_per_token(st["x"], st["xq"], st["sx"], stream=stream)
+        w8a8.w8a8_gemm_pc(st["xq"], st["sx"], st["wq"], st["sw"], y=st["y"], stream=stream)
+
+    def step(i):
+        cur = torch.cuda.current_stream()
+        for st in stages:
+            run(st, cur)
+
+    ms_per_step, event_ms = timed_steps(args, torch, step)
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    # dominant kernel: the gate+up GEMM (N = 24576, 52 % of the block's operations)
+    big = max(stages, key=lambda st: st["N"] * st["K"])
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        w8a8.w8a8_gemm_pc(big["xq"], big["sx"], big["wq"], big["sw"], y=big["y"], stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / args.steps
+    big_ops = 2.0 * M * big["N"] * big["K"]
+    achieved = big_ops / (gemm_ms * 1e-3) / 1e12
+    result = {
+        "metric": "INT8 TOPS of one Qwen3-8B block's seven W8A8 linears (quantize + GEMM + dequant), M=2048",
+        "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic",
+        "config": {"workload": "Qwen3-8B block linears at prefill: q,k,v | o | gate,up | down, per-channel, "
+                               "each input quantized per token in the step",
+                   "M": M, "shapes_NK": [[st["N"], st["K"]] for st in stages], "out": "bf16",
+                   "parallelism": "single GPU"},
+        "frac_of_peak_step": value / PEAK_INT8_TOPS,
+        "step_event_ms": event_ms,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                     "frac": achieved / PEAK_INT8_TOPS, "traffic": None,
+                     "kernel": f"gemm ({big['name']}: M={M} N={big['N']} K={big['K']})", "launch_ms": gemm_ms},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = qwen3_cpu_baseline(stages, args.cpu_seconds)
+    return result
+
+
+def qwen3_cpu_baseline(stages, budget_s):
+    """The CPU oracle on a bounded sample of token rows of every projection of the block."""
+    import oracle
+
+    oracle.build(force=False)
+    host = [(st["x_host"], *oracle.quantize_weight(st["W_host"], 8, 0)) for st in stages]
+    rows_done, chunk = 0, 8
+    t0 = time.perf_counter()
+    while rows_done < 2048:
+        for x, wq, sw in host:
+            oracle.linear_pc(x[rows_done:rows_done + chunk], wq, sw)
+        rows_done += chunk
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    ops = sum(2.0 * rows_done * wq.shape[0] * wq.shape[1] for _, wq, _ in host)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows_done} of 2048 token rows of each of the block's projections; "
+                      f"per-token quantize + int GEMM + fp64 dequant; {dt:.2f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,6 +261,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.workload == "qwen3":
+        print(json.dumps(qwen3_block(args, torch, w8a8)), flush=True)
+        return 0
 
     M, N, K, bits, gs = WORKLOADS[args.workload]
     x_np, W_np = linear_inputs(M, N, K, seed=0)

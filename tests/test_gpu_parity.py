@@ -344,6 +344,22 @@ def test_qwen3_block_sampled(w8a8):
             check_output(y[rows], "bf16", r["y"], np.abs(r["y"]), 1, f"qwen3 {name}")
 
 
+def test_concatenated_projections_equal_separate(w8a8):
+    """Projections that share an input (q, k, v; gate, up) run as one GEMM over their
+    concatenated weights in the block benchmark: per-channel scales belong to output rows,
+    so each column block is bit-identical to the projection's own GEMM (which the tests
+    above hold against the oracle), whatever tile configuration each shape selects."""
+    note("concatenated projections")
+    x, W = linear_inputs(520, 1024 + 256 + 256, 1024, seed=23)
+    xq, sx = w8a8.quantize_per_token(dev(x))
+    wq, sw = w8a8.quantize_weight(dev(W), 8, 0)
+    y = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.bfloat16))
+    for a, b in ((0, 1024), (1024, 1280), (1280, 1536)):
+        wq_i, sw_i = w8a8.quantize_weight(dev(W[a:b]), 8, 0)
+        y_i = host(w8a8.w8a8_gemm_pc(xq, sx, wq_i, sw_i, torch.bfloat16))
+        assert (y[:, a:b] == y_i).all(), f"columns {a}:{b} differ"
+
+
 def test_quantize_all_fp16_values_sampled_maxima(w8a8):
     """For 96 row maxima (extremes + random), a row holding every fp16 value of magnitude
     <= the maximum, both signs: codes and scales bit-exact against the oracle's IEEE
