@@ -282,23 +282,23 @@ def main():
     fused = M <= 16
 
     if bits == 4:
-        def gemm(w):
-            w8a8.w4a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=stream)
+        def gemm(w, st):
+            w8a8.w4a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=st)
     elif gs:
-        def gemm(w):
-            w8a8.w8a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=stream)
+        def gemm(w, st):
+            w8a8.w8a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=st)
     else:
-        def gemm(w):
-            w8a8.w8a8_gemm_pc(xq, sx, w, sw, y=y, stream=stream)
+        def gemm(w, st):
+            w8a8.w8a8_gemm_pc(xq, sx, w, sw, y=y, stream=st)
 
     def step(i):
         w = copies[i % len(copies)]
+        cur = torch.cuda.current_stream()
         if fused:
-            cur = torch.cuda.current_stream()
             w8a8.w8a8_linear(x, w, sw, bits, gs, y=y, x_q=xq, s_x=sx, stream=cur)
             return
-        w8a8.quantize_per_token(x, xq, sx, stream=stream)
-        gemm(w)
+        w8a8.quantize_per_token(x, xq, sx, stream=cur)
+        gemm(w, cur)
 
     def launch_ms(launch, stream):
         """Average duration of one launch: args.steps launches issued back to back on the
@@ -314,41 +314,10 @@ def main():
         return e0.elapsed_time(e1) / args.steps
 
     # setup, not a step: touch every weight copy once (page tables warm, as in a serving
-    # loop), then the warmup steps
+    # loop); then the warmup and timed steps
     for i in range(len(copies) if len(copies) > 1 else 0):
         step(i)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    if not args.no_graph:
-        # The timed steps are replayed as one captured graph: the kernels then run back to
-        # back (a fused step is a few microseconds, shorter than the host's time to issue
-        # it) and the events around the replay measure them, not the host.
-        stream = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(args.steps):
-                step(args.warmup + i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            e0.record()
-            graph.replay()
-            e1.record()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        step_event_ms = e0.elapsed_time(e1) / args.steps
-        stream = torch.cuda.current_stream()
-    else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(args.warmup + i)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        step_event_ms = None
+    ms_per_step, step_event_ms = timed_steps(args, torch, step)
     if fused:
         quant_ms = gemm_ms = step_event_ms if step_event_ms is not None else launch_ms(step, stream)
     else:
@@ -357,10 +326,9 @@ def main():
         # step the GEMM's traffic evicts x between two quantizations
         xs = [x] + [x.clone() for _ in range((512 << 20) // (x.numel() * x.element_size()))]
         quant_ms = launch_ms(lambda i: w8a8.quantize_per_token(xs[i % len(xs)], xq, sx, stream=stream), stream)
-        gemm_ms = launch_ms(lambda i: gemm(copies[i % len(copies)]), stream)
+        gemm_ms = launch_ms(lambda i: gemm(copies[i % len(copies)], stream), stream)
         del xs
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
 
@@ -397,6 +365,7 @@ def main():
                    "M": M, "N": N, "K": K, "weight_bits": bits, "group_size": gs, "out": "fp16",
                    "parallelism": "single GPU"},
         "frac_of_peak_step": value / PEAK_INT8_TOPS,
+        "step_event_ms": step_event_ms,
         "gemm_ms": None if fused else gemm_ms,
         "quantize_ms": None if fused else quant_ms,
         "fused_ms": quant_ms if fused else None,
