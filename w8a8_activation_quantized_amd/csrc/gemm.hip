@@ -83,6 +83,19 @@ __device__ __forceinline__ v4u unpack_nibbles(uint32_t d0, uint32_t d1) {
                recentre(interleave_lo(lo1, hi1)), recentre(interleave_hi(lo1, hi1))};
 }
 
+// Eight packed bytes -> sixteen int8 values 16 q in k order, q = u - 8. u ^ 8 is the 4-bit
+// two's complement of q; placed in the high half of a byte it reads as the int8 16 q. Per
+// dword: one xor, two masks (one after a shift) and two byte permutes; the MFMA sums are
+// then 16 x the int4 sums, exactly.
+__device__ __forceinline__ v4u unpack_nibbles_x16(uint32_t d0, uint32_t d1) {
+    const uint32_t e0 = d0 ^ 0x88888888u, e1 = d1 ^ 0x88888888u;
+    const uint32_t h0 = e0 & 0xF0F0F0F0u, l0 = (e0 << 4) & 0xF0F0F0F0u;  // odd k, even k
+    const uint32_t h1 = e1 & 0xF0F0F0F0u, l1 = (e1 << 4) & 0xF0F0F0F0u;
+    // v_perm_b32: selector byte i picks byte i of {h (bytes 4-7), l (bytes 0-3)}
+    return v4u{__builtin_amdgcn_perm(h0, l0, 0x05010400u), __builtin_amdgcn_perm(h0, l0, 0x07030602u),
+               __builtin_amdgcn_perm(h1, l1, 0x05010400u), __builtin_amdgcn_perm(h1, l1, 0x07030602u)};
+}
+
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);
     u += 0x7FFFu + ((u >> 16) & 1u);
@@ -873,8 +886,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
 //
 // int4 weights (WK = W_INT4) are 64 bytes per row per K-tile; a DMA instruction moves 16
 // rows x 64 bytes and the 16-byte pieces of row r sit at position piece ^ ((r >> 2) & 3),
-// which keeps the 8-byte fragment reads conflict-free; fragments are unpacked to int8
-// after the LDS read (nibble split, byte interleave, u - 8).
+// which keeps the 8-byte fragment reads conflict-free; fragments are unpacked after the
+// LDS read to the int8 values 16 q (see unpack_nibbles_x16), so each group's int32 sum is
+// 16 acc_g and the fold keeps 16 t: fma(fp32(16 a), s, 16 t) = 16 fma(fp32(a), s, t)
+// exactly while no value is subnormal (a power-of-two scaling commutes with rounding in
+// the normal range; every product of a nonzero sum and a scale >= 2^-100 is normal).
+// The epilogue multiplies by 2^-4 (exact) before s_x.
 template <int BN_, int BM_, int STAGES_, int WGN_, int WGM_, int GS_, int WK_>
 struct MgShape {
     static constexpr int BN = BN_, BM = BM_, BK = 128, STAGES = STAGES_, WGN = WGN_, WGM = WGM_, GS = GS_, WK = WK_;
@@ -966,7 +983,7 @@ __device__ __forceinline__ void mg_frags(const int8_t *st, int ks, int wm, int w
             const int byte = ks * 32 + fchunk * 8;  // 16 int4 values of this lane
             const uint2 w = *reinterpret_cast<const uint2 *>(st + r * 64 + (((byte >> 4) ^ ((r >> 2) & 3)) << 4) +
                                                              (byte & 15));
-            a[fn] = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
+            a[fn] = __builtin_bit_cast(v4i, unpack_nibbles_x16(w.x, w.y));
         } else {
             a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(r, ks * 4 + fchunk));
         }
@@ -1082,6 +1099,8 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
     }
 
     // ---- epilogue: y = t * s_x[m] ----
+    // int4: t holds 16 x the sum (the unpacked codes are 16 q); the scaling by 2^-4 is exact
+    constexpr float TS = S::WK == W_INT4 ? 0.0625f : 1.0f;
     const float *__restrict__ sxp = p.sx;
     float sxm[FM];
 #pragma unroll
@@ -1097,7 +1116,8 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const float4 v = t[fn][fm];
-                const float y0 = v.x * sxm[fm], y1 = v.y * sxm[fm], y2 = v.z * sxm[fm], y3 = v.w * sxm[fm];
+                const float y0 = (v.x * TS) * sxm[fm], y1 = (v.y * TS) * sxm[fm];
+                const float y2 = (v.z * TS) * sxm[fm], y3 = (v.w * TS) * sxm[fm];
                 const uint2 w = out == OUT_F16 ? make_uint2(f16_bits(y0) | (f16_bits(y1) << 16), f16_bits(y2) | (f16_bits(y3) << 16))
                                                : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
                 *reinterpret_cast<uint2 *>(smem + lr * RS + 2 * (wn * S::WN + fn * 16 + 4 * fchunk)) = w;
@@ -1125,7 +1145,8 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
             const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
             if (n >= N) continue;
             const float4 v = t[fn][fm];
-            store4(p.y, (int64_t)m * p.ldy + n, out, v.x * sxm[fm], v.y * sxm[fm], v.z * sxm[fm], v.w * sxm[fm]);
+            store4(p.y, (int64_t)m * p.ldy + n, out, (v.x * TS) * sxm[fm], (v.y * TS) * sxm[fm],
+                   (v.z * TS) * sxm[fm], (v.w * TS) * sxm[fm]);
         }
     }
 }
