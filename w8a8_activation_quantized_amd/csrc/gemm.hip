@@ -1649,7 +1649,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
                 const int byte = t * 32 + fchunk * 8;
                 const uint2 w = *reinterpret_cast<const uint2 *>(
                     slot + frow * 128 + (((byte >> 4) ^ ((frow >> 1) & 7)) << 4) + (byte & 15));
-                a = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
+                // grouped: 16 q, and facc holds 16 t; the raw int32 sums keep q
+                if constexpr (S::GROUPED)
+                    a = __builtin_bit_cast(v4i, unpack_nibbles_x16(w.x, w.y));
+                else
+                    a = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
             } else {
                 a = *reinterpret_cast<const v4i *>(slot + frow * 128 + (((t * 4 + fchunk) ^ ((frow >> 1) & 7)) << 4));
             }
@@ -1800,7 +1804,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
             t.z += u.z;
             t.w += u.w;
         }
-        store4(p.y, off, p.out, t.x * e_sx, t.y * e_sx, t.z * e_sx, t.w * e_sx);
+        // int4: the partials are 16 x the sums (codes unpacked as 16 q); 2^-4 is exact
+        constexpr float TS = WK == W_INT4 ? 0.0625f : 1.0f;
+        store4(p.y, off, p.out, (t.x * TS) * e_sx, (t.y * TS) * e_sx, (t.z * TS) * e_sx, (t.w * TS) * e_sx);
     } else {
         const int4 *red = reinterpret_cast<const int4 *>(gv_lds);
         int4 t = red[lane];
