@@ -20,10 +20,12 @@
 //    operand, so each lane's four accumulator values are four consecutive output
 //    channels n of one token m: the epilogue writes 8 (fp16/bf16) or 16 (fp32)
 //    contiguous bytes per lane.
-//  * LDS rows are BK bytes; 16-byte chunks are XOR-swizzled by row (chunk ^ ((row >> 1)
-//    & 7) for 128-byte rows). Measured on gfx950 with SQ_LDS_BANK_CONFLICT: this
-//    fragment-read pattern (16 rows x one logical chunk per 16 lanes) runs at the
-//    full 4 cycles per ds_read_b128, where an unswizzled layout takes 16.
+//  * LDS rows are BK bytes; 16-byte chunks are XOR-swizzled by row: chunk ^ ((row >> 1)
+//    & 7) for 128-byte rows, chunk ^ ((row >> 1) & 3) for 64-byte rows. Measured on
+//    gfx950 with SQ_LDS_BANK_CONFLICT: these fragment-read patterns (16 rows x one
+//    logical chunk per 16 lanes) run without conflicts, where an unswizzled 128-byte
+//    layout takes 4x the cycles; for 64-byte rows, (row >> 2) & 3, (row >> 3) & 3,
+//    row & 3 and no swizzle all lose a quarter of the LDS cycles to conflicts.
 //  * Two LDS stages: global loads for tile k+1 are issued into registers before the
 //    MFMAs of tile k and written to the other stage afterwards; one barrier per
 //    K-tile.
@@ -59,7 +61,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
     if constexpr (BK == 128)
         return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
     else
-        return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+        return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
 // Eight packed bytes (two dwords; 16 nibbles, even k in the low nibble) -> sixteen int8
@@ -775,7 +777,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
 
     // Loader: wave w issues pieces g = w + j * NW of each stage (pieces below BN / 16 are
     // weight rows, the rest token rows); lane i covers row 16 g + i / 4 of the stage and
-    // loads its 16-byte chunk (i & 3) ^ ((row >> 2) & 3), which is where the fragment
+    // loads its 16-byte chunk (i & 3) ^ ((row >> 1) & 3), which is where the fragment
     // reads look for it.
     const int8_t *src[PPW];
 #pragma unroll
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
         const int g = min(wave + j * S::NW, S::PIECES - 1);
         const bool is_w = g < BN / 16;
         const int lrow = (is_w ? g : g - BN / 16) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((lrow >> 2) & 3);
+        const int c = (lane & 3) ^ ((lrow >> 1) & 3);
         const int grow = is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
         src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + 16 * c);
     }
