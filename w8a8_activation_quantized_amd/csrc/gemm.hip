@@ -1929,7 +1929,7 @@ constexpr Config kConfigs[] = {
     {16, 16, 1},    // 10: small-M weight-streaming GEMV (M <= 16)
     {256, 128, 4},  // 11: per-group / W4A8 on the direct-to-LDS pipeline, BN=128 BM=256 (per-channel: 7)
     {64, 64, 4},    // 12: direct-to-LDS, BN=64 BM=64, 4 stages, 4 waves (32 n x 32 m each); small M
-    {256, 320, 4},  // 13: direct-to-LDS, BN=320 BM=256, 4 stages of 64, two wave groups in alternation
+    {256, 320, 8},  // 13: direct-to-LDS, BN=320 BM=256, 4 stages of 64, two wave groups in alternation
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
