@@ -157,6 +157,49 @@ int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const fl
                 int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream);
 
 /*
+ * Split-K form of the three GEMM calls, for problems whose output has too few tiles to
+ * occupy the chip (narrow N with long K at M in the hundreds or low thousands): K is cut
+ * into slices of whole 128-value K-tiles that run side by side, each writing its partial
+ * result to a caller-provided workspace, and a second kernel adds the slices in slice order
+ * and applies the dequantization of juejin post "W8A8 对称量化" (per-channel) or
+ * "三种量化粒度的实现" (per-group).
+ *
+ * w8a8_gemm_splitk_workspace: bytes of workspace the split form uses for this problem,
+ *   slices * M * N * 4; 0 when the library would not split it (M <= 16, K % 128 != 0, int4
+ *   weights with W8A8_I32 output, or a single pass estimated faster). The value depends only
+ *   on the arguments, the device's compute-unit count and the debug knobs below.
+ *   Negative: -status for invalid arguments (the checks of the GEMM calls).
+ *
+ * w8a8_gemm_splitk: the GEMM selected as in w8a8_linear (weight_bits 8 / group_size 0:
+ *   w8a8_gemm_pc; 8 / 64|128: w8a8_gemm_pg; 4 / 64|128: w4a8_gemm_pg, w = w_packed),
+ *   same operands, layouts and constraints, plus
+ *   workspace        device memory, 16-byte aligned, owned by the caller, not overlapping
+ *                    any operand; contents on return are unspecified. It must stay
+ *                    allocated until the stream has run the call; two calls in flight at
+ *                    once need two workspaces.
+ *   workspace_bytes  its size. With workspace NULL, or smaller than the query's value,
+ *                    the call runs the single-pass kernels of the matching GEMM call.
+ * Results: per-channel (and W8A8_I32) bit-identical to the matching GEMM call, since
+ * int32 sums are exact in any order; per-group within the same fp32 tolerance, the group
+ * terms being summed per slice and then across slices.
+ */
+int64_t w8a8_gemm_splitk_workspace(int weight_bits, int group_size, int y_dtype, int64_t M, int64_t N,
+                                   int64_t K);
+int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const float *s_w,
+                     int weight_bits, int group_size, void *y, int y_dtype, int64_t M, int64_t N,
+                     int64_t K, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                     void *stream);
+
+/*
+ * Debug knob: force the number of K-slices of w8a8_gemm_splitk (-1 = automatic, 1 = never
+ * split, n >= 2: n slices, at most K / 128). Combined with w8a8_debug_force_config a
+ * configuration with a split form (per-channel 7, 12, 14; per-group 11, 12) is used for the
+ * slices; forcing any other configuration runs the single-pass kernels. Returns W8A8_OK, or
+ * -W8A8_ERR_INVALID_ARGUMENT for 0, < -1 or > 4096. Process-wide.
+ */
+int w8a8_debug_force_splitk(int slices);
+
+/*
  * Debug knob: force the GEMM tile configuration (-1 = automatic choice by shape).
  * Every configuration computes identical results; tests use this to run each one.
  * Returns the number of configurations, or W8A8_ERR_INVALID_ARGUMENT (negated)

@@ -165,3 +165,71 @@ def test_linear_validation(w8a8, kw, status, needle):
 def test_linear_forced_unavailable(w8a8, unavailable):
     lib = w8a8.lib()
     assert _linear(lib) == UNSUPPORTED_DEVICE
+
+
+def _splitk(lib, x_q=FAKE, bits=8, gs=0, y_dtype=F16, M=128, N=2560, K=10240, ldy=2560, ws=FAKE,
+            ws_bytes=1 << 30):
+    return lib.w8a8_gemm_splitk(x_q, FAKE, FAKE, FAKE, bits, gs, FAKE, y_dtype, M, N, K, ldy, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(bits=2), INVALID, "weight_bits"),
+    (dict(gs=32), INVALID, "group_size"),
+    (dict(bits=4, gs=0), INVALID, "int4"),
+    (dict(y_dtype=7), INVALID, "y_dtype"),
+    (dict(N=250, ldy=256), UNSUPPORTED_SHAPE, "N"),
+    (dict(K=100), UNSUPPORTED_SHAPE, "K"),
+    (dict(gs=128, K=192), UNSUPPORTED_SHAPE, "group_size"),
+    (dict(ldy=2500), INVALID, "ldy"),
+    (dict(x_q=None), INVALID, "null"),
+    (dict(ws_bytes=-1), INVALID, "workspace_bytes"),
+    (dict(ws=ctypes.c_void_p(0x100008)), INVALID, "workspace"),
+])
+def test_splitk_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _splitk(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_splitk_forced_unavailable(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert _splitk(lib) == UNSUPPORTED_DEVICE
+    assert _splitk(lib, ws=None, ws_bytes=0) == UNSUPPORTED_DEVICE
+
+
+def test_splitk_workspace_query(w8a8):
+    """The query is host-only arithmetic: slices * M * N * 4 bytes, or 0 where no split runs."""
+    lib = w8a8.lib()
+    q = lib.w8a8_gemm_splitk_workspace
+    assert lib.w8a8_debug_force_splitk(0) < 0 and lib.w8a8_debug_force_splitk(-2) < 0
+    try:
+        # forced slice counts, per-channel and per-group, capped at K / 128
+        assert lib.w8a8_debug_force_splitk(4) == OK
+        assert q(8, 0, F16, 128, 2560, 10240) == 4 * 128 * 2560 * 4
+        assert q(8, 128, BF16, 100, 2560, 10240) == 4 * 100 * 2560 * 4
+        assert q(4, 64, F32, 64, 512, 10240) == 4 * 64 * 512 * 4
+        assert lib.w8a8_debug_force_splitk(100) == OK
+        assert q(8, 0, F16, 128, 2560, 1024) == 8 * 128 * 2560 * 4
+        # never split: GEMV range, K not a whole number of 128-value tiles, int4 with I32 out
+        assert q(8, 0, F16, 16, 2560, 10240) == 0
+        assert q(8, 0, F16, 128, 2560, 10240 + 64) == 0
+        assert q(4, 128, I32, 128, 2560, 10240) == 0
+        assert q(8, 0, F16, 0, 2560, 10240) == 0
+        # a forced configuration without a split form runs the single pass
+        lib.w8a8_debug_force_config(13)
+        assert q(8, 0, F16, 128, 2560, 10240) == 0
+        lib.w8a8_debug_force_config(-1)
+        assert lib.w8a8_debug_force_splitk(1) == OK
+        assert q(8, 0, F16, 128, 2560, 10240) == 0
+        # automatic: a narrow-N long-K problem splits, a large square-ish one does not
+        assert lib.w8a8_debug_force_splitk(-1) == OK
+        n = q(8, 0, F16, 128, 2560, 10240)
+        assert n > 0 and n % (128 * 2560 * 4) == 0
+        assert q(8, 0, F16, 4096, 10240, 2560) == 0
+        # invalid shapes: -status
+        assert q(8, 0, F16, 128, 250, 10240) == -UNSUPPORTED_SHAPE
+        assert q(8, 32, F16, 128, 256, 1024) == -INVALID
+        assert q(8, 0, F16, -1, 256, 1024) == -INVALID
+    finally:
+        lib.w8a8_debug_force_config(-1)
+        lib.w8a8_debug_force_splitk(-1)

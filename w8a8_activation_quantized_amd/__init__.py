@@ -39,6 +39,10 @@ _SIGNATURES = {
     "w4a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w8a8_linear": ([_vp, _int, _i64, _vp, _vp, _int, _int, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp],
                     _int),
+    "w8a8_gemm_splitk_workspace": ([_int, _int, _int, _i64, _i64, _i64], _i64),
+    "w8a8_gemm_splitk": ([_vp, _vp, _vp, _vp, _int, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
+                         _int),
+    "w8a8_debug_force_splitk": ([_int], _int),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -90,6 +94,12 @@ def w8a8_debug_force_config(config_id: int) -> int:
     if n < 0:
         raise W8A8Error(-n, f"unknown config id {config_id}")
     return n
+
+
+def w8a8_debug_force_splitk(slices: int) -> None:
+    rc = _lib.w8a8_debug_force_splitk(slices)
+    if rc != 0:
+        raise W8A8Error(-rc, f"bad slice count {slices}")
 
 
 def quantize_per_token(x: torch.Tensor, x_q: torch.Tensor | None = None,
@@ -184,3 +194,26 @@ def w8a8_linear(x, w, s_w, weight_bits=8, group_size=0, out_dtype=torch.float16,
                             group_size, _ptr(x_q), _ptr(s_x), _ptr(y), _DTYPE_CODE[y.dtype], M, N, K,
                             y.stride(0), _stream(stream)))
     return y, x_q, s_x
+
+
+def w8a8_gemm_splitk_workspace(M, N, K, weight_bits=8, group_size=0, out_dtype=torch.float16) -> int:
+    """Workspace bytes w8a8_gemm_splitk uses for this problem (0: it runs the single pass)."""
+    n = _lib.w8a8_gemm_splitk_workspace(weight_bits, group_size, _DTYPE_CODE[out_dtype], M, N, K)
+    if n < 0:
+        raise W8A8Error(-n, _lib.w8a8_last_error().decode())
+    return n
+
+
+def w8a8_gemm_splitk(x_q, s_x, w, s_w, weight_bits=8, group_size=0, out_dtype=torch.float16, y=None,
+                     workspace=None, stream=None):
+    """The GEMM selected by (weight_bits, group_size) as in w8a8_linear, with K cut into slices
+    whose partial results go to `workspace` (a device tensor of at least
+    w8a8_gemm_splitk_workspace(...) bytes; None or smaller: the single-pass kernels)."""
+    M, K = x_q.shape
+    N = w.shape[0]
+    y = _out(y, M, N, out_dtype, x_q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.w8a8_gemm_splitk(_ptr(x_q), _ptr(s_x), _ptr(w), _ptr(s_w), weight_bits, group_size, _ptr(y),
+                                 _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _ptr(workspace), ws_bytes,
+                                 _stream(stream)))
+    return y

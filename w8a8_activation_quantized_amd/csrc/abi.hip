@@ -37,6 +37,7 @@ bool forced_unavailable() {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_force_cfg{-1};
+std::atomic<int> g_force_slices{-1};
 
 bool device_is_gfx950(int device) {
     if (device < 0 || device >= kMaxDevices) return false;
@@ -74,10 +75,9 @@ int launched(hipError_t e, const char *what) {
 
 bool valid_out(int d) { return d == W8A8_F16 || d == W8A8_BF16 || d == W8A8_F32 || d == W8A8_I32; }
 
-// Shared validation of the three GEMM entry points.
-int check_gemm(const char *fn, const void *x_q, const float *s_x, const void *w, const float *s_w,
-               int gs, const void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
-               bool per_group) {
+// Shape, dtype and stride checks shared by the GEMM entry points.
+int check_gemm_shape(const char *fn, int gs, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                     bool per_group) {
     if (M < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: M = %lld < 0", fn, (long long)M);
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || N * K > ((int64_t)1 << 40) ||
         M * K > ((int64_t)1 << 40))
@@ -99,6 +99,15 @@ int check_gemm(const char *fn, const void *x_q, const float *s_x, const void *w,
     if (ldy < N || ldy % 4 != 0)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldy = %lld must be >= N and a multiple of 4", fn,
                     (long long)ldy);
+    return W8A8_OK;
+}
+
+// Shared validation of the GEMM entry points.
+int check_gemm(const char *fn, const void *x_q, const float *s_x, const void *w, const float *s_w,
+               int gs, const void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+               bool per_group) {
+    const int rc = check_gemm_shape(fn, gs, y_dtype, M, N, K, ldy, per_group);
+    if (rc != W8A8_OK) return rc;
     if (M == 0) return W8A8_OK;
     if (!x_q || !s_x || !w || !s_w || !y) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
     if (!aligned16(x_q) || !aligned16(s_x) || !aligned16(w) || !aligned16(s_w) || !aligned16(y))
@@ -130,6 +139,8 @@ w8a8::GemmProblem make_problem(const int8_t *x_q, const float *s_x, const void *
     p.x_bf16 = 0;
     p.xq_out = nullptr;
     p.sx_out = nullptr;
+    p.ksplit = 1;
+    p.ws = nullptr;
     return p;
 }
 
@@ -252,6 +263,22 @@ int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, c
                     K, ldy, stream);
 }
 
+// Validation shared by the split-K query and call: weight_bits / group_size as for w8a8_linear.
+int check_split_kind(const char *fn, int weight_bits, int group_size) {
+    if (weight_bits != 8 && weight_bits != 4)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: weight_bits must be 8 or 4", fn);
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
+    if (weight_bits == 4 && group_size == 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
+    return W8A8_OK;
+}
+
+w8a8::SplitPlan current_split_plan(const w8a8::GemmProblem &p) {
+    return w8a8::splitk_plan(p, g_force_cfg.load(std::memory_order_relaxed),
+                             g_force_slices.load(std::memory_order_relaxed));
+}
+
 int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const float *s_w, int weight_bits,
                 int group_size, int8_t *x_q, float *s_x, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
                 int64_t ldy, void *stream) {
@@ -295,6 +322,51 @@ int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const fl
     hipError_t e = w8a8::launch_quantize_per_token(x, x_dtype == W8A8_BF16, ldx, (int)M, (int)K, x_q, s_x, st);
     if (e != hipSuccess) return launched(e, fn);
     return launched(w8a8::launch_gemm(p, force, st), fn);
+}
+
+int64_t w8a8_gemm_splitk_workspace(int weight_bits, int group_size, int y_dtype, int64_t M, int64_t N,
+                                   int64_t K) {
+    const char *fn = "w8a8_gemm_splitk_workspace";
+    int rc = check_split_kind(fn, weight_bits, group_size);
+    if (rc == W8A8_OK) rc = check_gemm_shape(fn, group_size, y_dtype, M, N, K, N, group_size != 0 || weight_bits == 4);
+    if (rc != W8A8_OK) return -(int64_t)rc;
+    ok();
+    if (M == 0) return 0;
+    const int wkind = weight_bits == 4 ? w8a8::W_INT4 : w8a8::W_INT8;
+    const w8a8::GemmProblem p = make_problem(nullptr, nullptr, nullptr, nullptr, group_size, wkind, nullptr, y_dtype,
+                                             M, N, K, N);
+    return w8a8::splitk_workspace_bytes(p, current_split_plan(p));
+}
+
+int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const float *s_w, int weight_bits,
+                     int group_size, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                     void *workspace, int64_t workspace_bytes, void *stream) {
+    const char *fn = "w8a8_gemm_splitk";
+    int rc = check_split_kind(fn, weight_bits, group_size);
+    if (rc != W8A8_OK) return rc;
+    rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0 || weight_bits == 4);
+    if (rc != W8A8_OK) return rc;
+    if (workspace_bytes < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace_bytes < 0", fn);
+    if (workspace && !aligned16(workspace))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    const int wkind = weight_bits == 4 ? w8a8::W_INT4 : w8a8::W_INT8;
+    w8a8::GemmProblem p = make_problem(x_q, s_x, w, s_w, group_size, wkind, y, y_dtype, M, N, K, ldy);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const w8a8::SplitPlan plan = current_split_plan(p);
+    const int64_t need = w8a8::splitk_workspace_bytes(p, plan);
+    if (plan.slices > 1 && workspace && workspace_bytes >= need) {
+        p.ws = workspace;
+        return launched(w8a8::launch_gemm_splitk(p, plan, st), fn);
+    }
+    return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed), st), fn);
+}
+
+int w8a8_debug_force_splitk(int slices) {
+    if (slices < -1 || slices == 0 || slices > 4096) return -W8A8_ERR_INVALID_ARGUMENT;
+    g_force_slices.store(slices, std::memory_order_relaxed);
+    return W8A8_OK;
 }
 
 }  // extern "C"

@@ -166,6 +166,25 @@ __device__ __forceinline__ void map_tile(const TileMap &t, int &tm, int &tn) {
     logical_tile(t, x * q + min(x, r) + i, tm, tn);
 }
 
+// Split-K: block -> (tile_m, tile_n, K-slice). The units are the tiles times the slices,
+// slice-major: the run of units that one XCD is given covers neighbouring tiles of one
+// slice, which share that slice's activation and weight panels in the XCD's L2.
+__device__ __forceinline__ void map_unit(const TileMap &t, int slices, int &tm, int &tn, int &ks) {
+    const int T = t.tiles_m * t.tiles_n, U = T * slices;
+    const int b = blockIdx.x;
+    const int x = b & 7, i = b >> 3;
+    const int q = U >> 3, r = U & 7;
+    const int L = x * q + min(x, r) + i;
+    ks = L / T;
+    logical_tile(t, L - ks * T, tm, tn);
+}
+
+// K-tiles [kt0, kt0 + KT) of slice ks: the KTT K-tiles dealt as evenly as whole tiles allow.
+__device__ __forceinline__ void slice_range(int KTT, int slices, int ks, int &kt0, int &KT) {
+    kt0 = ks * KTT / slices;
+    KT = (ks + 1) * KTT / slices - kt0;
+}
+
 // Compile-time shape of one kernel instantiation.
 template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int GS_, int WK_>
 struct Shape {
@@ -516,7 +535,9 @@ __device__ __forceinline__ void ms_mma(v4i (&acc)[S::FN][S::FM], const v4i (&a)[
         for (int fm = 0; fm < S::FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
 }
 
-template <int BN, int BM, int STAGES, int WGN, int WGM>
+// SPLIT: the workgroup runs one K-slice of its tile and stores the int32 sums of that slice
+// to p.ws (slice-major, [M, N] each); the dequantization happens after all slices.
+template <int BN, int BM, int STAGES, int WGN, int WGM, bool SPLIT>
 // Declared for 512 threads even when launched with 4 waves: at that bound the compiler
 // budgets 256 registers per wave and keeps the MFMA accumulators in arch VGPRs, each MFMA
 // accumulating in place. With a 256-thread bound it moves them to AGPRs without tying
@@ -526,13 +547,18 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
     constexpr int FM = S::FM, FN = S::FN, GPW = S::GPW;
     __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * S::STAGE];
 
-    int tm, tn;
-    map_tile(tmap, tm, tn);
+    int tm, tn, ks = 0;
+    if constexpr (SPLIT)
+        map_unit(tmap, p.ksplit, tm, tn, ks);
+    else
+        map_tile(tmap, tm, tn);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WGN, wm = wave / WGN;
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
+    int kt0 = 0, KT = K / S::BK;
+    if constexpr (SPLIT) slice_range(K / S::BK, p.ksplit, ks, kt0, KT);
 
     // Loader: wave w issues row groups g = w + j * NW of each stage (groups below BN / 8
     // are weight rows, the rest token rows); lane i covers row 8 g + i / 8 of the stage.
@@ -544,7 +570,7 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
         const int lrow = (is_w ? g : g - BN / 8) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((lrow >> 1) & 7);
         const int grow = is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
-        src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + 16 * c);
+        src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + kt0 * S::BK + 16 * c);
     }
 
     v4i acc[FN][FM];
@@ -554,7 +580,6 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
         for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     const int frow = lane & 15, fchunk = lane >> 4;
-    const int KT = K / S::BK;
     // prologue: stages 0 .. STAGES-2 in flight, wait for stage 0
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
@@ -589,6 +614,23 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
         }
         ms_mma<S>(acc, a1, b1);
         wait_lgkmcnt0();
+    }
+
+    if constexpr (SPLIT) {
+        int32_t *ws = static_cast<int32_t *>(p.ws) + (int64_t)ks * M * N;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + wm * S::WM + fm * 16 + frow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+                if (n >= N) continue;
+                const v4i v = acc[fn][fm];
+                *reinterpret_cast<int4 *>(ws + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        return;
     }
 
     // ---- epilogue (per-channel dequant or raw int32) ----
@@ -1027,21 +1069,27 @@ __device__ __forceinline__ void mg_scales(const int8_t *st, int gi, int wn, int 
     for (int fn = 0; fn < S::FN; ++fn) sw[fn] = *reinterpret_cast<const float4 *>(sc + wn * S::WN + fn * 16 + 4 * fchunk);
 }
 
-template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK>
+// SPLIT: one K-slice per workgroup; the slice's fold t (times 2^-4 for int4) goes to p.ws as
+// fp32, and the slices are added and scaled by s_x afterwards.
+template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK, bool SPLIT>
 __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tmap) {  // see gemm_ms_kernel
     using S = MgShape<BN, BM, STAGES, WGN, WGM, GS, WK>;
     constexpr int FM = S::FM, FN = S::FN;
     __shared__ __attribute__((aligned(1024))) int8_t smem[STAGES * S::STAGE];
 
-    int tm, tn;
-    map_tile(tmap, tm, tn);
+    int tm, tn, ks = 0;
+    if constexpr (SPLIT)
+        map_unit(tmap, p.ksplit, tm, tn, ks);
+    else
+        map_tile(tmap, tm, tn);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WGN, wm = wave / WGN;
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N;
     const int frow = lane & 15, fchunk = lane >> 4;
-    const int KT = p.K / S::BK;
+    int kt0 = 0, KT = p.K / S::BK;
+    if constexpr (SPLIT) slice_range(p.K / S::BK, p.ksplit, ks, kt0, KT);
     const int OPS = mg_ops_per_stage<S>(wave);
 
     v4i acc[FN][FM];
@@ -1057,7 +1105,7 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
     // prologue: stages 0 .. STAGES-2 in flight, wait for stage 0
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-        if (s < KT) mg_issue<S>(p, m0, n0, s, smem + s * S::STAGE, wave, lane);
+        if (s < KT) mg_issue<S>(p, m0, n0, kt0 + s, smem + s * S::STAGE, wave, lane);
     wait_vmcnt_rt(OPS * min(STAGES - 2, KT - 1));
     lds_barrier();
 
@@ -1071,7 +1119,7 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
         if (fill < KT) {
             int fb = cur + STAGES - 1;
             fb -= fb >= STAGES ? STAGES : 0;
-            mg_issue<S>(p, m0, n0, fill, smem + fb * S::STAGE, wave, lane);
+            mg_issue<S>(p, m0, n0, kt0 + fill, smem + fb * S::STAGE, wave, lane);
         }
         const int8_t *st = smem + cur * S::STAGE;
         // everything this wave still needs from stage kt is read before its barrier
@@ -1103,6 +1151,22 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
     // ---- epilogue: y = t * s_x[m] ----
     // int4: t holds 16 x the sum (the unpacked codes are 16 q); the scaling by 2^-4 is exact
     constexpr float TS = S::WK == W_INT4 ? 0.0625f : 1.0f;
+    if constexpr (SPLIT) {
+        float *ws = static_cast<float *>(p.ws) + (int64_t)ks * M * N;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + wm * S::WM + fm * 16 + frow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+                if (n >= N) continue;
+                const float4 v = t[fn][fm];
+                *reinterpret_cast<float4 *>(ws + (int64_t)m * N + n) = make_float4(v.x * TS, v.y * TS, v.z * TS, v.w * TS);
+            }
+        }
+        return;
+    }
     const float *__restrict__ sxp = p.sx;
     float sxm[FM];
 #pragma unroll
@@ -1908,6 +1972,68 @@ hipError_t linear_small_fq(const GemmProblem &p, hipStream_t stream) {
     return launch_gemv_dma_x<0, W_INT8, true, FQ>(p, stream);
 }
 
+// ---- split-K: the sum of the slices and the dequantization ---------------------------
+//
+// Thread i covers the outputs (m, n .. n + 3) with m N + n = 4 i. The slices are added in
+// slice order, up to eight loads in flight at a time. Per-channel (and I32 output): int32
+// sums, exact in any order, then the arithmetic of the single-pass epilogue, so the result is
+// bit-identical to the single-pass kernels. Per-group: the slices' fp32 folds are added,
+// then y = t * s_x[m].
+template <bool GROUPED>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(GemmProblem p) {
+    const int N = p.N, S = p.ksplit;
+    const int64_t quads = (int64_t)p.M * N / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (int64_t)gridDim.x * 256) {
+        const int m = (int)(4 * i / N), n = (int)(4 * i - (int64_t)m * N);
+        const int64_t off = (int64_t)m * p.ldy + n;
+        if constexpr (GROUPED) {
+            const float4 *ws = static_cast<const float4 *>(p.ws) + i;
+            float4 t = ws[0];
+            for (int s0 = 1; s0 < S; s0 += 8) {
+                float4 v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (s0 + j < S) v[j] = ws[(s0 + j) * quads];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (s0 + j < S) {
+                        t.x += v[j].x;
+                        t.y += v[j].y;
+                        t.z += v[j].z;
+                        t.w += v[j].w;
+                    }
+            }
+            const float sx = p.sx[m];
+            store4(p.y, off, p.out, t.x * sx, t.y * sx, t.z * sx, t.w * sx);
+        } else {
+            const int4 *ws = static_cast<const int4 *>(p.ws) + i;
+            int4 a = ws[0];
+            for (int s0 = 1; s0 < S; s0 += 8) {
+                int4 v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (s0 + j < S) v[j] = ws[(s0 + j) * quads];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (s0 + j < S) {
+                        a.x += v[j].x;
+                        a.y += v[j].y;
+                        a.z += v[j].z;
+                        a.w += v[j].w;
+                    }
+            }
+            if (p.out == OUT_I32) {
+                *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = a;
+            } else {
+                const float sx = p.sx[m];
+                const float4 sw = *reinterpret_cast<const float4 *>(p.sw + n);
+                store4(p.y, off, p.out, ((float)a.x * sx) * sw.x, ((float)a.y * sx) * sw.y, ((float)a.z * sx) * sw.z,
+                       ((float)a.w * sx) * sw.w);
+            }
+        }
+    }
+}
+
 // ---- configuration table ------------------------------------------------------------
 
 struct Config {
@@ -1930,6 +2056,7 @@ constexpr Config kConfigs[] = {
     {256, 128, 4},  // 11: per-group / W4A8 on the direct-to-LDS pipeline, BN=128 BM=256 (per-channel: 7)
     {64, 64, 4},    // 12: direct-to-LDS, BN=64 BM=64, 4 stages, 4 waves (32 n x 32 m each); small M
     {256, 320, 8},  // 13: direct-to-LDS, BN=320 BM=256, 4 stages of 64, two wave groups in alternation
+    {128, 128, 4},  // 14: direct-to-LDS, BN=128 BM=128, 4 stages, 4 waves (64 n x 64 m each)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1963,14 +2090,14 @@ hipError_t launch_grouped(const GemmProblem &p, int group_m, hipStream_t stream)
     return launch_cfg<BM, BN, WGM, WGN, 128, W_INT8>(p, group_m, stream);
 }
 
-template <int BN, int BM, int STAGES, int WGN, int WGM>
+template <int BN, int BM, int STAGES, int WGN, int WGM, bool SPLIT = false>
 hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
     TileMap t;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.group_m = group_m;
-    dim3 grid(t.tiles_m * t.tiles_n), block(64 * WGM * WGN);
-    hipLaunchKernelGGL((gemm_ms_kernel<BN, BM, STAGES, WGN, WGM>), grid, block, 0, stream, p, t);
+    dim3 grid(t.tiles_m * t.tiles_n * (SPLIT ? p.ksplit : 1)), block(64 * WGM * WGN);
+    hipLaunchKernelGGL((gemm_ms_kernel<BN, BM, STAGES, WGN, WGM, SPLIT>), grid, block, 0, stream, p, t);
     return hipGetLastError();
 }
 
@@ -1986,32 +2113,33 @@ hipError_t launch_pp(const GemmProblem &p, int group_m, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK>
+template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK, bool SPLIT>
 hipError_t launch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
     TileMap t;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.group_m = group_m;
-    dim3 grid(t.tiles_m * t.tiles_n), block(64 * WGM * WGN);
-    hipLaunchKernelGGL((gemm_mg_kernel<BN, BM, STAGES, WGN, WGM, GS, WK>), grid, block, 0, stream, p, t);
+    dim3 grid(t.tiles_m * t.tiles_n * (SPLIT ? p.ksplit : 1)), block(64 * WGM * WGN);
+    hipLaunchKernelGGL((gemm_mg_kernel<BN, BM, STAGES, WGN, WGM, GS, WK, SPLIT>), grid, block, 0, stream, p, t);
     return hipGetLastError();
 }
 
 // Per-group / W4A8 on the DMA pipeline: 128 x 256 tiles, or 64 x 64 for small M.
+template <bool SPLIT = false>
 hipError_t dispatch_mg(const GemmProblem &p, bool small, int group_m, hipStream_t stream) {
     if (small) {
         if (p.wkind == W_INT4)
-            return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT4>(p, group_m, stream)
-                              : launch_mg<64, 64, 4, 2, 2, 128, W_INT4>(p, group_m, stream);
-        return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT8>(p, group_m, stream)
-                          : launch_mg<64, 64, 4, 2, 2, 128, W_INT8>(p, group_m, stream);
+            return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT4, SPLIT>(p, group_m, stream)
+                              : launch_mg<64, 64, 4, 2, 2, 128, W_INT4, SPLIT>(p, group_m, stream);
+        return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT8, SPLIT>(p, group_m, stream)
+                          : launch_mg<64, 64, 4, 2, 2, 128, W_INT8, SPLIT>(p, group_m, stream);
     }
     if (p.wkind == W_INT4) {
-        if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT4>(p, group_m, stream);
-        return launch_mg<128, 256, 3, 2, 4, 128, W_INT4>(p, group_m, stream);
+        if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT4, SPLIT>(p, group_m, stream);
+        return launch_mg<128, 256, 3, 2, 4, 128, W_INT4, SPLIT>(p, group_m, stream);
     }
-    if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT8>(p, group_m, stream);
-    return launch_mg<128, 256, 3, 2, 4, 128, W_INT8>(p, group_m, stream);
+    if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT8, SPLIT>(p, group_m, stream);
+    return launch_mg<128, 256, 3, 2, 4, 128, W_INT8, SPLIT>(p, group_m, stream);
 }
 
 int choose_config(const GemmProblem &p) {
@@ -2021,12 +2149,13 @@ int choose_config(const GemmProblem &p) {
     const int64_t cus = num_cus();
     if (p.gs > 0 && p.out != OUT_I32) {
         // per-group: the 128 x 256 DMA kernel once it has enough tiles to spread over the
-        // chip (the group fold is VALU work it does not overlap); below that the
-        // register-staged 64 x 64 kernel, except int8 at M <= 128 (64 x 64 DMA tiles)
+        // chip (the group fold is VALU work it does not overlap), else 64 x 64 DMA tiles up
+        // to M = 512 (int8) / 1024 (int4), else the register-staged 64 x 64 kernel; without
+        // 128-value K-tiles the register-staged kernels
         if (!dma) return p.M <= 128 ? 4 : 0;
         const int64_t t11 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
-        if (t11 >= (p.wkind == W_INT4 ? cus : cus / 2)) return 11;
-        return p.wkind == W_INT8 && p.M <= 128 ? 12 : 4;
+        if (t11 >= cus / 2) return 11;
+        return p.M <= (p.wkind == W_INT4 ? 1024 : 512) ? 12 : 4;
     }
     if (!dma || p.wkind != W_INT8) return p.M <= 128 ? 4 : 1;
     // per-channel: among the DMA kernels, the fewest chip-wide rounds of tiles times tile
@@ -2046,9 +2175,119 @@ int choose_config(const GemmProblem &p) {
     return c6 <= c7 ? 6 : 7;
 }
 
+// Tile configurations with a split-K form: per-channel 7, 12, 14 (gemm_ms_kernel), per-group
+// 11 and 12 (gemm_mg_kernel).
+bool split_config(const GemmProblem &p, int cfg) {
+    if (p.gs > 0 && p.out != OUT_I32) return cfg == 11 || cfg == 12;
+    return p.wkind == W_INT8 && (cfg == 7 || cfg == 12 || cfg == 14);
+}
+
+// Time model of the slice kernels, fitted to launches on MI355X (N = 2560 .. 10240,
+// K = 2560 .. 12288, M = 32 .. 4096, every slice count up to 32; the chosen plan is within
+// 20 % of the fastest measured one on every shape). A launch is bound either by its rounds
+// of workgroups, each `fill_us + kt_us` per K-tile, or by the operand bytes all workgroups
+// fetch into LDS over `fetch_tbs`; a split adds the finish pass and the partial results'
+// traffic (written once, read once).
+struct SplitCost {
+    int bn, bm;
+    int per_cu;        // workgroups that fit one CU (LDS)
+    double fill_us;    // per workgroup: first stages' latency and the epilogue
+    double kt_us;      // per 128-value K-tile
+    double fetch_tbs;  // operand fetch rate of the whole chip, TB/s
+};
+
+SplitCost split_cost(const GemmProblem &p, int cfg) {
+    const bool grouped = p.gs > 0 && p.out != OUT_I32, w4 = grouped && p.wkind == W_INT4;
+    switch (cfg) {
+        case 7: return {128, 256, 1, 1.81, 0.732, 14.4};
+        case 14: return {128, 128, 1, 1.48, 0.565, 13.4};
+        case 11: return w4 ? SplitCost{128, 256, 1, 0.77, 1.795, 6.6} : SplitCost{128, 256, 1, 1.04, 1.652, 9.6};
+        default:
+            if (!grouped) return {64, 64, 2, 0.96, 0.315, 20.7};
+            return w4 ? SplitCost{64, 64, 2, 0.0, 0.685, 12.6} : SplitCost{64, 64, 2, 0.18, 0.798, 10.5};
+    }
+}
+
+double split_time(const GemmProblem &p, int cfg, int slices) {
+    const SplitCost c = split_cost(p, cfg);
+    const int64_t units = (int64_t)((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn) * slices;
+    const int64_t slots = (int64_t)num_cus() * c.per_cu;
+    const int kt = (p.K / 128 + slices - 1) / slices;
+    const double rounds = (double)((units + slots - 1) / slots) * (c.fill_us + c.kt_us * kt);
+    const double fetch = (double)units * kt * (c.bn + c.bm) * 128 / (c.fetch_tbs * 1e6);
+    double t = rounds > fetch ? rounds : fetch;
+    if (slices > 1) t += 7.5 + 2.0 * slices * p.M * p.N * 4 / 6.15e6;  // finish; partials at 6.15 TB/s
+    return t;
+}
+
 }  // namespace
 
 int gemm_num_configs() { return kNumConfigs; }
+
+SplitPlan splitk_plan(const GemmProblem &p, int force_cfg, int force_slices) {
+    const SplitPlan none{-1, 1};
+    // M <= 16 runs the weight-streaming GEMV, whose workgroups already cover the chip
+    if (p.M <= 16 || p.N < 16 || p.K % 128 != 0) return none;
+    const bool grouped = p.gs > 0 && p.out != OUT_I32;
+    if (!grouped && p.wkind != W_INT8) return none;
+    const int KTT = p.K / 128;
+    if (KTT < 2) return none;
+    if (force_cfg >= 0 && !split_config(p, force_cfg)) return none;
+    if (force_slices == 1) return none;
+    const int smax = force_slices > 1 ? min(force_slices, KTT) : min(KTT, 32);
+    const int smin = force_slices > 1 ? smax : 1;
+    static const int cands[] = {7, 12, 14, 11};
+    SplitPlan best = none;
+    double best_t = 0, single_t = 0;
+    for (int cfg : cands) {
+        if (!split_config(p, cfg) || (force_cfg >= 0 && cfg != force_cfg)) continue;
+        const double t1 = split_time(p, cfg, 1);
+        if (single_t == 0 || t1 < single_t) single_t = t1;
+        for (int sl = smin; sl <= smax; ++sl) {
+            const double t = split_time(p, cfg, sl);
+            if (best.cfg < 0 || t < best_t) {
+                best = {cfg, sl};
+                best_t = t;
+            }
+        }
+    }
+    if (best.cfg < 0 || best.slices == 1) return none;
+    // automatic: split only with a 10 % predicted gain over the best single pass modelled
+    // (the per-channel single pass may also take tiles outside the model, 320 x 256 or
+    // 160 x 256, which do better where the output has enough tiles)
+    if (force_slices < 0 && best_t >= 0.9 * single_t) return none;
+    return best;
+}
+
+int64_t splitk_workspace_bytes(const GemmProblem &p, const SplitPlan &plan) {
+    return plan.slices > 1 ? (int64_t)plan.slices * p.M * p.N * 4 : 0;
+}
+
+hipError_t launch_gemm_splitk(GemmProblem p, const SplitPlan &plan, hipStream_t stream) {
+    if (plan.slices < 2 || plan.slices > p.K / 128 || p.ws == nullptr || !split_config(p, plan.cfg))
+        return hipErrorInvalidValue;
+    p.ksplit = plan.slices;
+    const bool grouped = p.gs > 0 && p.out != OUT_I32;
+    const int gm = kConfigs[plan.cfg].group_m;
+    hipError_t e;
+    if (grouped) {
+        e = dispatch_mg<true>(p, plan.cfg == 12, gm, stream);
+    } else {
+        switch (plan.cfg) {
+            case 7: e = launch_ms<128, 256, 3, 2, 4, true>(p, gm, stream); break;
+            case 14: e = launch_ms<128, 128, 4, 2, 2, true>(p, gm, stream); break;
+            default: e = launch_ms<64, 64, 4, 2, 2, true>(p, gm, stream); break;
+        }
+    }
+    if (e != hipSuccess) return e;
+    const int64_t quads = (int64_t)p.M * p.N / 4;
+    const int blocks = (int)min((quads + 255) / 256, (int64_t)num_cus() * 8);
+    if (grouped)
+        hipLaunchKernelGGL(splitk_finish_kernel<true>, dim3(blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(splitk_finish_kernel<false>, dim3(blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream) {
     if (p.x == nullptr || p.M < 1 || p.M > 16 || p.out == OUT_I32) return hipErrorNotSupported;
@@ -2077,6 +2316,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 11: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
         case 12: return launch_ms<64, 64, 4, 2, 2>(p, gm, stream);
         case 13: return launch_pp<320, 256, 4>(p, gm, stream);
+        case 14: return launch_ms<128, 128, 4, 2, 2>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
         case 6: return launch_ms<160, 256, 3, 2, 4>(p, gm, stream);
         case 7: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);

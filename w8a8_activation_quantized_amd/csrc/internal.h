@@ -29,6 +29,11 @@ struct GemmProblem {
     int x_bf16;
     int8_t *xq_out;    // [M, K]
     float *sx_out;     // [M]
+    // split-K: K is cut into ksplit slices of whole 128-value K-tiles; slice s writes its
+    // partial result to ws + s * M * N ([M, N], row stride N: int32 sums for per-channel and
+    // I32 output, fp32 group folds for per-group); 1 and null for the single-pass kernels
+    int ksplit;
+    void *ws;
 };
 
 // Activation quantization (fp16 / bf16 rows -> int8 + fp32 scale).
@@ -47,5 +52,19 @@ hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream);
 
 // Number of GEMM tile configurations selectable via force_cfg.
 int gemm_num_configs();
+
+// Split-K, for problems whose output tiles are too few to occupy the chip (narrow N, long K).
+struct SplitPlan {
+    int cfg;     // tile configuration of the slice kernel
+    int slices;  // 1: no split (run launch_gemm)
+};
+// The plan for p (force_cfg / force_slices >= 0 override the automatic choice; a forced
+// plan that the problem cannot take gives slices = 1).
+SplitPlan splitk_plan(const GemmProblem &p, int force_cfg, int force_slices);
+// Workspace bytes of a plan: slices * M * N * 4 (0 when slices == 1).
+int64_t splitk_workspace_bytes(const GemmProblem &p, const SplitPlan &plan);
+// Runs the slices into p.ws, then one kernel that adds them in slice order and writes y.
+// Requires plan.slices > 1, p.ws with splitk_workspace_bytes(p, plan) bytes.
+hipError_t launch_gemm_splitk(GemmProblem p, const SplitPlan &plan, hipStream_t stream);
 
 }  // namespace w8a8
