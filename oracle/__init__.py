@@ -51,9 +51,10 @@ def _load():
         lib.oracle_group_acc.argtypes = [vp, vp, i64, i64, i64, i32, vp]
         lib.oracle_dequant_pc.argtypes = [vp, vp, vp, i64, i64, vp]
         lib.oracle_dequant_pg.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_mv.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, vp]
         for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
                   lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
-                  lib.oracle_dequant_pg):
+                  lib.oracle_dequant_pg, lib.oracle_mv):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -195,3 +196,25 @@ def linear_w4(x: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray, group_size: 
     """W4A8 per-group linear: unpack the int4 codes, then the per-group path."""
     K = x.shape[1]
     return linear_pg(x, unpack_int4(w_packed, K), s_w, group_size)
+
+
+def linear_mv(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int = 0, bf16: bool = False):
+    """Decode matrix-vector product without activation quantization: fp64
+    y[m, n] = sum_k x[m, k] * w_q[n, k] * s_w[n, k // group_size] (s_w[n] for group_size 0).
+
+    x: float16 [M, K], or (bf16=True) a uint16 array of bfloat16 bit patterns.
+    Returns dict with y and mag (the sum of the terms' magnitudes), both fp64 [M, N].
+    """
+    bits = np.ascontiguousarray(x.view(np.uint16) if x.dtype == np.float16 else x, dtype=np.uint16)
+    if x.dtype == np.float16 and bf16:
+        raise TypeError("bf16=True expects bfloat16 bit patterns (uint16), not float16")
+    w_q = np.ascontiguousarray(w_q, dtype=np.int8)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    M, K = bits.shape
+    N = w_q.shape[0]
+    assert w_q.shape[1] == K
+    y = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    _check(_load().oracle_mv(_p(bits), 1 if bf16 else 0, M, K, K, _p(w_q), _p(s_w), N, group_size, _p(y), _p(mag)),
+           "mv")
+    return {"y": y, "mag": mag}

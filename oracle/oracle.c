@@ -265,3 +265,39 @@ int oracle_dequant_pg(const int32_t *acc_g, const float *s_x, const float *s_w, 
         }
     return ORACLE_OK;
 }
+
+/*
+ * Decode matrix-vector product with the activations as they are [P5 "Metal Kernel 流水线",
+ * decode (M = 1): the int8 matrix-vector kernel dequantizes the weights as it goes and
+ * quantizes no activation; P2 "INT8 TensorOps 内核设计", the two paths: seq_len = 1 takes
+ * a dedicated int8 matrix-vector kernel]. x: M rows of K half (or bf16) values, row
+ * stride ldx elements; w_q int8 [N, K]; s_w fp32 [N] (group_size 0) or [N, K / group_size]:
+ *   y[m, n]   = sum_k x[m, k] * (w_q[n, k] * s_w[n, g(k)])           (fp64)
+ *   mag[m, n] = sum_k |x[m, k] * w_q[n, k] * s_w[n, g(k)]|
+ * with g(k) = k / group_size (0 for per-channel). Every term is exact in fp64 (a half has
+ * 11 significant bits, a code 8, a scale 24), so y is the exact value up to the rounding of
+ * the fp64 sum.
+ */
+int oracle_mv(const uint16_t *x, int x_is_bf16, int64_t M, int64_t K, int64_t ldx, const int8_t *w_q,
+              const float *s_w, int64_t N, int group_size, double *y, double *mag)
+{
+    if (M < 0 || N < 0 || K <= 0 || ldx < K || group_size < 0 || (group_size && K % group_size))
+        return ORACLE_BAD_ARG;
+    const int64_t G = group_size ? K / group_size : 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double t = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint16_t h = x[m * ldx + k];
+                const double xv = x_is_bf16 ? (double)bf16_to_float(h) : (double)half_to_float(h);
+                const double s = (double)s_w[group_size ? n * G + k / group_size : n];
+                const double term = xv * ((double)w_q[n * K + k] * s);
+                t += term;
+                a += fabs(term);
+            }
+            y[m * N + n] = t;
+            if (mag) mag[m * N + n] = a;
+        }
+    return ORACLE_OK;
+}

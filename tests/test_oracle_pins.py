@@ -311,3 +311,87 @@ def test_w4_path_equals_pg_on_unpacked_codes():
     r4 = oracle.linear_w4(x, packed, sw, 128)
     r8 = oracle.linear_pg(x, oracle.unpack_int4(packed, 256), sw, 128)
     assert (r4["acc"] == r8["acc"]).all() and (r4["y"] == r8["y"]).all()
+
+
+# ---- decode matrix-vector product without activation quantization (linear_mv) ----------
+# Plausible mistakes caught: a quantized activation slipping in (one-hot and exact
+# rational sums), a wrong group index for the weight scale (per-slice rational brute
+# force at gs 64 / 128 with distinct scales per group), transposed operands (non-square
+# shapes), a dropped scale (one-hot), the bf16 path reading the wrong half of the bits.
+
+def _mv_exact(x16, wq, sw, gs):
+    M, K = x16.shape
+    N = wq.shape[0]
+    y = np.zeros((M, N), dtype=object)
+    for m in range(M):
+        xs = [Fraction(float(v)) for v in x16[m].astype(np.float64)]
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                s = Fraction(float(sw[n] if gs == 0 else sw[n, k // gs]))
+                acc += xs[k] * int(wq[n, k]) * s
+            y[m, n] = acc
+    return y
+
+
+@pytest.mark.parametrize("gs", [0, 64, 128])
+def test_mv_exact_rational_brute_force(gs):
+    rng = np.random.default_rng(5 + gs)
+    M, N, K = 3, 5, 256
+    x = (rng.standard_normal((M, K)) * 3).astype(np.float16)
+    wq = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    sw = (rng.random(N if gs == 0 else (N, K // gs)) * 0.01 + 1e-3).astype(np.float32)
+    r = oracle.linear_mv(x, wq, sw, gs)
+    ex = _mv_exact(x, wq, sw, gs)
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(float(r["y"][m, n])) - ex[m, n]) <= abs(ex[m, n]) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+    # mag is the sum of |terms|: at least |y|, equal when all terms share a sign
+    assert (r["mag"] >= np.abs(r["y"]) * (1 - 1e-15)).all()
+
+
+def test_mv_one_hot_picks_dequantized_weight():
+    rng = np.random.default_rng(6)
+    N, K, gs = 16, 256, 64
+    wq = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    sw = (rng.random((N, K // gs)) + 0.5).astype(np.float32)
+    for j in (0, 63, 64, 200, 255):
+        x = np.zeros((1, K), np.float16)
+        x[0, j] = 2.0
+        y = oracle.linear_mv(x, wq, sw, gs)["y"][0]
+        assert (y == 2.0 * wq[:, j].astype(np.float64) * sw[:, j // gs].astype(np.float64)).all()
+
+
+def test_mv_equals_w8a8_on_exactly_quantizable_activations():
+    """x = c * 2^-e with integer |c| <= 127 and max |c| = 127 per row: per-token quantization
+    gives s_x = 2^-e and x_q = c exactly, so the W8A8 result and the matrix-vector result are
+    the same real number (and both are exact in fp64 here)."""
+    rng = np.random.default_rng(7)
+    M, N, K = 4, 24, 384
+    c = rng.integers(-127, 128, (M, K))
+    c[:, 5] = 127
+    x = (c * 2.0 ** -6).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq, sw = oracle.quantize_weight(W, 8, 0)
+    pc = oracle.linear_pc(x, wq, sw)
+    assert (pc["x_q"] == c).all() and (pc["s_x"] == np.float32(2.0 ** -6)).all()
+    assert (oracle.linear_mv(x, wq, sw, 0)["y"] == pc["y"]).all()
+    wq, sw = oracle.quantize_weight(W, 8, 128)
+    pg = oracle.linear_pg(x, wq, sw, 128)
+    assert np.allclose(oracle.linear_mv(x, wq, sw, 128)["y"], pg["y"], rtol=1e-13, atol=0)
+
+
+def test_mv_group_scales_equal_channel_scale_and_bf16_bits():
+    rng = np.random.default_rng(8)
+    M, N, K = 2, 16, 256
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    wq = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    s = (rng.random(N) + 0.1).astype(np.float32)
+    y0 = oracle.linear_mv(x, wq, s, 0)["y"]
+    assert (oracle.linear_mv(x, wq, np.repeat(s[:, None], K // 64, 1), 64)["y"] == y0).all()
+    # values exact in both formats (8 significant bits, normal range): same result from bf16 bits
+    xb = np.round(rng.standard_normal((M, K)) * 64).astype(np.float32) / 64
+    bits = (xb.view(np.uint32) >> 16).astype(np.uint16)
+    assert (bits.astype(np.uint32) << 16).view(np.float32).tolist() == xb.tolist()
+    assert (oracle.linear_mv(bits, wq, s, 0, bf16=True)["y"] ==
+            oracle.linear_mv(xb.astype(np.float16), wq, s, 0)["y"]).all()
