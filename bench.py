@@ -22,7 +22,7 @@ same graph runs up to 20 % slower per step (clocks still ramping), so a short ru
 that transient rather than the kernels.
 
 Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 1000] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1|m1w4] [--copy-ref-mb MB] [--no-graph]
+       [--workload pc|pg64|pg128|w4|m1|m1w4|qwen3|mv|mvg128] [--copy-ref-mb MB] [--no-graph]
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3"])
+    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3", "mv", "mvg128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle sample")
@@ -123,6 +123,60 @@ def cpu_baseline(x, W, bits, gs, budget_s):
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": f"first {rows_done} of {x.shape[0]} token rows (full N={N}, K={K}); "
                       f"per-token quantize + int GEMM + fp64 dequant; {dt:.2f} s"}
+
+
+def mv_decode(args, torch, w8a8, gs):
+    """The decode path without activation quantization (int8_mv) at M=1, N=10240, K=2560:
+    one step is one int8_mv call on fp16 activations, weights streamed from HBM (rotated over
+    copies larger than the Infinity Cache)."""
+    import oracle
+    from synth_inputs import linear_inputs
+
+    M, N, K = 1, 10240, 2560
+    x_np, W_np = linear_inputs(M, N, K, seed=0)
+    x = torch.from_numpy(x_np).cuda()
+    wq, sw = w8a8.quantize_weight(torch.from_numpy(W_np).cuda(), 8, gs)  # offline: not timed
+    wbytes = wq.numel()
+    copies = [wq] + [wq.clone() for _ in range((512 << 20) // wbytes)]
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def step(i):
+        w8a8.int8_mv(x, copies[i % len(copies)], sw, gs, y=y, stream=torch.cuda.current_stream())
+
+    for i in range(len(copies)):
+        step(i)
+    ms_per_step, event_ms = timed_steps(args, torch, step)
+    kernel_ms = event_ms if event_ms is not None else ms_per_step
+    ops = 2.0 * M * N * K
+    alg_bytes = wbytes + sw.numel() * 4 + M * K * 2 + M * N * 2  # weights + scales, x in, y out
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    result = {
+        "metric": f"decode matrix-vector (int8 weights x fp16 activations, no activation quantization), "
+                  f"M={M} N={N} K={K}",
+        "value": ops / (ms_per_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"int8_mv ({args.workload}): weights dequantized on the fly, fp32 products and sums",
+                   "M": M, "N": N, "K": K, "weight_bits": 8, "group_size": gs, "out": "fp16",
+                   "parallelism": "single GPU"},
+        "step_event_ms": event_ms, "weight_copies": len(copies),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
+                     "kernel": "int8_mv (mv_kernel)", "launch_ms": kernel_ms, "alg_bytes": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        oracle.build(force=False)
+        owq, osw = oracle.quantize_weight(W_np, 8, gs)
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < min(args.cpu_seconds, 2.0):
+            oracle.linear_mv(x_np, owq, osw, gs)
+            reps += 1
+        dt = time.perf_counter() - t0
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        result["cpu_baseline"] = {"value": reps * ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+                                  "sample": f"{reps} full calls (M=1, N={N}, K={K}); fp64 sum of x * q * s; "
+                                            f"{dt:.2f} s"}
+    return result
 
 
 def timed_steps(args, torch, step):
@@ -277,6 +331,9 @@ def main():
 
     if args.workload == "qwen3":
         print(json.dumps(qwen3_block(args, torch, w8a8)), flush=True)
+        return 0
+    if args.workload in ("mv", "mvg128"):
+        print(json.dumps(mv_decode(args, torch, w8a8, 0 if args.workload == "mv" else 128)), flush=True)
         return 0
 
     M, N, K, bits, gs = WORKLOADS[args.workload]

@@ -157,6 +157,26 @@ int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const fl
                 int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream);
 
 /*
+ * int8_mv -- the decode path without activation quantization (Cider README "Metal Kernel
+ * 流水线", decode: the int8 matrix-vector kernel dequantizes the weights on the fly; juejin
+ * post "INT8 TensorOps 内核设计": seq_len = 1 takes a dedicated matrix-vector kernel).
+ *   x    [M, K] fp16 or bf16 (x_dtype), row stride ldx elements, 1 <= M <= 16 (M = 0: no-op)
+ *   w_q  [N, K] int8, s_w [N] (group_size 0) or [N, K / group_size] (64 | 128), as
+ *        quantize_weight writes them with bits = 8
+ *   y    [M, N] of y_dtype (F16, BF16 or F32), row stride ldy elements:
+ *        y[m, n] = sum_k x[m, k] * (w_q[n, k] * s_w[n, k / group_size])
+ *   evaluated with fp32 products and sums (the codes are converted exactly to the
+ *   activation format; per channel the K-sum is scaled by s_w[n] at the end, per group each
+ *   group's sum is folded in fp32, groups ascending within a K-segment), then rounded once
+ *   to y_dtype. The fp32 sums follow no fixed order: results are within the fp32 evaluation
+ *   bound (K + 2) * 2^-24 * sum_k |terms| of the exact value, plus the output rounding.
+ * Constraints: N >= 16, N % 16 == 0, K >= 128, K % 128 == 0, ldx >= K, ldx % 8 == 0,
+ * ldy >= N, ldy % 4 == 0; inputs finite.
+ */
+int int8_mv(const void *x, int x_dtype, int64_t ldx, const int8_t *w_q, const float *s_w, int group_size,
+            void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream);
+
+/*
  * Split-K form of the three GEMM calls, for problems whose output has too few tiles to
  * occupy the chip (narrow N with long K at M in the hundreds or low thousands): K is cut
  * into slices of whole 128-value K-tiles that run side by side, each writing its partial

@@ -39,7 +39,7 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for required in ("quantize_per_token", "quantize_weight", "w8a8_gemm_pc", "w8a8_gemm_pg",
                      "w4a8_gemm_pg", "w8a8_linear", "w8a8_is_available", "w8a8_last_error",
-                     "w8a8_status_string"):
+                     "w8a8_status_string", "int8_mv", "w8a8_gemm_splitk", "w8a8_gemm_splitk_workspace"):
         assert required in names, names
 
 
@@ -233,3 +233,34 @@ def test_splitk_workspace_query(w8a8):
     finally:
         lib.w8a8_debug_force_config(-1)
         lib.w8a8_debug_force_splitk(-1)
+
+
+def _mv(lib, x=FAKE, x_dtype=F16, ldx=256, w=FAKE, gs=0, y_dtype=F16, M=1, N=256, K=256, ldy=256):
+    return lib.int8_mv(x, x_dtype, ldx, w, FAKE, gs, FAKE, y_dtype, M, N, K, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x_dtype=F32), INVALID, "x_dtype"),
+    (dict(gs=32), INVALID, "group_size"),
+    (dict(y_dtype=I32), INVALID, "y_dtype"),
+    (dict(M=-1), INVALID, "M"),
+    (dict(M=17), UNSUPPORTED_SHAPE, "M"),
+    (dict(N=250), UNSUPPORTED_SHAPE, "N"),
+    (dict(K=192, ldx=192), UNSUPPORTED_SHAPE, "K"),
+    (dict(ldx=200), INVALID, "ldx"),
+    (dict(ldx=260), INVALID, "ldx"),
+    (dict(ldy=250), INVALID, "ldy"),
+    (dict(x=None), INVALID, "null"),
+    (dict(w=None), INVALID, "null"),
+    (dict(x=ctypes.c_void_p(0x100008)), INVALID, "aligned"),
+])
+def test_mv_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _mv(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_mv_forced_unavailable(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert _mv(lib) == UNSUPPORTED_DEVICE
+    assert _mv(lib, M=0, x=None) == UNSUPPORTED_DEVICE

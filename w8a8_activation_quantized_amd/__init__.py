@@ -43,6 +43,7 @@ _SIGNATURES = {
     "w8a8_gemm_splitk": ([_vp, _vp, _vp, _vp, _int, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
                          _int),
     "w8a8_debug_force_splitk": ([_int], _int),
+    "int8_mv": ([_vp, _int, _i64, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -216,4 +217,20 @@ def w8a8_gemm_splitk(x_q, s_x, w, s_w, weight_bits=8, group_size=0, out_dtype=to
     _check(_lib.w8a8_gemm_splitk(_ptr(x_q), _ptr(s_x), _ptr(w), _ptr(s_w), weight_bits, group_size, _ptr(y),
                                  _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+    return y
+
+
+def int8_mv(x, w_q, s_w, group_size=0, out_dtype=torch.float16, y=None, stream=None):
+    """Decode path without activation quantization: y = x . (w_q * s_w)^T in fp32.
+
+    x [M, K] fp16/bf16 with 1 <= M <= 16; w_q int8 [N, K]; s_w [N] or [N, K/group_size]."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last dimension")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x must be float16 or bfloat16")
+    M, K = x.shape
+    N = w_q.shape[0]
+    y = _out(y, M, N, out_dtype, x.device)
+    _check(_lib.int8_mv(_ptr(x), _DTYPE_CODE[x.dtype], x.stride(0), _ptr(w_q), _ptr(s_w), group_size, _ptr(y),
+                        _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
     return y

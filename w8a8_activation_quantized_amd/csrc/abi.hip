@@ -324,6 +324,44 @@ int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const fl
     return launched(w8a8::launch_gemm(p, force, st), fn);
 }
 
+int int8_mv(const void *x, int x_dtype, int64_t ldx, const int8_t *w_q, const float *s_w, int group_size, void *y,
+            int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream) {
+    const char *fn = "int8_mv";
+    if (x_dtype != W8A8_F16 && x_dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: x_dtype must be F16 or BF16", fn);
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
+    if (y_dtype != W8A8_F16 && y_dtype != W8A8_BF16 && y_dtype != W8A8_F32)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: y_dtype must be F16, BF16 or F32", fn);
+    if (M < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: M = %lld < 0", fn, (long long)M);
+    if (M > 16) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: M = %lld > 16 (decode batches only)", fn, (long long)M);
+    if (N > INT32_MAX || K > INT32_MAX || N * K > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (N < 16 || N % 16 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: N = %lld must be a positive multiple of 16", fn, (long long)N);
+    if (K < 128 || K % 128 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 128", fn, (long long)K);
+    if (ldx < K || ldx % 8 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldx = %lld must be >= K and a multiple of 8", fn, (long long)ldx);
+    if (ldy < N || ldy % 4 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldy = %lld must be >= N and a multiple of 4", fn, (long long)ldy);
+    if (M > 0) {
+        if (!x || !w_q || !s_w || !y) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if (!aligned16(x) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y))
+            return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    }
+    int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    w8a8::GemmProblem p = make_problem(nullptr, nullptr, w_q, s_w, group_size, w8a8::W_INT8, y, y_dtype, M, N, K, ldy);
+    p.x = x;
+    p.ldx = ldx;
+    p.x_bf16 = x_dtype == W8A8_BF16 ? 1 : 0;
+    const hipError_t e = w8a8::launch_mv(p, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: shape does not fit the kernel's LDS plan", fn);
+    return launched(e, fn);
+}
+
 int64_t w8a8_gemm_splitk_workspace(int weight_bits, int group_size, int y_dtype, int64_t M, int64_t N,
                                    int64_t K) {
     const char *fn = "w8a8_gemm_splitk_workspace";

@@ -50,6 +50,11 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream);
 // launching when the shape does not fit it; the caller then quantizes and runs launch_gemm.
 hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream);
 
+// Decode matrix-vector product without activation quantization: y = x . (w_q * s_w)^T from
+// fp16 / bf16 x (p.x, p.ldx, p.x_bf16), int8 weights, per channel or per group (p.gs);
+// 1 <= M <= 16, K % 128 == 0. hipErrorNotSupported when the LDS plan does not fit.
+hipError_t launch_mv(const GemmProblem &p, hipStream_t stream);
+
 // Number of GEMM tile configurations selectable via force_cfg.
 int gemm_num_configs();
 
