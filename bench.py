@@ -26,8 +26,8 @@ Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 1000] [--no-cpu-basel
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
-counters measured on a plain copy of known size; it is reported only while the GEMM
-source still has the hash recorded there, else null.
+counters measured on a plain copy of known size; it is reported only while the kernel's
+source file (named in the summary) still has the hash recorded there, else null.
 """
 from __future__ import annotations
 
@@ -44,7 +44,6 @@ import numpy as np
 PEAK_INT8_TOPS = 5000.0  # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E, 8 TB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
-GEMM_SRC = os.path.join(ROOT, "w8a8_activation_quantized_amd", "csrc", "gemm.hip")
 
 # name -> (M, N, K, weight bits, group size)
 WORKLOADS = {
@@ -74,19 +73,21 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_sha():
-    with open(GEMM_SRC, "rb") as f:
+def source_sha(rel_path):
+    with open(os.path.join(ROOT, rel_path), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
 def measured_traffic(workload):
-    """HBM bytes per GEMM launch from the committed counter summary, if still current."""
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if the
+    kernel's source file still has the hash recorded there."""
     path = os.path.join(ROOT, "profiles", f"traffic_gemm_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     fields = dict(re.findall(r"^\s*-?\s*(\w+)\s*=\s*(\S+)\s*$", text, flags=re.M))
-    if fields.get("gemm_source_sha256") != gemm_source_sha():
+    src = fields.get("kernel_source")
+    if not src or not os.path.exists(os.path.join(ROOT, src)) or fields.get("kernel_source_sha256") != source_sha(src):
         return None
     try:
         return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])

@@ -159,6 +159,21 @@ int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w,
 
 }  // namespace
 
+namespace w8a8 {
+
+int num_cus() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cached.store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace w8a8
+
 extern "C" {
 
 int w8a8_is_available(int device) {

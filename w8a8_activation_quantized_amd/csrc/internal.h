@@ -55,6 +55,10 @@ hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream);
 // 1 <= M <= 16, K % 128 == 0. hipErrorNotSupported when the LDS plan does not fit.
 hipError_t launch_mv(const GemmProblem &p, hipStream_t stream);
 
+// Compute units of the current device (cached after the first call; 256 when no device
+// answers, which is the MI355X count).
+int num_cus();
+
 // Number of GEMM tile configurations selectable via force_cfg.
 int gemm_num_configs();
 
