@@ -52,9 +52,10 @@ def _load():
         lib.oracle_dequant_pc.argtypes = [vp, vp, vp, i64, i64, vp]
         lib.oracle_dequant_pg.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
         lib.oracle_mv.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, vp]
+        lib.oracle_quantize_weight_clipped.argtypes = [vp, i64, i64, i32, i32, ctypes.c_float, vp, vp]
         for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
                   lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
-                  lib.oracle_dequant_pg, lib.oracle_mv):
+                  lib.oracle_dequant_pg, lib.oracle_mv, lib.oracle_quantize_weight_clipped):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -112,6 +113,18 @@ def quantize_weight(W: np.ndarray, bits: int = 8, group_size: int = 0):
     sw = np.empty((N,) if group_size == 0 else (N, K // group_size), np.float32)
     _check(_load().oracle_quantize_weight(_p(W), N, K, bits, group_size, _p(wq), _p(sw)),
            "quantize_weight")
+    return wq, sw
+
+
+def quantize_weight_clipped(W: np.ndarray, bits: int, group_size: int, pct: float):
+    """quantize_weight with each run's scale taken from the pct-th percentile of |W| (linear
+    interpolation between order statistics) instead of the maximum; pct in (0, 100]."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    wq = np.empty((N, K) if bits == 8 else (N, K // 2), np.int8 if bits == 8 else np.uint8)
+    sw = np.empty((N,) if group_size == 0 else (N, K // group_size), np.float32)
+    _check(_load().oracle_quantize_weight_clipped(_p(W), N, K, bits, group_size, float(pct), _p(wq), _p(sw)),
+           "quantize_weight_clipped")
     return wq, sw
 
 

@@ -40,6 +40,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_OK 0
@@ -81,6 +82,8 @@ static float bf16_to_float(uint16_t b)
  *   q = clamp(rint(v / s), lo, hi)  (fp32 division, round half to even).
  * Returns s. A zero scale gives all-zero codes.
  */
+static float quantize_run_amax(const float *v, int64_t n, float a, float qdiv, int lo, int hi, int8_t *q);
+
 static float quantize_run(const float *v, int64_t n, float qdiv, int lo, int hi, int8_t *q)
 {
     float a = 0.0f;
@@ -88,6 +91,12 @@ static float quantize_run(const float *v, int64_t n, float qdiv, int lo, int hi,
         float m = fabsf(v[i]);
         if (m > a) a = m;
     }
+    return quantize_run_amax(v, n, a, qdiv, lo, hi, q);
+}
+
+/* The steps after the run's magnitude a: s = a / qdiv, q = clamp(rint(v / s), lo, hi). */
+static float quantize_run_amax(const float *v, int64_t n, float a, float qdiv, int lo, int hi, int8_t *q)
+{
     float s = a / qdiv;
     for (int64_t i = 0; i < n; ++i) {
         if (s == 0.0f) {
@@ -299,5 +308,62 @@ int oracle_mv(const uint16_t *x, int x_is_bf16, int64_t M, int64_t K, int64_t ld
             y[m * N + n] = t;
             if (mag) mag[m * N + n] = a;
         }
+    return ORACLE_OK;
+}
+
+/*
+ * Offline weight quantization with a clipped scale [P5 "说明": besides the default min-max
+ * scale, the scale can come from a percentile of the weights, clip_percentile]. For each run
+ * (row, or group of group_size along K) the magnitude a is the pct-th percentile of |v|
+ * instead of the maximum, read as the usual linear interpolation between order statistics:
+ * with u_0 <= ... <= u_{n-1} the sorted magnitudes, h = (pct * (n - 1)) / 100 in fp64,
+ * i = floor(h); a = u_{n-1} if i >= n - 1, else a = u_i + (h - i) * (u_{i+1} - u_i) in fp64,
+ * rounded once to fp32. Then the min-max steps with that a: s = a / qdiv, codes clamped, so
+ * weights beyond the percentile saturate. pct in (0, 100]; pct = 100 is min-max.
+ */
+static int cmp_float(const void *x, const void *y)
+{
+    float a = *(const float *)x, b = *(const float *)y;
+    return (a > b) - (a < b);
+}
+
+int oracle_quantize_weight_clipped(const float *W, int64_t N, int64_t K, int bits, int group_size, float pct,
+                                   void *w_q, float *s_w)
+{
+    if (N < 0 || K <= 0) return ORACLE_BAD_ARG;
+    if (bits != 8 && bits != 4) return ORACLE_BAD_ARG;
+    if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return ORACLE_BAD_ARG;
+    if (bits == 4 && (group_size == 0 || group_size % 2 != 0)) return ORACLE_BAD_ARG;
+    if (!(pct > 0.0f && pct <= 100.0f)) return ORACLE_BAD_ARG;
+    const int64_t run = group_size ? group_size : K;
+    const int64_t G = K / run;
+    const float qdiv = bits == 8 ? 127.0f : 7.0f;
+    const int lo = bits == 8 ? -128 : -8;
+    const int hi = bits == 8 ? 127 : 7;
+    const double h = ((double)pct * (double)(run - 1)) / 100.0;
+    const int64_t i = (int64_t)floor(h);
+    const double f = h - (double)i;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        int8_t codes[K];
+        float u[run];
+        for (int64_t g = 0; g < G; ++g) {
+            const float *v = W + n * K + g * run;
+            for (int64_t j = 0; j < run; ++j) u[j] = fabsf(v[j]);
+            qsort(u, (size_t)run, sizeof(float), cmp_float);
+            const float a = i >= run - 1 ? u[run - 1] : (float)((double)u[i] + f * ((double)u[i + 1] - (double)u[i]));
+            s_w[n * G + g] = quantize_run_amax(v, run, a, qdiv, lo, hi, codes + g * run);
+        }
+        if (bits == 8) {
+            memcpy((int8_t *)w_q + n * K, codes, (size_t)K);
+        } else {
+            uint8_t *dst = (uint8_t *)w_q + n * (K / 2);
+            for (int64_t j = 0; j < K / 2; ++j) {
+                unsigned lo_u = (unsigned)(codes[2 * j] + 8);
+                unsigned hi_u = (unsigned)(codes[2 * j + 1] + 8);
+                dst[j] = (uint8_t)(lo_u | (hi_u << 4));
+            }
+        }
+    }
     return ORACLE_OK;
 }

@@ -395,3 +395,50 @@ def test_mv_group_scales_equal_channel_scale_and_bf16_bits():
     assert (bits.astype(np.uint32) << 16).view(np.float32).tolist() == xb.tolist()
     assert (oracle.linear_mv(bits, wq, s, 0, bf16=True)["y"] ==
             oracle.linear_mv(xb.astype(np.float16), wq, s, 0)["y"]).all()
+
+
+# ---- clipped weight scales (quantize_weight_clipped) --------------------------------------
+# Mistakes caught: an off-by-one order statistic or a missing interpolation (closed forms at
+# integer and half positions), percentile applied to signed values instead of magnitudes
+# (random signs), percentile in percent vs fraction (numpy comparison), a clamp that does
+# not saturate the clipped tail, pct = 100 not reducing to min-max.
+
+@pytest.mark.parametrize("bits,gs", [(8, 0), (8, 64), (8, 128), (4, 64), (4, 128)])
+def test_clipped_at_100_is_min_max(bits, gs):
+    rng = np.random.default_rng(21 + gs + bits)
+    W = (rng.standard_normal((9, 256)) * 0.03).astype(np.float32)
+    a = oracle.quantize_weight(W, bits, gs)
+    b = oracle.quantize_weight_clipped(W, bits, gs, 100.0)
+    assert (a[0] == b[0]).all() and (a[1].view(np.uint32) == b[1].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("n,pct,pos", [(101, 99.0, 99.0), (101, 50.0, 50.0), (101, 1.0, 1.0), (11, 25.0, 2.5),
+                                       (11, 95.0, 9.5), (5, 100.0, 4.0), (5, 10.0, 0.4)])
+def test_clipped_closed_form(n, pct, pos):
+    """Magnitudes j * 2^-7 (j = 0 .. n-1, shuffled, random signs): the percentile is pos * 2^-7
+    (pos = pct (n - 1) / 100, exact here), s = that / 127, and every weight beyond it saturates."""
+    rng = np.random.default_rng(n * 7 + int(pct * 10))
+    mags = rng.permutation(np.arange(n)) * 2.0 ** -7
+    W = (mags * rng.choice([-1.0, 1.0], n)).astype(np.float32)[None, :]
+    wq, sw = oracle.quantize_weight_clipped(W, 8, 0, pct)
+    a = np.float32(pos * 2.0 ** -7)
+    assert sw[0] == a / np.float32(127.0)
+    big = np.abs(W[0]) >= a
+    assert (np.abs(wq[0][big].astype(int)) >= 127).all()  # saturated (+127, or -128 past -127.5)
+    assert (np.abs(wq[0]).astype(int) <= 128).all()
+
+
+def test_clipped_against_numpy_percentile():
+    rng = np.random.default_rng(33)
+    for n, gs in ((2560, 0), (128, 128), (64, 64)):
+        W = (rng.standard_normal((40, 2560 if gs == 0 else 1024)) * 0.02).astype(np.float32)
+        W[:, ::97] *= 30.0  # outliers
+        for pct in (99.9, 99.0, 50.0, 0.5):
+            _, sw = oracle.quantize_weight_clipped(W, 8, gs, pct)
+            runs = np.abs(W).reshape(W.shape[0], -1, n)
+            # the percentile travels as an fp32 argument: numpy gets the same value
+            p32 = float(np.float32(pct))
+            ref = (np.percentile(runs.astype(np.float64), p32, axis=2).astype(np.float32) / np.float32(127)).ravel()
+            got = sw.ravel()
+            ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+            assert ulps.max() <= 1 and (ulps == 0).mean() >= 0.95, (n, pct, ulps.max())
