@@ -96,6 +96,22 @@ int quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_si
                     float *s_w, void *stream);
 
 /*
+ * quantize_weight_clipped -- quantize_weight with a clipped scale (Cider README "说明": the
+ * scale comes from min-max by default, or from a percentile of the weights, clip_percentile).
+ * Per run (row for group_size 0, else group of group_size along K) the magnitude used in
+ * place of max|W| is the clip_percentile-th percentile of |W| over the run, with linear
+ * interpolation between order statistics: with u_0 <= ... <= u_{n-1} the sorted
+ * magnitudes, h = (clip_percentile * (n - 1)) / 100 and i = floor(h) in fp64,
+ *   a = u_{n-1} if i >= n - 1, else (float)(u_i + (h - i) * (u_{i+1} - u_i)) (fp64, one rounding)
+ * then s = a / 127 (int8) or a / 7 (int4) and the codes as quantize_weight computes them, so
+ * weights beyond the percentile saturate at the clamp. clip_percentile = 100 gives exactly
+ * quantize_weight's output.
+ * Constraints: those of quantize_weight, and 0 < clip_percentile <= 100.
+ */
+int quantize_weight_clipped(const float *W, int64_t N, int64_t K, int bits, int group_size,
+                            float clip_percentile, void *w_q, float *s_w, void *stream);
+
+/*
  * w8a8_gemm_pc -- int8 GEMM with per-channel dequant fused into the store
  * (juejin post, "W8A8 对称量化" and "INT8 TensorOps 内核设计"; README "量化":
  * C = C_int32 * s_act * s_weight).

@@ -264,3 +264,25 @@ def test_mv_forced_unavailable(w8a8, unavailable):
     lib = w8a8.lib()
     assert _mv(lib) == UNSUPPORTED_DEVICE
     assert _mv(lib, M=0, x=None) == UNSUPPORTED_DEVICE
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(pct=0.0), INVALID, "clip_percentile"),
+    (dict(pct=100.5), INVALID, "clip_percentile"),
+    (dict(pct=float("nan")), INVALID, "clip_percentile"),
+    (dict(bits=3), INVALID, "bits"),
+    (dict(bits=4, gs=0), INVALID, "int4"),
+    (dict(gs=32), INVALID, "group_size"),
+    (dict(K=200), UNSUPPORTED_SHAPE, "K"),
+    (dict(N=0), INVALID, "N"),
+])
+def test_quantize_weight_clipped_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    a = dict(N=16, K=256, bits=8, gs=0, pct=99.9)
+    a.update(kw)
+    assert lib.quantize_weight_clipped(FAKE, a["N"], a["K"], a["bits"], a["gs"], a["pct"], FAKE, FAKE, None) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_quantize_weight_clipped_forced_unavailable(w8a8, unavailable):
+    assert w8a8.lib().quantize_weight_clipped(FAKE, 16, 256, 8, 0, 99.0, FAKE, FAKE, None) == UNSUPPORTED_DEVICE

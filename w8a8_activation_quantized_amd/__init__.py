@@ -44,6 +44,7 @@ _SIGNATURES = {
                          _int),
     "w8a8_debug_force_splitk": ([_int], _int),
     "int8_mv": ([_vp, _int, _i64, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
+    "quantize_weight_clipped": ([_vp, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp, _vp], _int),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -132,6 +133,23 @@ def quantize_weight(W: torch.Tensor, bits: int = 8, group_size: int = 0, stream=
     s_w = torch.empty((N,) if group_size == 0 else (N, K // max(group_size, 1)), dtype=torch.float32,
                       device=W.device)
     _check(_lib.quantize_weight(_ptr(W), N, K, bits, group_size, _ptr(w_q), _ptr(s_w), _stream(stream)))
+    return w_q, s_w
+
+
+def quantize_weight_clipped(W: torch.Tensor, bits: int = 8, group_size: int = 0, clip_percentile: float = 99.9,
+                            stream=None):
+    """quantize_weight with each run's scale from the clip_percentile-th percentile of |W|."""
+    if W.dtype != torch.float32 or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous fp32 [N, K] tensor")
+    N, K = W.shape
+    if bits == 8:
+        w_q = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    else:
+        w_q = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    s_w = torch.empty((N,) if group_size == 0 else (N, K // max(group_size, 1)), dtype=torch.float32,
+                      device=W.device)
+    _check(_lib.quantize_weight_clipped(_ptr(W), N, K, bits, group_size, clip_percentile, _ptr(w_q), _ptr(s_w),
+                                        _stream(stream)))
     return w_q, s_w
 
 

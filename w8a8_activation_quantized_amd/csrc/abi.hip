@@ -255,6 +255,34 @@ int quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_si
                     fn);
 }
 
+int quantize_weight_clipped(const float *W, int64_t N, int64_t K, int bits, int group_size, float clip_percentile,
+                            void *w_q, float *s_w, void *stream) {
+    const char *fn = "quantize_weight_clipped";
+    if (!(clip_percentile > 0.0f && clip_percentile <= 100.0f))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: clip_percentile must be in (0, 100]", fn);
+    if (bits != 8 && bits != 4) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: bits must be 8 or 4", fn);
+    if (group_size != 0 && group_size != 64 && group_size != 128)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
+    if (bits == 4 && group_size == 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
+    if (N < 1) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: N = %lld < 1", fn, (long long)N);
+    if (K < 64 || K % 64 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 64", fn,
+                    (long long)K);
+    if (group_size && K % group_size != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K not a multiple of group_size", fn);
+    if (N > INT32_MAX || K > INT32_MAX || N * K > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (!W || !w_q || !s_w) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (!aligned16(W) || !aligned16(w_q) || !aligned16(s_w))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    return launched(w8a8::launch_quantize_weight_clipped(W, (int)N, (int)K, bits, group_size, clip_percentile, w_q,
+                                                         s_w, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int w8a8_gemm_pc(const int8_t *x_q, const float *s_x, const int8_t *w_q, const float *s_w, void *y,
                  int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream) {
     return run_gemm("w8a8_gemm_pc", x_q, s_x, w_q, s_w, 0, w8a8::W_INT8, y, y_dtype, M, N, K, ldy, stream);

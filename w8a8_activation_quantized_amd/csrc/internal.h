@@ -43,6 +43,10 @@ hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int 
 // Offline weight quantization.
 hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
                                   float *sw, hipStream_t stream);
+// quantize_weight with each run's magnitude from the pct-th percentile of |W| (pct in (0, 100];
+// 100 is the maximum, i.e. launch_quantize_weight).
+hipError_t launch_quantize_weight_clipped(const float *W, int N, int K, int bits, int gs, float pct, void *wq,
+                                          float *sw, hipStream_t stream);
 
 // GEMM + fused dequant. `force_cfg` < 0 lets the launcher choose by shape.
 hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream);

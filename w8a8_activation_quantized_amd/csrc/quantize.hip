@@ -15,6 +15,8 @@
 // CPL chunks per lane), so HBM sees exactly one read of x and one write of x_q.
 // The absmax works on the magnitude bit patterns (bits & 0x7fff), which order
 // like the magnitudes for finite fp16/bf16 values.
+#include <cmath>
+
 #include "act_quant.h"
 #include "internal.h"
 
@@ -114,11 +116,84 @@ hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, flo
 // Min-max symmetric (Cider README "说明"): s = max|W| / qdiv, q = clamp(rne(W / s)).
 // int4: s = max / 7, codes in [-8, 7] stored as u = q + 8, even k in the low nibble
 // (README "模式" / "量化").
-template <int BITS>
+//
+// Clipped scale (README "说明", clip_percentile): the run's magnitude is the percentile
+// u_i + f (u_{i+1} - u_i) of the sorted magnitudes u instead of the maximum, with i and f
+// from the host (the same for every run: i = floor(h), f = h - i, h = pct (n - 1) / 100 in
+// fp64), interpolated in fp64 and rounded once to fp32. u_i is found by radix selection on
+// the magnitudes' fp32 bit patterns (non-negative floats order like their bit patterns):
+// four passes over 8-bit digits, most significant first, each counting the run's values
+// that match the digits chosen so far into a 256-bin histogram of this wave in LDS.
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
+    return v;
+}
+
+// Bit pattern of the rank-k (0-based, ascending) magnitude of src[0, n). Every lane returns it.
+__device__ uint32_t run_select(const float *src, int n, uint32_t k, uint32_t *hist, int lane) {
+    uint32_t prefix = 0, mask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        // the wave's LDS operations run in issue order: the clears land before the counts
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0;
+        __builtin_amdgcn_wave_barrier();
+        for (int i = lane; i < n; i += 64) {
+            const uint32_t key = __float_as_uint(src[i]) & 0x7fffffffu;
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane l holds bins 4l .. 4l + 3; the lane whose bins hold rank k picks the digit
+        const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                       c3 = hist[4 * lane + 3];
+        const uint32_t own = c0 + c1 + c2 + c3;
+        uint32_t incl = own;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
+        }
+        const uint32_t excl = incl - own;
+        const bool mine = excl <= k && k < incl;
+        uint32_t below = excl;
+        int bin = 0;
+        if (mine) {
+            if (k < below + c0) {
+                bin = 0;
+            } else if (k < below + c0 + c1) {
+                bin = 1;
+                below += c0;
+            } else if (k < below + c0 + c1 + c2) {
+                bin = 2;
+                below += c0 + c1;
+            } else {
+                bin = 3;
+                below += c0 + c1 + c2;
+            }
+        }
+        const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+        const uint32_t digit = (uint32_t)__shfl(4 * lane + bin, owner, 64);
+        k -= (uint32_t)__shfl((int)below, owner, 64);
+        prefix |= digit << shift;
+        mask |= 0xffu << shift;
+        __builtin_amdgcn_wave_barrier();
+    }
+    return prefix;
+}
+
+template <int BITS, bool CLIP>
 __global__ __launch_bounds__(256) void quantize_weight_kernel(const float *__restrict__ W, int N,
                                                                int K, int run,
                                                                void *__restrict__ wq,
-                                                               float *__restrict__ sw) {
+                                                               float *__restrict__ sw, int sel_i,
+                                                               double sel_f) {
+    __shared__ uint32_t hist[CLIP ? 4 * 256 : 1];
     const int lane = threadIdx.x & 63;
     const int runs_per_row = K / run;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -128,8 +203,25 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const float *__res
     const float *src = W + n * K + (int64_t)g * run;
 
     float a = 0.f;
-    for (int i = lane; i < run; i += 64) a = fmaxf(a, fabsf(src[i]));
-    a = wave_max_f32(a);
+    if constexpr (CLIP) {
+        // u_i, then u_{i+1}: u_i again when more than i + 1 magnitudes are <= u_i, else the
+        // smallest magnitude above it
+        const uint32_t ui = run_select(src, run, (uint32_t)sel_i, hist + (threadIdx.x >> 6) * 256, lane);
+        uint32_t le = 0, above = 0xffffffffu;
+        for (int i = lane; i < run; i += 64) {
+            const uint32_t key = __float_as_uint(src[i]) & 0x7fffffffu;
+            le += key <= ui ? 1u : 0u;
+            if (key > ui) above = min(above, key);
+        }
+        le = wave_sum_u32(le);
+        above = wave_min_u32(above);
+        const uint32_t ui1 = le >= (uint32_t)sel_i + 2 ? ui : above;
+        const double d0 = (double)__uint_as_float(ui), d1 = (double)__uint_as_float(ui1);
+        a = (float)(d0 + sel_f * (d1 - d0));
+    } else {
+        for (int i = lane; i < run; i += 64) a = fmaxf(a, fabsf(src[i]));
+        a = wave_max_f32(a);
+    }
     const float qdiv = BITS == 8 ? 127.0f : 7.0f;
     const float s = a / qdiv;
     if (lane == 0) sw[r] = s;
@@ -157,13 +249,29 @@ hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int 
 
 hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
                                   float *sw, hipStream_t stream) {
+    return launch_quantize_weight_clipped(W, N, K, bits, gs, 100.0f, wq, sw, stream);
+}
+
+hipError_t launch_quantize_weight_clipped(const float *W, int N, int K, int bits, int gs, float pct, void *wq,
+                                          float *sw, hipStream_t stream) {
     const int run = gs ? gs : K;
     const int64_t runs = (int64_t)N * (K / run);
     dim3 grid((unsigned)((runs + 3) / 4)), block(256);
-    if (bits == 8)
-        hipLaunchKernelGGL(quantize_weight_kernel<8>, grid, block, 0, stream, W, N, K, run, wq, sw);
-    else
-        hipLaunchKernelGGL(quantize_weight_kernel<4>, grid, block, 0, stream, W, N, K, run, wq, sw);
+    // position of the percentile among the run's sorted magnitudes (the maximum at 100)
+    const double h = ((double)pct * (double)(run - 1)) / 100.0;
+    const int64_t i = (int64_t)floor(h);
+    const double f = h - (double)i;
+    if (i >= run - 1) {
+        if (bits == 8)
+            hipLaunchKernelGGL((quantize_weight_kernel<8, false>), grid, block, 0, stream, W, N, K, run, wq, sw, 0, 0.0);
+        else
+            hipLaunchKernelGGL((quantize_weight_kernel<4, false>), grid, block, 0, stream, W, N, K, run, wq, sw, 0, 0.0);
+    } else {
+        if (bits == 8)
+            hipLaunchKernelGGL((quantize_weight_kernel<8, true>), grid, block, 0, stream, W, N, K, run, wq, sw, (int)i, f);
+        else
+            hipLaunchKernelGGL((quantize_weight_kernel<4, true>), grid, block, 0, stream, W, N, K, run, wq, sw, (int)i, f);
+    }
     return hipGetLastError();
 }
 
