@@ -53,9 +53,11 @@ def _load():
         lib.oracle_dequant_pg.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
         lib.oracle_mv.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, vp]
         lib.oracle_quantize_weight_clipped.argtypes = [vp, i64, i64, i32, i32, ctypes.c_float, vp, vp]
+        lib.oracle_sdpa_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, ctypes.c_double, vp, vp, vp]
         for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
                   lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
-                  lib.oracle_dequant_pg, lib.oracle_mv, lib.oracle_quantize_weight_clipped):
+                  lib.oracle_dequant_pg, lib.oracle_mv, lib.oracle_quantize_weight_clipped,
+                  lib.oracle_sdpa_decode):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -231,3 +233,23 @@ def linear_mv(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int =
     _check(_load().oracle_mv(_p(bits), 1 if bf16 else 0, M, K, K, _p(w_q), _p(s_w), N, group_size, _p(y), _p(mag)),
            "mv")
     return {"y": y, "mag": mag}
+
+
+def sdpa_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, N: int = None, scale: float = None,
+                bf16: bool = False):
+    """Decode-step attention in fp64. q [B, Hq, D]; k, v [B, Hkv, Ncap, D] (first N rows used),
+    float16 arrays, or (bf16=True) uint16 bfloat16 bit patterns. scale defaults to 1/sqrt(D).
+    Returns dict with o [B, Hq, D], vmag [B, Hq, D] and smag [B, Hq] (fp64)."""
+    def bits(a):
+        return np.ascontiguousarray(a.view(np.uint16) if a.dtype == np.float16 else a, dtype=np.uint16)
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    B, Hq, D = qb.shape
+    _, Hkv, Ncap, _ = kb.shape
+    N = Ncap if N is None else N
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    o = np.empty((B, Hq, D), np.float64)
+    vmag = np.empty((B, Hq, D), np.float64)
+    smag = np.empty((B, Hq), np.float64)
+    _check(_load().oracle_sdpa_decode(_p(qb), _p(kb), _p(vb), 1 if bf16 else 0, B, Hq, Hkv, N, Ncap, D, float(scale),
+                                      _p(o), _p(vmag), _p(smag)), "sdpa_decode")
+    return {"o": o, "vmag": vmag, "smag": smag}

@@ -367,3 +367,59 @@ int oracle_quantize_weight_clipped(const float *W, int64_t N, int64_t K, int bit
     }
     return ORACLE_OK;
 }
+
+/*
+ * Decode-step attention [P5 "优化 SDPA（解码注意力）": one query token per head (Q_seq = 1),
+ * no mask, grouped-query heads sharing a KV head]. q [B, Hq, D]; k, v [B, Hkv, Ncap, D] of
+ * which the first N rows per head are used; half or bf16 bit patterns. Query head h reads KV
+ * head h / (Hq / Hkv). In fp64:
+ *   s_n = scale * sum_d q[d] k[n, d];  p_n = exp(s_n - max s);  o[d] = sum_n p_n v[n, d] / sum_n p_n
+ * Also returns per (b, h, d) vmag = sum_n p_n |v[n, d]| / sum_n p_n, and per (b, h)
+ * smag = max_n scale * sum_d |q[d] k[n, d]| (the sizes an fp32 evaluation's errors scale with).
+ */
+int oracle_sdpa_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, int is_bf16, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t N, int64_t Ncap, int64_t D, double scale, double *o, double *vmag,
+                       double *smag)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N <= 0 || Ncap < N || D <= 0) return ORACLE_BAD_ARG;
+    const int64_t G = Hq / Hkv;
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < B * Hq; ++bh) {
+        const int64_t b = bh / Hq, h = bh % Hq, kvh = h / G;
+        const uint16_t *qh = q + bh * D;
+        const uint16_t *kb = k + (b * Hkv + kvh) * Ncap * D;
+        const uint16_t *vb = v + (b * Hkv + kvh) * Ncap * D;
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        double mx = -INFINITY, sm = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double t = 0.0, a = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                const double qv = is_bf16 ? (double)bf16_to_float(qh[d]) : (double)half_to_float(qh[d]);
+                const double kv = is_bf16 ? (double)bf16_to_float(kb[n * D + d]) : (double)half_to_float(kb[n * D + d]);
+                t += qv * kv;
+                a += fabs(qv * kv);
+            }
+            s[n] = scale * t;
+            if (s[n] > mx) mx = s[n];
+            if (scale * a > sm) sm = scale * a;
+        }
+        double l = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            s[n] = exp(s[n] - mx);
+            l += s[n];
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0, am = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double vv = is_bf16 ? (double)bf16_to_float(vb[n * D + d]) : (double)half_to_float(vb[n * D + d]);
+                acc += s[n] * vv;
+                am += s[n] * fabs(vv);
+            }
+            o[bh * D + d] = acc / l;
+            if (vmag) vmag[bh * D + d] = am / l;
+        }
+        if (smag) smag[bh] = sm;
+        free(s);
+    }
+    return ORACLE_OK;
+}

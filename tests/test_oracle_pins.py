@@ -442,3 +442,73 @@ def test_clipped_against_numpy_percentile():
             got = sw.ravel()
             ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
             assert ulps.max() <= 1 and (ulps == 0).mean() >= 0.95, (n, pct, ulps.max())
+
+
+# ---- decode-step attention (sdpa_decode) --------------------------------------------------
+# Mistakes caught: a missing scale or max subtraction (scipy softmax comparison, large scores),
+# a wrong GQA head mapping (per-head comparison with repeated KV heads), rows past N read
+# (garbage in the unused cache rows), a transposed q . k (non-square D / N).
+
+def _sdpa_ref(q, k, v, N, scale):
+    from scipy.special import softmax
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    o = np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            kk = k[b, h // (Hq // Hkv), :N].astype(np.float64)
+            vv = v[b, h // (Hq // Hkv), :N].astype(np.float64)
+            p = softmax(scale * (kk @ q[b, h].astype(np.float64)))
+            o[b, h] = p @ vv
+    return o
+
+
+def test_sdpa_against_scipy_softmax_gqa_and_cache_rows():
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, D, N, Ncap = 2, 8, 2, 64, 37, 50
+    q = (rng.standard_normal((B, Hq, D)) * 2).astype(np.float16)
+    k = rng.standard_normal((B, Hkv, Ncap, D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, Ncap, D)).astype(np.float16)
+    k[:, :, N:] = np.float16(300.0)  # rows past N must not count
+    v[:, :, N:] = np.float16(-7.0)
+    r = oracle.sdpa_decode(q, k, v, N=N)
+    ref = _sdpa_ref(q, k, v, N, 1 / np.sqrt(D))
+    assert np.allclose(r["o"], ref, rtol=1e-12, atol=1e-13)
+    assert (r["vmag"] >= np.abs(r["o"]) - 1e-12).all()
+
+
+def test_sdpa_closed_forms():
+    rng = np.random.default_rng(42)
+    D = 128
+    v = rng.standard_normal((1, 1, 9, D)).astype(np.float16)
+    k = rng.standard_normal((1, 1, 9, D)).astype(np.float16)
+    q = rng.standard_normal((1, 4, D)).astype(np.float16)
+    # one key: the output is that value row
+    r = oracle.sdpa_decode(q, k, v, N=1)
+    assert (r["o"][0] == v[0, 0, 0].astype(np.float64)).all()
+    # q = 0 (all scores equal): the mean of the value rows
+    r = oracle.sdpa_decode(np.zeros_like(q), k, v)
+    assert np.allclose(r["o"][0], v[0, 0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-14)
+    # one score far above the rest (about 80 after the scale): that value row
+    kk = np.zeros_like(k)
+    kk[0, 0, 5, 0] = np.float16(30.0)
+    qq = np.zeros_like(q)
+    qq[0, :, 0] = np.float16(30.0)
+    r = oracle.sdpa_decode(qq, kk, v)
+    assert np.allclose(r["o"][0], v[0, 0, 5].astype(np.float64), rtol=0, atol=1e-30)
+
+
+def test_sdpa_gqa_equals_mha_with_repeated_heads_and_bf16():
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, D, N = 1, 8, 2, 64, 20
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    k = rng.standard_normal((B, Hkv, N, D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, N, D)).astype(np.float16)
+    gqa = oracle.sdpa_decode(q, k, v)["o"]
+    mha = oracle.sdpa_decode(q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1))["o"]
+    assert (gqa == mha).all()
+    # bf16 bit patterns of values exact in both formats give the fp16 result
+    r16 = [np.round(a.astype(np.float32) * 8) / 8 for a in (q, k, v)]
+    bits = [(a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16) for a in r16]
+    assert (oracle.sdpa_decode(*[a.astype(np.float16) for a in r16])["o"] ==
+            oracle.sdpa_decode(*bits, bf16=True)["o"]).all()
