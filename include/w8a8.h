@@ -227,6 +227,30 @@ int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const f
                      void *stream);
 
 /*
+ * sdpa_decode -- attention for one decode step (Cider README "优化 SDPA（解码注意力）": one
+ * query token per head, no mask; the query heads that share a KV head are served together so
+ * each K / V row is read once; long caches are split over workgroups and merged in a second
+ * pass, two-pass FlashDecoding).
+ *   q [B, Hq, D], k and v [B, Hkv, Ncap, D] of dtype (F16 or BF16), row-major; the first N
+ *   rows of each head's cache are used. Query head h reads KV head h / (Hq / Hkv).
+ *   o [B, Hq, D] of o_dtype (F16, BF16 or F32):
+ *     o[b, h, :] = sum_n p_n v[b, h / G, n, :],  p = softmax_n(scale * q[b, h, :] . k[b, h / G, n, :])
+ *   evaluated in fp32 (exact products on the matrix cores, fp32 sums, exp2 on pre-scaled
+ *   scores) and rounded once to o_dtype.
+ *   workspace / workspace_bytes: device memory for the per-slice partial results, at least
+ *   sdpa_decode_workspace(B, Hq, Hkv, N, D) bytes (0 means one pass suffices); NULL or less
+ *   runs a single slice per KV head (correct, slower for long caches). Caller-owned, 16-byte
+ *   aligned, contents unspecified on return; one per call in flight.
+ * Constraints: B >= 0 (0: no-op), Hq % Hkv == 0, Hq / Hkv <= 16, D in {64, 128},
+ * 1 <= N <= Ncap, 0 < scale < inf (usually 1 / sqrt(D)); inputs finite.
+ * sdpa_decode_workspace returns -status for invalid arguments.
+ */
+int64_t sdpa_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D);
+int sdpa_decode(const void *q, const void *k, const void *v, int dtype, void *o, int o_dtype, int64_t B,
+                int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap, int64_t D, float scale, void *workspace,
+                int64_t workspace_bytes, void *stream);
+
+/*
  * Debug knob: force the number of K-slices of w8a8_gemm_splitk (-1 = automatic, 1 = never
  * split, n >= 2: n slices, at most K / 128). Combined with w8a8_debug_force_config a
  * configuration with a split form (per-channel 7, 12, 14; per-group 11, 12) is used for the

@@ -286,3 +286,39 @@ def test_quantize_weight_clipped_validation(w8a8, kw, status, needle):
 
 def test_quantize_weight_clipped_forced_unavailable(w8a8, unavailable):
     assert w8a8.lib().quantize_weight_clipped(FAKE, 16, 256, 8, 0, 99.0, FAKE, FAKE, None) == UNSUPPORTED_DEVICE
+
+
+def _sdpa(lib, q=FAKE, dtype=F16, o_dtype=F16, B=1, Hq=8, Hkv=2, N=64, Ncap=64, D=128, scale=0.088, ws=None,
+          ws_bytes=0):
+    return lib.sdpa_decode(q, FAKE, FAKE, dtype, FAKE, o_dtype, B, Hq, Hkv, N, Ncap, D, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F32), INVALID, "dtype"),
+    (dict(o_dtype=I32), INVALID, "o_dtype"),
+    (dict(B=-1), INVALID, "B"),
+    (dict(Hq=6, Hkv=4), INVALID, "Hkv"),
+    (dict(Hq=34, Hkv=2), UNSUPPORTED_SHAPE, "16"),
+    (dict(D=96), UNSUPPORTED_SHAPE, "D"),
+    (dict(N=0), INVALID, "N"),
+    (dict(N=65, Ncap=64), INVALID, "N"),
+    (dict(scale=0.0), INVALID, "scale"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(q=None), INVALID, "null"),
+    (dict(ws_bytes=-1), INVALID, "workspace_bytes"),
+    (dict(ws=ctypes.c_void_p(0x100008), ws_bytes=4096), INVALID, "workspace"),
+])
+def test_sdpa_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _sdpa(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_sdpa_forced_unavailable_and_workspace_query(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert _sdpa(lib) == UNSUPPORTED_DEVICE
+    # the size query is host arithmetic: slices * B * Hq * (D + 4) * 4 bytes, 0 for one slice
+    assert lib.sdpa_decode_workspace(1, 32, 8, 64, 128) == 0
+    n = lib.sdpa_decode_workspace(1, 32, 4, 32768, 128)
+    assert n > 0 and n % (32 * 132 * 4) == 0
+    assert lib.sdpa_decode_workspace(1, 32, 3, 1024, 128) < 0

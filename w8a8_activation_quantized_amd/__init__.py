@@ -45,6 +45,9 @@ _SIGNATURES = {
     "w8a8_debug_force_splitk": ([_int], _int),
     "int8_mv": ([_vp, _int, _i64, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "quantize_weight_clipped": ([_vp, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp, _vp], _int),
+    "sdpa_decode_workspace": ([_i64, _i64, _i64, _i64, _i64], _i64),
+    "sdpa_decode": ([_vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _i64,
+                     _vp], _int),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -252,3 +255,31 @@ def int8_mv(x, w_q, s_w, group_size=0, out_dtype=torch.float16, y=None, stream=N
     _check(_lib.int8_mv(_ptr(x), _DTYPE_CODE[x.dtype], x.stride(0), _ptr(w_q), _ptr(s_w), group_size, _ptr(y),
                         _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
     return y
+
+
+def sdpa_decode_workspace(B, Hq, Hkv, N, D) -> int:
+    n = _lib.sdpa_decode_workspace(B, Hq, Hkv, N, D)
+    if n < 0:
+        raise W8A8Error(-n, _lib.w8a8_last_error().decode())
+    return n
+
+
+def sdpa_decode(q, k, v, N=None, scale=None, out_dtype=None, o=None, workspace=None, stream=None):
+    """Attention for one decode step: q [B, Hq, D]; k, v [B, Hkv, Ncap, D] (contiguous, fp16 or
+    bf16, first N rows used). Returns o [B, Hq, D]. workspace: a device tensor of at least
+    sdpa_decode_workspace(...) bytes for the split-KV pass (None: one slice per KV head)."""
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("q, k, v must be contiguous fp16 / bf16 tensors")
+    if not (q.dtype == k.dtype == v.dtype) or k.shape != v.shape or q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q [B, Hq, D] and k, v [B, Hkv, Ncap, D] of one dtype")
+    B, Hq, D = q.shape
+    _, Hkv, Ncap, _ = k.shape
+    N = Ncap if N is None else N
+    scale = 1.0 / (D ** 0.5) if scale is None else scale
+    if o is None:
+        o = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.sdpa_decode(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], _ptr(o), _DTYPE_CODE[o.dtype], B, Hq, Hkv,
+                            N, Ncap, D, scale, _ptr(workspace), ws_bytes, _stream(stream)))
+    return o

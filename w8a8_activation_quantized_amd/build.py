@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw8a8.so")
-SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "mv.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "mv.hip", "sdpa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -405,6 +405,59 @@ int int8_mv(const void *x, int x_dtype, int64_t ldx, const int8_t *w_q, const fl
     return launched(e, fn);
 }
 
+namespace {
+
+int check_sdpa(const char *fn, int dtype, int o_dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap,
+               int64_t D, float scale) {
+    if (dtype != W8A8_F16 && dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: dtype must be F16 or BF16", fn);
+    if (o_dtype != W8A8_F16 && o_dtype != W8A8_BF16 && o_dtype != W8A8_F32)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: o_dtype must be F16, BF16 or F32", fn);
+    if (B < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: B = %lld < 0", fn, (long long)B);
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: Hq must be a positive multiple of Hkv", fn);
+    if (Hq / Hkv > 16) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: Hq / Hkv = %lld > 16", fn, (long long)(Hq / Hkv));
+    if (D != 64 && D != 128) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: D = %lld must be 64 or 128", fn, (long long)D);
+    if (N < 1 || Ncap < N) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: need 1 <= N <= Ncap", fn);
+    if (!(scale > 0.0f) || !(scale < INFINITY))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: scale must be positive and finite", fn);
+    if (B > INT32_MAX || Hq > INT32_MAX || Ncap > INT32_MAX || B * Hkv * Ncap * D > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    return W8A8_OK;
+}
+
+}  // namespace
+
+int64_t sdpa_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D) {
+    const int rc = check_sdpa("sdpa_decode_workspace", W8A8_F16, W8A8_F16, B, Hq, Hkv, N, N, D, 1.0f);
+    if (rc != W8A8_OK) return -(int64_t)rc;
+    ok();
+    if (B == 0) return 0;
+    return w8a8::sdpa_workspace_bytes((int)B, (int)Hq, (int)Hkv, (int)N, (int)D);
+}
+
+int sdpa_decode(const void *q, const void *k, const void *v, int dtype, void *o, int o_dtype, int64_t B, int64_t Hq,
+                int64_t Hkv, int64_t N, int64_t Ncap, int64_t D, float scale, void *workspace, int64_t workspace_bytes,
+                void *stream) {
+    const char *fn = "sdpa_decode";
+    int rc = check_sdpa(fn, dtype, o_dtype, B, Hq, Hkv, N, Ncap, D, scale);
+    if (rc != W8A8_OK) return rc;
+    if (workspace_bytes < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace_bytes < 0", fn);
+    if (workspace && !aligned16(workspace))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+    if (B > 0) {
+        if (!q || !k || !v || !o) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+            return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    }
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    if (B == 0) return ok();
+    return launched(w8a8::launch_sdpa_decode(q, k, v, dtype == W8A8_BF16, o, o_dtype, (int)B, (int)Hq, (int)Hkv, (int)N,
+                                             (int)Ncap, (int)D, scale, workspace, workspace_bytes,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int64_t w8a8_gemm_splitk_workspace(int weight_bits, int group_size, int y_dtype, int64_t M, int64_t N,
                                    int64_t K) {
     const char *fn = "w8a8_gemm_splitk_workspace";

@@ -59,6 +59,16 @@ hipError_t launch_linear_small(const GemmProblem &p, hipStream_t stream);
 // 1 <= M <= 16, K % 128 == 0. hipErrorNotSupported when the LDS plan does not fit.
 hipError_t launch_mv(const GemmProblem &p, hipStream_t stream);
 
+// Decode-step attention (one query token per head, grouped KV heads). q [B, Hq, D]; k, v
+// [B, Hkv, Ncap, D] (first N rows used); fp16 or bf16; o [B, Hq, D] of out. Splits the keys
+// over sdpa_slices(...) workgroups per KV head when ws holds sdpa_workspace_bytes(...), else
+// runs one slice.
+int sdpa_slices(int B, int Hkv, int N);
+int64_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int N, int D);
+hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool bf16, void *o, int out, int B, int Hq,
+                              int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes,
+                              hipStream_t stream);
+
 // Compute units of the current device (cached after the first call; 256 when no device
 // answers, which is the MI355X count).
 int num_cus();
