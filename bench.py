@@ -22,7 +22,7 @@ same graph runs up to 20 % slower per step (clocks still ramping), so a short ru
 that transient rather than the kernels.
 
 Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 1000] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1|m1w4|qwen3|mv|mvg128] [--copy-ref-mb MB] [--no-graph]
+       [--workload pc|pg64|pg128|w4|m1|m1w4|qwen3|mv|mvg128|sdpa] [--copy-ref-mb MB] [--no-graph]
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3", "mv", "mvg128"])
+    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3", "mv", "mvg128", "sdpa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle sample")
@@ -176,6 +176,59 @@ def mv_decode(args, torch, w8a8, gs):
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         result["cpu_baseline"] = {"value": reps * ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
                                   "sample": f"{reps} full calls (M=1, N={N}, K={K}); fp64 sum of x * q * s; "
+                                            f"{dt:.2f} s"}
+    return result
+
+
+def sdpa_bench(args, torch, w8a8):
+    """Decode-step attention (sdpa_decode) for GQA8 (32 query heads over 4 KV heads), D = 128, a
+    32768-token fp16 cache, batch 1: one step is one call; the cache (67 MB) is read once per
+    step, so the roofline is HBM."""
+    import oracle
+
+    B, Hq, Hkv, N, D = 1, 32, 4, 32768, 128
+    rng = np.random.default_rng(0)
+    q = (rng.standard_normal((B, Hq, D)) * 1.5).astype(np.float16)
+    k = rng.standard_normal((B, Hkv, N, D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, N, D)).astype(np.float16)
+    qd, kd, vd = (torch.from_numpy(a).cuda() for a in (q, k, v))
+    ws = torch.empty(max(w8a8.sdpa_decode_workspace(B, Hq, Hkv, N, D), 16) // 4, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+
+    def step(i):
+        w8a8.sdpa_decode(qd, kd, vd, o=o, workspace=ws, stream=torch.cuda.current_stream())
+
+    ms_per_step, event_ms = timed_steps(args, torch, step)
+    kernel_ms = event_ms if event_ms is not None else ms_per_step
+    alg_bytes = 2 * B * Hkv * N * D * 2 + 2 * B * Hq * D * 2  # K and V once, q in, o out
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    result = {
+        "metric": f"decode attention (sdpa_decode), GQA {Hq}/{Hkv} heads, D={D}, N={N} fp16 cache, batch {B}",
+        "value": alg_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "sdpa_decode: one query token per head, grouped KV heads, split-KV + merge",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "in": "fp16", "out": "fp16",
+                   "parallelism": "single GPU"},
+        "step_event_ms": event_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
+                     "kernel": "sdpa_kernel + sdpa_combine_kernel", "launch_ms": kernel_ms, "alg_bytes": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        oracle.build(force=False)
+        heads, t0 = 0, time.perf_counter()
+        while heads < Hq and time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            # query heads of one KV head at a time (each reads that KV head's cache once)
+            g = Hq // Hkv
+            kv = heads // g
+            oracle.sdpa_decode(q[:, heads:heads + g], k[:, kv:kv + 1], v[:, kv:kv + 1])
+            heads += g
+        dt = time.perf_counter() - t0
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        done = alg_bytes * heads / Hq
+        result["cpu_baseline"] = {"value": done / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                                  "sample": f"{heads} of {Hq} query heads ({heads * Hkv // Hq} KV heads), fp64; "
                                             f"{dt:.2f} s"}
     return result
 
@@ -332,6 +385,9 @@ def main():
 
     if args.workload == "qwen3":
         print(json.dumps(qwen3_block(args, torch, w8a8)), flush=True)
+        return 0
+    if args.workload == "sdpa":
+        print(json.dumps(sdpa_bench(args, torch, w8a8)), flush=True)
         return 0
     if args.workload in ("mv", "mvg128"):
         print(json.dumps(mv_decode(args, torch, w8a8, 0 if args.workload == "mv" else 128)), flush=True)

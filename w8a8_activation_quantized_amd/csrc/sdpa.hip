@@ -62,17 +62,37 @@ struct SdpaArgs {
     float c;  // scale * log2(e)
 };
 
-// Workgroup (slice, b * Hkv + kvh). GMAX >= G bounds the per-lane accumulators.
-template <int D, int GMAX, bool BF16>
+// Workgroup (slice, b * Hkv + kvh): four waves, each a contiguous quarter of the slice's keys,
+// merged at the end.
+//
+// Per 32-key block of a wave: the K rows go straight from HBM into MFMA A operands (one block
+// ahead in registers); the V rows go to a per-wave LDS buffer by global_load_lds (one block
+// ahead, two buffers), 16-byte pieces of key row r at position piece ^ 2 ((r >> 3) & 3), so
+// that the transposed reads of the P . V operands (16 lanes: 16 consecutive d of one key; 4
+// lane groups: keys 8 apart) fall in different banks.
+//
+// P . V on the matrix cores: o^T tiles of 16 heads x 16 d, A = P [heads x 32 keys], B =
+// V [32 keys x 16 d] read transposed from LDS. P (fp32) is split into parts of the input
+// format whose sum is P to about fp32 precision (fp16: hi + lo; bf16: hi + mid + lo), each
+// part one MFMA; the products with V are exact and accumulate in fp32. The probabilities are
+// scaled by 2^12 (p = exp2(s - m + 12)) so the fp16 residual parts stay normal down to
+// p = 2^-15 of the block maximum; the scale cancels in o / l.
+template <int D, bool BF16>
 __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
-    constexpr int T = D / 32;          // MFMAs per 16-key tile
-    constexpr int LPR = D / 8;         // lanes per value row (8 d each)
-    constexpr int KG = 64 / LPR;       // key residue classes per wave
-    constexpr int KPL = SD_BK / KG;    // keys per lane per block
-    constexpr int GV = (GMAX + 3) / 4; // float4 reads per probability row
-    __shared__ __attribute__((aligned(16))) float p_lds[SD_WAVES][SD_BK][16];
-    __shared__ __attribute__((aligned(16))) float al_lds[SD_WAVES][16];
-    __shared__ __attribute__((aligned(16))) float red_o[SD_WAVES][GMAX][D];
+    constexpr int T = D / 32;              // QK MFMAs per 16-key tile
+    constexpr int DT = D / 16;             // P . V output tiles (16 d each)
+    constexpr int PARTS = BF16 ? 3 : 2;    // pieces of P in the input format
+    constexpr int VROW = 2 * D;            // bytes per V row
+    constexpr int VBUF = SD_BK * VROW;     // bytes per V block
+    constexpr int VDMA = VBUF / 1024;      // 1 KiB DMA instructions per V block
+    constexpr int RPD = 1024 / VROW;       // V rows per DMA instruction
+    constexpr int CPR = VROW / 16;         // 16-byte pieces per V row
+    constexpr int PBUF = PARTS * 16 * SD_BK * 2;  // P parts [part][head][key], 2 bytes each
+    static_assert(VBUF % 1024 == 0, "V block in whole DMA instructions");
+    // separate arrays, so that the compiler sees the DMA-written V buffers and the P tiles as
+    // distinct memory
+    __shared__ __attribute__((aligned(1024))) int8_t vlds[SD_WAVES * 2 * VBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t plds[SD_WAVES * PBUF / 2];
     __shared__ float red_ml[SD_WAVES][2][16];
 
     const int lane = threadIdx.x & 63;
@@ -80,16 +100,17 @@ __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
     const int slice = blockIdx.x, bk = blockIdx.y;
     const int b = bk / a.Hkv, kvh = bk % a.Hkv;
     const int G = a.G, N = a.N;
-    // keys of this slice, then of this wave
     const int s0 = (int)((int64_t)slice * N / a.slices), s1 = (int)((int64_t)(slice + 1) * N / a.slices);
     const int w0 = s0 + (int)((int64_t)wave * (s1 - s0) / SD_WAVES);
     const int w1 = s0 + (int)((int64_t)(wave + 1) * (s1 - s0) / SD_WAVES);
     const uint16_t *K = a.k + ((int64_t)b * a.Hkv + kvh) * a.Ncap * D;
     const uint16_t *V = a.v + ((int64_t)b * a.Hkv + kvh) * a.Ncap * D;
+    int8_t *vbuf = vlds + wave * 2 * VBUF;  // two V blocks
+    uint16_t *pbuf = plds + wave * PBUF / 2;
 
     // MFMA lane roles: row / column r16 = lane % 16, quarter q4 = lane / 16
     const int r16 = lane & 15, q4 = lane >> 4;
-    // q^T columns: head r16 of the group (zero past G), d in [32 t + 8 q4, + 8)
+    // q^T columns (QK B operand): head r16 of the group (zero past G), d in [32 t + 8 q4, + 8)
     v4u qf[T];
     {
         const uint16_t *qh = a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G + min(r16, G - 1)) * D;
@@ -99,30 +120,30 @@ __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
             qf[t] = r16 < G ? x : v4u{0, 0, 0, 0};
         }
     }
-    // value roles: 8 d starting at 8 dq, keys kq, kq + KG, ... of each block
-    const int dq = lane % LPR, kq = lane / LPR;
 
-    float m = -INFINITY, l = 0.f;  // of head r16 (copies in the 4 lanes of a column)
-    float o[GMAX][8];
+    float m = -INFINITY, l = 0.f;  // of head r16 (QK layout; copies in the 4 quarters)
+    sd_v4f o[DT];                  // o^T tiles: lane holds heads 4 q4 + e, d = 16 dt + r16
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+    for (int dt = 0; dt < DT; ++dt) o[dt] = sd_v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int n0 = w0; n0 < w1; n0 += SD_BK) {
-        // loads: K rows of both tiles (A operands) and this lane's V pieces
-        v4u kf[2][T], vf[KPL];
+    auto load_k = [&](int n0, v4u (&kf)[2][T]) __attribute__((always_inline)) {
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
             const int row = min(n0 + 16 * tile + r16, w1 - 1);
 #pragma unroll
             for (int t = 0; t < T; ++t) kf[tile][t] = *reinterpret_cast<const v4u *>(K + (int64_t)row * D + 32 * t + 8 * q4);
         }
+    };
+    auto load_v = [&](int n0, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            const int row = min(n0 + kq + KG * i, w1 - 1);
-            vf[i] = *reinterpret_cast<const v4u *>(V + (int64_t)row * D + 8 * dq);
+        for (int i = 0; i < VDMA; ++i) {
+            const int r = RPD * i + lane / CPR, pc = lane % CPR;
+            const int lc = pc ^ (2 * ((r >> 3) & 3));
+            const int row = min(n0 + r, w1 - 1);
+            dma_16B(V + (int64_t)row * D + 8 * lc, vbuf + buf * VBUF + i * 1024);
         }
+    };
+    auto block = [&](int n0, int buf, const v4u (&kf)[2][T]) __attribute__((always_inline)) {
         // scores: lane holds keys 16 tile + 4 q4 + e of head r16
         sd_v4f sc[2];
 #pragma unroll
@@ -150,77 +171,111 @@ __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            s[i] = __builtin_amdgcn_exp2f(s[i] - mn);
+            s[i] = __builtin_amdgcn_exp2f(s[i] - mn + 12.0f);  // 2^12 p
             ps += s[i];
         }
         ps += __shfl_xor(ps, 16, 64);
         ps += __shfl_xor(ps, 32, 64);
         l = l * alpha + ps;
         m = mn;
-        // probabilities and rescale factors to LDS: P[key][head]
+        // P parts to LDS, [part][head][key]: this lane's 4 consecutive keys of each tile
 #pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
+        for (int tile = 0; tile < 2; ++tile) {
+            uint32_t w[PARTS][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p_lds[wave][16 * tile + 4 * q4 + e][r16] = s[4 * tile + e];
-        if (q4 == 0) al_lds[wave][r16] = alpha;
-        __builtin_amdgcn_wave_barrier();
-        // (this wave's LDS writes and reads run in issue order)
-        float al[GMAX];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                float r0 = s[4 * tile + 2 * h2], r1 = s[4 * tile + 2 * h2 + 1];
 #pragma unroll
-        for (int j = 0; j < GV; ++j) {
-            const float4 x = *reinterpret_cast<const float4 *>(&al_lds[wave][4 * j]);
-            al[4 * j] = x.x;
-            if (4 * j + 1 < GMAX) al[4 * j + 1] = x.y;
-            if (4 * j + 2 < GMAX) al[4 * j + 2] = x.z;
-            if (4 * j + 3 < GMAX) al[4 * j + 3] = x.w;
-        }
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[g][j] *= al[g];
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            const int r = kq + KG * i;
-            float pr[GMAX];
-#pragma unroll
-            for (int j = 0; j < GV; ++j) {
-                const float4 x = *reinterpret_cast<const float4 *>(&p_lds[wave][r][4 * j]);
-                pr[4 * j] = x.x;
-                if (4 * j + 1 < GMAX) pr[4 * j + 1] = x.y;
-                if (4 * j + 2 < GMAX) pr[4 * j + 2] = x.z;
-                if (4 * j + 3 < GMAX) pr[4 * j + 3] = x.w;
-            }
-            float vv[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                vv[2 * j] = half_to_f32<BF16>(vf[i][j] & 0xffffu);
-                vv[2 * j + 1] = half_to_f32<BF16>(vf[i][j] >> 16);
+                for (int pt = 0; pt < PARTS; ++pt) {
+                    uint32_t b0, b1;
+                    if constexpr (BF16) {
+                        b0 = bf16_rne(r0);
+                        b1 = bf16_rne(r1);
+                        r0 -= __builtin_bit_cast(float, b0 << 16);
+                        r1 -= __builtin_bit_cast(float, b1 << 16);
+                    } else {
+                        b0 = f16_bits(r0);
+                        b1 = f16_bits(r1);
+                        r0 -= (float)__builtin_bit_cast(_Float16, (uint16_t)b0);
+                        r1 -= (float)__builtin_bit_cast(_Float16, (uint16_t)b1);
+                    }
+                    w[pt][h2] = b0 | (b1 << 16);
+                }
             }
 #pragma unroll
-            for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) o[g][j] = __builtin_fmaf(pr[g], vv[j], o[g][j]);
+            for (int pt = 0; pt < PARTS; ++pt)
+                *reinterpret_cast<uint2 *>(pbuf + (pt * 16 + r16) * SD_BK + 16 * tile + 4 * q4) =
+                    make_uint2(w[pt][0], w[pt][1]);
         }
-        __builtin_amdgcn_wave_barrier();
+        // rescale o: heads 4 q4 + e take alpha from lane 4 q4 + e (head r16 = that lane)
+        float al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * q4 + e, 64);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[dt][e] *= al[e];
+        // this block's V has landed (only the next block's K loads and V DMA may be in flight)
+        wait_lgkmcnt0();
+        // P A operands: head r16, keys 8 q4 .. 8 q4 + 8
+        v4u pa[PARTS];
+#pragma unroll
+        for (int pt = 0; pt < PARTS; ++pt) pa[pt] = *reinterpret_cast<const v4u *>(pbuf + (pt * 16 + r16) * SD_BK + 8 * q4);
+        const int8_t *vb = vbuf + buf * VBUF;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            // V^T B operand: d = 16 dt + r16, keys 8 q4 + j (2-byte reads, transposed)
+            const int d = 16 * dt + r16, lc = d >> 3, off = 2 * (d & 7);
+            uint32_t hv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 8 * q4 + j;
+                hv[j] = *reinterpret_cast<const uint16_t *>(vb + r * VROW + 16 * (lc ^ (2 * ((r >> 3) & 3))) + off);
+            }
+            const v4u vfrag = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+#pragma unroll
+            for (int pt = 0; pt < PARTS; ++pt) o[dt] = mfma_qk<BF16>(pa[pt], vfrag, o[dt]);
+        }
+    };
+
+    // pipeline: block j + 1's K loads and V DMA go out before block j computes
+    v4u ka[2][T], kb[2][T];
+    int nblk = (w1 - w0 + SD_BK - 1) / SD_BK;
+    if (nblk > 0) {
+        load_k(w0, ka);
+        load_v(w0, 0);
+    }
+    for (int j = 0; j < nblk; j += 2) {
+        const int n0 = w0 + j * SD_BK;
+        wait_lgkmcnt0();  // the other V buffer's reads (block j - 1) are done
+        if (j + 1 < nblk) {
+            load_k(n0 + SD_BK, kb);
+            load_v(n0 + SD_BK, 1);
+            wait_vmcnt<2 * T + VDMA>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        block(n0, 0, ka);
+        if (j + 1 >= nblk) break;
+        wait_lgkmcnt0();
+        if (j + 2 < nblk) {
+            load_k(n0 + 2 * SD_BK, ka);
+            load_v(n0 + 2 * SD_BK, 0);
+            wait_vmcnt<2 * T + VDMA>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        block(n0 + SD_BK, 1, kb);
     }
 
-    // the wave's key classes -> one sum per (head, d): butterfly over the lanes of a d range
+    // merge the waves: (m, l) per head and o^T tiles to LDS (the V buffers, now free)
+    __syncthreads();
+    float *red_o = reinterpret_cast<float *>(vlds);  // [wave][16 heads][D]
+    static_assert(SD_WAVES * 16 * D * 4 <= SD_WAVES * 2 * VBUF, "merge buffer");
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float x = o[g][j];
-#pragma unroll
-            for (int sh = LPR; sh < 64; sh <<= 1) x += __shfl_xor(x, sh, 64);
-            o[g][j] = x;
-        }
-    // merge the waves: wave w's (m, l, o) to LDS, then each thread combines one (head, d) set
-    if (kq == 0) {
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) red_o[wave][g][8 * dq + j] = o[g][j];
-    }
+        for (int e = 0; e < 4; ++e) red_o[(wave * 16 + 4 * q4 + e) * D + 16 * dt + r16] = o[dt][e];
     if (q4 == 0) {
         red_ml[wave][0][r16] = m;  // -inf for a wave without keys
         red_ml[wave][1][r16] = l;
@@ -237,7 +292,7 @@ __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
             const float mw = red_ml[w][0][g];
             const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
             L += red_ml[w][1][g] * f;
-            acc += red_o[w][g][d] * f;
+            acc += red_o[(w * 16 + g) * D + d] * f;
         }
         const int h = kvh * G + g;
         if (a.slices == 1) {
@@ -260,19 +315,43 @@ __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
     }
 }
 
-// Second pass: merge the slices of one (b, h), thread d.
+// Second pass: merge the slices of one (b, h). 256 threads: the slices' maxima and sums are
+// reduced across the block, then thread (d, part) adds the weighted sums of every fourth slice
+// (loads of different slices in flight together) and the four parts meet in LDS.
 template <int D>
-__global__ __launch_bounds__(D) void sdpa_combine_kernel(const float *part, void *o, int slices, int out) {
-    const int bh = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(256) void sdpa_combine_kernel(const float *part, void *o, int slices, int out) {
+    constexpr int PARTS = 256 / D;
+    __shared__ float red[256];
+    __shared__ float sum_o[PARTS][D];
+    const int bh = blockIdx.x, tid = threadIdx.x;
     const float *pp = part + (int64_t)bh * slices * (D + 4);
     float M = -INFINITY;
-    for (int s = 0; s < slices; ++s) M = fmaxf(M, pp[s * (D + 4)]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < slices; ++s) {
-        const float f = __builtin_amdgcn_exp2f(pp[s * (D + 4)] - M);
-        L += pp[s * (D + 4) + 1] * f;
-        acc += pp[s * (D + 4) + 4 + d] * f;
+    for (int s = tid; s < slices; s += 256) M = fmaxf(M, pp[s * (D + 4)]);
+    red[tid] = M;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
     }
+    M = red[0];
+    __syncthreads();
+    float L = 0.f;
+    for (int s = tid; s < slices; s += 256) L += pp[s * (D + 4) + 1] * __builtin_amdgcn_exp2f(pp[s * (D + 4)] - M);
+    red[tid] = L;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    L = red[0];
+    const int d = tid % D, pt = tid / D;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int s = pt; s < slices; s += PARTS) acc += pp[s * (D + 4) + 4 + d] * __builtin_amdgcn_exp2f(pp[s * (D + 4)] - M);
+    sum_o[pt][d] = acc;
+    __syncthreads();
+    if (pt != 0) return;
+    for (int q = 1; q < PARTS; ++q) acc += sum_o[q][d];
     const float y = acc / L;
     const int64_t off = (int64_t)bh * D + d;
     if (out == OUT_F32)
@@ -283,29 +362,23 @@ __global__ __launch_bounds__(D) void sdpa_combine_kernel(const float *part, void
         static_cast<uint16_t *>(o)[off] = (uint16_t)f16_bits(y);
 }
 
-template <int D, int GMAX, bool BF16>
+template <int D, bool BF16>
 hipError_t launch_sdpa_t(const SdpaArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((sdpa_kernel<D, GMAX, BF16>), dim3(a.slices, a.B * a.Hkv), dim3(64 * SD_WAVES), 0, stream, a);
+    hipLaunchKernelGGL((sdpa_kernel<D, BF16>), dim3(a.slices, a.B * a.Hkv), dim3(64 * SD_WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.slices == 1) return e;
-    hipLaunchKernelGGL((sdpa_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, stream, a.part, a.o, a.slices, a.out);
+    hipLaunchKernelGGL((sdpa_combine_kernel<D>), dim3(a.B * a.Hq), dim3(256), 0, stream, a.part, a.o, a.slices, a.out);
     return hipGetLastError();
-}
-
-template <int D, bool BF16>
-hipError_t launch_sdpa_d(const SdpaArgs &a, hipStream_t stream) {
-    if (a.G <= 4) return launch_sdpa_t<D, 4, BF16>(a, stream);
-    if (a.G <= 8) return launch_sdpa_t<D, 8, BF16>(a, stream);
-    return launch_sdpa_t<D, 16, BF16>(a, stream);
 }
 
 }  // namespace
 
 int sdpa_slices(int B, int Hkv, int N) {
-    // about two workgroups per CU, each slice at least 256 keys (two blocks per wave)
+    // about one workgroup per CU, each slice at least 128 keys (one block per wave); swept on
+    // the box over 8 .. 256 slices for 4, 8 and 32 KV heads at N = 4096 and 32768
     const int64_t groups = (int64_t)B * Hkv;
-    int s = (int)((2 * (int64_t)num_cus() + groups - 1) / groups);
-    s = std::min(s, std::max(1, N / 256));
+    int s = (int)(((int64_t)num_cus() + groups - 1) / groups);
+    s = std::min(s, std::max(1, N / 128));
     return std::max(1, std::min(s, 1024));
 }
 
@@ -333,8 +406,8 @@ hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool 
     a.slices = sdpa_slices(B, Hkv, N);
     if (a.slices > 1 && (ws == nullptr || ws_bytes < sdpa_workspace_bytes(B, Hq, Hkv, N, D))) a.slices = 1;
     a.part = static_cast<float *>(ws);
-    if (D == 64) return bf16 ? launch_sdpa_d<64, true>(a, stream) : launch_sdpa_d<64, false>(a, stream);
-    return bf16 ? launch_sdpa_d<128, true>(a, stream) : launch_sdpa_d<128, false>(a, stream);
+    if (D == 64) return bf16 ? launch_sdpa_t<64, true>(a, stream) : launch_sdpa_t<64, false>(a, stream);
+    return bf16 ? launch_sdpa_t<128, true>(a, stream) : launch_sdpa_t<128, false>(a, stream);
 }
 
 }  // namespace w8a8
