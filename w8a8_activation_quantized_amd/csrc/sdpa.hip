@@ -315,44 +315,63 @@ __global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
     }
 }
 
-// Second pass: merge the slices of one (b, h). 256 threads: the slices' maxima and sums are
-// reduced across the block, then thread (d, part) adds the weighted sums of every fourth slice
-// (loads of different slices in flight together) and the four parts meet in LDS.
+// Second pass: merge the slices of one (b, h). Thread (d, part) of 256 merges every PARTS-th
+// slice's (m, l, o[d]) into a running (M, L, A), eight slices at a time: their loads go out
+// together, then the running sums are rescaled once to the new maximum. The PARTS states then
+// meet in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void sdpa_combine_kernel(const float *part, void *o, int slices, int out) {
     constexpr int PARTS = 256 / D;
-    __shared__ float red[256];
-    __shared__ float sum_o[PARTS][D];
+    __shared__ float st[3][PARTS][D];
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const float *pp = part + (int64_t)bh * slices * (D + 4);
-    float M = -INFINITY;
-    for (int s = tid; s < slices; s += 256) M = fmaxf(M, pp[s * (D + 4)]);
-    red[tid] = M;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
-    M = red[0];
-    __syncthreads();
-    float L = 0.f;
-    for (int s = tid; s < slices; s += 256) L += pp[s * (D + 4) + 1] * __builtin_amdgcn_exp2f(pp[s * (D + 4)] - M);
-    red[tid] = L;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    L = red[0];
     const int d = tid % D, pt = tid / D;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int s = pt; s < slices; s += PARTS) acc += pp[s * (D + 4) + 4 + d] * __builtin_amdgcn_exp2f(pp[s * (D + 4)] - M);
-    sum_o[pt][d] = acc;
+    const float *pp = part + (int64_t)bh * slices * (D + 4);
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int s0 = pt; s0 < slices; s0 += 8 * PARTS) {
+        // eight slices' values, all loads issued before any is used (clamped addresses)
+        float ms[8], ls[8], os[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int sv = s0 + i * PARTS;
+            const bool ok = sv < slices;
+            const float *q = pp + (int64_t)(ok ? sv : pt) * (D + 4);
+            ms[i] = q[0];
+            ls[i] = q[1];
+            os[i] = q[4 + d];
+            if (!ok) ms[i] = -INFINITY;
+        }
+        float mx = M;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ms[i]);
+        // mx is finite: slice s0 exists
+        const float f = __builtin_amdgcn_exp2f(M - mx);  // 0 while M = -inf
+        L *= f;
+        A *= f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = __builtin_amdgcn_exp2f(ms[i] - mx);  // 0 for the missing slices
+            L += ls[i] * w;
+            A += os[i] * w;
+        }
+        M = mx;
+    }
+    st[0][pt][d] = M;
+    st[1][pt][d] = L;
+    st[2][pt][d] = A;
     __syncthreads();
     if (pt != 0) return;
-    for (int q = 1; q < PARTS; ++q) acc += sum_o[q][d];
-    const float y = acc / L;
+    float Mx = M;
+#pragma unroll
+    for (int q = 1; q < PARTS; ++q) Mx = fmaxf(Mx, st[0][q][d]);
+    float Lt = 0.f, At = 0.f;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) {
+        const float mq = st[0][q][d];
+        const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - Mx);
+        Lt += st[1][q][d] * f;
+        At += st[2][q][d] * f;
+    }
+    const float y = At / Lt;
     const int64_t off = (int64_t)bh * D + d;
     if (out == OUT_F32)
         static_cast<float *>(o)[off] = y;
