@@ -78,7 +78,7 @@ struct SdpaArgs {
 // scaled by 2^12 (p = exp2(s - m + 12)) so the fp16 residual parts stay normal down to
 // p = 2^-15 of the block maximum; the scale cancels in o / l.
 template <int D, bool BF16>
-__global__ __launch_bounds__(64 * SD_WAVES) void sdpa_kernel(SdpaArgs a) {
+__global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void sdpa_kernel(SdpaArgs a) {
     constexpr int T = D / 32;              // QK MFMAs per 16-key tile
     constexpr int DT = D / 16;             // P . V output tiles (16 d each)
     constexpr int PARTS = BF16 ? 3 : 2;    // pieces of P in the input format
