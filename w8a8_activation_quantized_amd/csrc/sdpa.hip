@@ -315,13 +315,16 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
     }
 }
 
-// Second pass: merge the slices of one (b, h). Thread (d, part) of 256 merges every PARTS-th
+constexpr int SD_COMBINE_THREADS = 1024;
+
+// Second pass: merge the slices of one (b, h). Thread (d, part) of 1024 merges every PARTS-th
 // slice's (m, l, o[d]) into a running (M, L, A), eight slices at a time: their loads go out
 // together, then the running sums are rescaled once to the new maximum. The PARTS states then
 // meet in LDS.
 template <int D>
-__global__ __launch_bounds__(256) void sdpa_combine_kernel(const float *part, void *o, int slices, int out) {
-    constexpr int PARTS = 256 / D;
+__global__ __launch_bounds__(SD_COMBINE_THREADS) void sdpa_combine_kernel(const float *part, void *o, int slices,
+                                                                          int out) {
+    constexpr int PARTS = SD_COMBINE_THREADS / D;
     __shared__ float st[3][PARTS][D];
     const int bh = blockIdx.x, tid = threadIdx.x;
     const int d = tid % D, pt = tid / D;
@@ -386,7 +389,8 @@ hipError_t launch_sdpa_t(const SdpaArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((sdpa_kernel<D, BF16>), dim3(a.slices, a.B * a.Hkv), dim3(64 * SD_WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.slices == 1) return e;
-    hipLaunchKernelGGL((sdpa_combine_kernel<D>), dim3(a.B * a.Hq), dim3(256), 0, stream, a.part, a.o, a.slices, a.out);
+    hipLaunchKernelGGL((sdpa_combine_kernel<D>), dim3(a.B * a.Hq), dim3(SD_COMBINE_THREADS), 0, stream, a.part, a.o,
+                       a.slices, a.out);
     return hipGetLastError();
 }
 
