@@ -11,13 +11,11 @@
 //  * Long caches are split over workgroups (two-pass FlashDecoding): each slice keeps its own
 //    running maximum, sum and weighted value sum, written to a caller-provided workspace and
 //    merged by a second kernel; with one slice the first kernel writes the output directly.
-//  * Scores on the matrix cores: S^T = K_block . q^T with v_mfma_f32_16x16x32_{f16,bf16}, the
-//    block's 16 keys as A rows and the (up to 16) query heads as B columns, so K rows are
-//    loaded straight from HBM into the A operand (16 bytes of one row per lane). Products are
-//    exact in fp32; scores, the softmax and every sum are fp32.
-//  * P . V on the vector units: V's contiguous dimension is d, not the summed key dimension
-//    the MFMA operands want, so each lane owns 8 consecutive d of one key residue class and
-//    accumulates all G heads; the probabilities pass through a small per-wave LDS tile.
+//  * Both products on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}): scores S^T =
+//    K_block . q^T with the block's 16 keys as A rows (K rows loaded straight from HBM into the
+//    operand) and the (up to 16) query heads as B columns; then o^T = P . V with V staged in
+//    LDS and read transposed, P split into input-format parts so that the result keeps fp32
+//    precision (see sdpa_kernel). Scores, the softmax and every sum are fp32.
 //  * Online softmax per 32-key block in base 2: scores are scaled by scale * log2(e) once,
 //    p = exp2(s - m), and the running sums are rescaled by exp2(m_old - m_new) per block.
 #include <algorithm>
@@ -36,16 +34,9 @@ typedef float sd_v4f __attribute__((ext_vector_type(4)));
 constexpr int SD_WAVES = 4;  // waves per workgroup
 constexpr int SD_BK = 32;    // keys per block (two MFMA row tiles)
 
+// v_mfma_f32_16x16x32 on 8 values of the input format per lane (both products use it)
 template <bool BF16>
-__device__ __forceinline__ float half_to_f32(uint32_t bits16) {
-    if constexpr (BF16)
-        return __builtin_bit_cast(float, bits16 << 16);
-    else
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-template <bool BF16>
-__device__ __forceinline__ sd_v4f mfma_qk(v4u a, v4u b, sd_v4f c) {
+__device__ __forceinline__ sd_v4f mma16x16x32(v4u a, v4u b, sd_v4f c) {
     if constexpr (BF16)
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sd_v8bf, a), __builtin_bit_cast(sd_v8bf, b), c, 0,
                                                        0, 0);
@@ -150,7 +141,7 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
         for (int tile = 0; tile < 2; ++tile) {
             sd_v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < T; ++t) acc = mfma_qk<BF16>(kf[tile][t], qf[t], acc);
+            for (int t = 0; t < T; ++t) acc = mma16x16x32<BF16>(kf[tile][t], qf[t], acc);
             sc[tile] = acc;
         }
         float s[8];
@@ -234,7 +225,7 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
             }
             const v4u vfrag = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
 #pragma unroll
-            for (int pt = 0; pt < PARTS; ++pt) o[dt] = mfma_qk<BF16>(pa[pt], vfrag, o[dt]);
+            for (int pt = 0; pt < PARTS; ++pt) o[dt] = mma16x16x32<BF16>(pa[pt], vfrag, o[dt]);
         }
     };
 
