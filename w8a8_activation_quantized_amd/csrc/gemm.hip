@@ -979,6 +979,29 @@ __device__ __forceinline__ void mg_fold(const v4i (&acc)[S::FN][S::FM], const fl
         }
 }
 
+// The fold of the group held in acc, interleaved with the MFMAs that open the next group:
+// per fragment, fold it (its MFMA was issued a full K-step earlier), then issue the MFMA
+// that overwrites it. A wave's VALU work then issues while its own MFMAs run.
+template <class S>
+__device__ __forceinline__ void mg_fold_mma(v4i (&acc)[S::FN][S::FM], const float4 (&sw)[S::FN],
+                                            float4 (&t)[S::FN][S::FM], const v4i (&a)[S::FN],
+                                            const v4i (&b)[S::FM]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < S::FM; ++fm) {
+            t[fn][fm].x = __builtin_fmaf((float)acc[fn][fm][0], sw[fn].x, t[fn][fm].x);
+            t[fn][fm].y = __builtin_fmaf((float)acc[fn][fm][1], sw[fn].y, t[fn][fm].y);
+            t[fn][fm].z = __builtin_fmaf((float)acc[fn][fm][2], sw[fn].z, t[fn][fm].z);
+            t[fn][fm].w = __builtin_fmaf((float)acc[fn][fm][3], sw[fn].w, t[fn][fm].w);
+            // the fold stays here (not sunk behind the MFMAs, which would keep both
+            // accumulator sets live)
+            asm volatile("" : "+v"(t[fn][fm].x), "+v"(t[fn][fm].y), "+v"(t[fn][fm].z), "+v"(t[fn][fm].w));
+            acc[fn][fm] = mfma_i8(a[fn], b[fm], v4i{0, 0, 0, 0});
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
 template <class S>
 __device__ __forceinline__ void mg_scales(const int8_t *st, int gi, int wn, int fchunk, float4 (&sw)[S::FN]) {
     const float *sc = reinterpret_cast<const float *>(st + S::W_TILE + S::X_TILE) + gi * S::BN;
@@ -1027,7 +1050,10 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
     lds_barrier();
 
     v4i a0[FN], b0[FM], a1[FN], b1[FM];
+    // scales of the group acc holds (zero before the first group, whose fold adds +0 to t = +0)
     float4 sw0[FN], sw1[FN];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) sw0[i] = sw1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     mg_frags<S>(smem, 0, wm, wn, frow, fchunk, a0, b0);
     wait_lgkmcnt0();
     int cur = 0;
@@ -1041,11 +1067,11 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
         const int8_t *st = smem + cur * S::STAGE;
         // everything this wave still needs from stage kt is read before its barrier
         mg_frags<S>(st, 1, wm, wn, frow, fchunk, a1, b1);
+        // K-step 0 opens group kt (gs 128) or 2 kt (gs 64) while the previous group is folded
+        mg_fold_mma<S>(acc, S::GPK == 2 ? sw1 : sw0, t, a0, b0);
         mg_scales<S>(st, 0, wn, fchunk, sw0);
         if constexpr (S::GPK == 2) mg_scales<S>(st, 1, wn, fchunk, sw1);
-        mg_mma<S, true>(acc, a0, b0);  // K-step 0 opens group kt (or 2 kt)
         wait_lgkmcnt0();
-        if constexpr (S::GPK == 2) mg_fold<S>(acc, sw0, t);
         if (kt + 1 < KT) {
             wait_vmcnt_rt(OPS * min(STAGES - 2, KT - 2 - kt));
             lds_barrier();
@@ -1055,15 +1081,13 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
             cur = nb;
         }
         if constexpr (S::GPK == 2) {
-            mg_mma<S, true>(acc, a1, b1);  // K-step 1 is group 2 kt + 1
-            wait_lgkmcnt0();
-            mg_fold<S>(acc, sw1, t);
+            mg_fold_mma<S>(acc, sw0, t, a1, b1);  // K-step 1 is group 2 kt + 1; group 2 kt folds
         } else {
             mg_mma<S, false>(acc, a1, b1);  // K-step 1 closes group kt
-            wait_lgkmcnt0();
-            mg_fold<S>(acc, sw0, t);
         }
+        wait_lgkmcnt0();
     }
+    mg_fold<S>(acc, S::GPK == 2 ? sw1 : sw0, t);  // the last group
 
     // ---- epilogue: y = t * s_x[m] ----
     // int4: t holds 16 x the sum (the unpacked codes are 16 q); the scaling by 2^-4 is exact
