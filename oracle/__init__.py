@@ -54,10 +54,11 @@ def _load():
         lib.oracle_mv.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, vp]
         lib.oracle_quantize_weight_clipped.argtypes = [vp, i64, i64, i32, i32, ctypes.c_float, vp, vp]
         lib.oracle_sdpa_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, ctypes.c_double, vp, vp, vp]
+        lib.oracle_rmsnorm_quantize.argtypes = [vp, i32, vp, i32, ctypes.c_double, i64, i64, i64, vp, vp, vp]
         for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
                   lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
                   lib.oracle_dequant_pg, lib.oracle_mv, lib.oracle_quantize_weight_clipped,
-                  lib.oracle_sdpa_decode):
+                  lib.oracle_sdpa_decode, lib.oracle_rmsnorm_quantize):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -101,6 +102,26 @@ def _qpt(bits: np.ndarray, is_bf16: int):
     _check(_load().oracle_quantize_per_token(_p(bits), is_bf16, M, K, K, _p(xq), _p(sx)),
            "quantize_per_token")
     return xq, sx
+
+
+def rmsnorm_quantize(x: np.ndarray, g: np.ndarray, eps: float, x_bf16: bool = False, g_bf16: bool = False):
+    """RMSNorm with the per-token quantization folded in (oracle.c cites the passages).
+
+    x [M, K] and g [K]: float16 arrays, or uint16 arrays of bfloat16 bit patterns with the
+    matching flag set. Returns (x_q int8 [M, K], s_u float32 [M], s_x float64 [M]): x_q and
+    s_u are the symmetric quantization of u = x * g (one fp32 multiply per element), and
+    s_x = s_u / sqrt(mean(x^2) + eps), so s_x * x_q approximates the normalized row.
+    """
+    xb = np.ascontiguousarray(x).view(np.uint16)
+    gb = np.ascontiguousarray(g).view(np.uint16)
+    M, K = xb.shape
+    assert gb.shape == (K,)
+    xq = np.empty((M, K), np.int8)
+    su = np.empty((M,), np.float32)
+    sx = np.empty((M,), np.float64)
+    _check(_load().oracle_rmsnorm_quantize(_p(xb), int(x_bf16), _p(gb), int(g_bf16), float(eps), M, K, K,
+                                           _p(xq), _p(su), _p(sx)), "rmsnorm_quantize")
+    return xq, su, sx
 
 
 def quantize_weight(W: np.ndarray, bits: int = 8, group_size: int = 0):

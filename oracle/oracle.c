@@ -423,3 +423,44 @@ int oracle_sdpa_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
     }
     return ORACLE_OK;
 }
+
+/*
+ * RMSNorm with the per-token quantization folded in: the producer of a linear layer's
+ * input emits int8 codes and a per-token scale instead of a normalized half row, so the
+ * activation quantization needs no pass of its own [P5 "Metal Kernel 流水线": the layer
+ * runs quantize_per_token, then the GEMM, as two dispatches; P2 "W8A8 对称量化": the online
+ * quantization must not become the new bottleneck]. The pages name no producer; the one
+ * taken is RMSNorm with a per-channel weight g, the norm in front of the q/k/v and
+ * gate/up linears of a Qwen3 block:
+ *     n[k] = x[k] * g[k] / sqrt(mean_k x[k]^2 + eps).
+ * The row factor 1 / sqrt(...) is positive and common to the row, so it cancels in
+ * n[k] / (max_k |n[k]| / 127) and moves into the scale:
+ *     u[k]  = x[k] * g[k]                 (one fp32 multiply)
+ *     x_q, s_u = the symmetric quantization of the run u (as quantize_per_token)
+ *     r     = 1 / sqrt(sum_k x[k]^2 / K + eps)   (fp64; every square is exact in fp64)
+ *     s_x   = s_u * r                     (fp64, returned for the caller's tolerance)
+ * so s_x * x_q[k] approximates n[k] within half a quantization step. x and g: half or bf16
+ * bit patterns; x rows of stride ldx elements; outputs x_q [M, K], s_u [M] (fp32) and
+ * s_x [M] (fp64).
+ */
+int oracle_rmsnorm_quantize(const uint16_t *x, int x_is_bf16, const uint16_t *g, int g_is_bf16, double eps,
+                            int64_t M, int64_t K, int64_t ldx, int8_t *x_q, float *s_u, double *s_x)
+{
+    if (M < 0 || K <= 0 || ldx < K || !(eps >= 0.0)) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float u[K];
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const uint16_t xb = x[m * ldx + k];
+            const float xv = x_is_bf16 ? bf16_to_float(xb) : half_to_float(xb);
+            const float gv = g_is_bf16 ? bf16_to_float(g[k]) : half_to_float(g[k]);
+            u[k] = xv * gv;
+            ss += (double)xv * (double)xv;
+        }
+        const float s = quantize_run(u, K, 127.0f, -128, 127, x_q + m * K);
+        s_u[m] = s;
+        s_x[m] = (double)s * (1.0 / sqrt(ss / (double)K + eps));
+    }
+    return ORACLE_OK;
+}

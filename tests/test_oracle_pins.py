@@ -512,3 +512,86 @@ def test_sdpa_gqa_equals_mha_with_repeated_heads_and_bf16():
     bits = [(a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16) for a in r16]
     assert (oracle.sdpa_decode(*[a.astype(np.float16) for a in r16])["o"] ==
             oracle.sdpa_decode(*bits, bf16=True)["o"]).all()
+
+
+# ---- RMSNorm with the per-token quantization folded in ------------------------------------
+
+def _exact_rmsnorm_quantize(xrow, grow, eps):
+    """Exact rationals: u = RN32(x g), the exact quantization of u, and s_x from a 40-digit
+    square root of the exact mean of squares."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 40
+    u = [float(round_to_f32(Fraction(float(a)) * Fraction(float(b)))) for a, b in zip(xrow, grow)]
+    s, codes = exact_quantize(np.array(u, np.float32))
+    ms = sum(Fraction(float(a)) ** 2 for a in xrow) / len(xrow) + Fraction(eps)
+    d = Decimal(ms.numerator) / Decimal(ms.denominator)
+    sx = float(Decimal(s) / d.sqrt()) if ms > 0 else float("inf")
+    return s, codes, sx
+
+
+def test_rmsnorm_quantize_hand_worked():
+    """x = [3, 4], g = 1, eps = 0: mean square 12.5; s_u = RN32(4 / 127); 3 / s_u = 95.25 -> 95."""
+    q, su, sx = oracle.rmsnorm_quantize(np.array([[3, 4]], np.float16), np.ones(2, np.float16), 0.0)
+    assert q.tolist() == [[95, 127]]
+    assert Fraction(float(su[0])) == round_to_f32(Fraction(4, 127))
+    assert abs(sx[0] - float(su[0]) / 12.5 ** 0.5) <= 1e-16
+    # an all-zero row: zero codes and zero scales (eps > 0 keeps the norm finite)
+    q, su, sx = oracle.rmsnorm_quantize(np.zeros((1, 8), np.float16), np.ones(8, np.float16), 1e-6)
+    assert (q == 0).all() and su[0] == 0 and sx[0] == 0
+
+
+def test_rmsnorm_quantize_exact_rational_brute_force():
+    rng = np.random.default_rng(11)
+    for r in range(12):
+        K = int(rng.integers(2, 40))
+        x = (rng.standard_normal(K) * (50 if r % 3 == 0 else 1)).astype(np.float16)
+        g = (1 + 0.3 * rng.standard_normal(K)).astype(np.float16)
+        if r % 4 == 1:
+            x = (x * np.float16(1e-3)).astype(np.float16)
+        eps = [0.0, 1e-6, 1e-2][r % 3]
+        q, su, sx = oracle.rmsnorm_quantize(x[None, :], g, eps)
+        es, ec, esx = _exact_rmsnorm_quantize(x, g, eps)
+        assert q[0].tolist() == ec and float(su[0]) == es, r
+        assert abs(sx[0] - esx) <= 1e-15 * esx, r
+
+
+def test_rmsnorm_quantize_bf16_inputs_brute_force():
+    rng = np.random.default_rng(12)
+    K = 24
+    xf = (rng.standard_normal((3, K)) * 4).astype(np.float32)
+    xb = (xf.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 bits will do
+    gb = ((1 + 0.2 * rng.standard_normal(K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q, su, sx = oracle.rmsnorm_quantize(xb, gb, 1e-5, x_bf16=True, g_bf16=True)
+    to32 = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    for m in range(3):
+        es, ec, esx = _exact_rmsnorm_quantize(to32(xb[m]), to32(gb), 1e-5)
+        assert q[m].tolist() == ec and float(su[m]) == es
+        assert abs(sx[m] - esx) <= 1e-15 * esx
+
+
+def test_rmsnorm_quantize_reduces_to_quantize_and_is_scale_invariant():
+    from synth_inputs import linear_inputs
+    x, _ = linear_inputs(6, 16, 512, seed=13)
+    q0, s0 = oracle.quantize_per_token(x)
+    q, su, sx = oracle.rmsnorm_quantize(x, np.ones(512, np.float16), 1e-6)
+    assert (q == q0).all() and (su.view(np.uint32) == s0.view(np.uint32)).all()  # g = 1: u = x exactly
+    # eps = 0: the norm of 2^j x is the norm of x (the power of two is exact in every step)
+    g = (1 + 0.1 * np.random.default_rng(3).standard_normal(512)).astype(np.float16)
+    qa, _, sa = oracle.rmsnorm_quantize(x, g, 0.0)
+    qb, _, sb = oracle.rmsnorm_quantize((x.astype(np.float32) / 4).astype(np.float16), g, 0.0)
+    assert (qa == qb).all() and np.allclose(sa, sb, rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_quantize_reconstructs_the_normalized_row():
+    """s_x * q is the RMSNorm output (numpy fp64) within half a quantization step."""
+    from synth_inputs import linear_inputs
+    x, _ = linear_inputs(8, 16, 1024, seed=14)
+    g = (1 + 0.1 * np.random.default_rng(4).standard_normal(1024)).astype(np.float16)
+    eps = 1e-6
+    q, su, sx = oracle.rmsnorm_quantize(x, g, eps)
+    xf, gf = x.astype(np.float64), g.astype(np.float64)
+    n = xf / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + eps) * gf
+    err = np.abs(sx[:, None] * q - n)
+    # half a step, plus the fp32 roundings of x g and of the quotient (each <= 127 * 2^-24 steps)
+    assert (err <= sx[:, None] * (0.5 + 2 * 127 * 2.0 ** -24)).all()
+    assert (np.abs(q).max(axis=1) == 127).all()
