@@ -460,7 +460,8 @@ int oracle_rmsnorm_quantize(const uint16_t *x, int x_is_bf16, const uint16_t *g,
         }
         const float s = quantize_run(u, K, 127.0f, -128, 127, x_q + m * K);
         s_u[m] = s;
-        s_x[m] = (double)s * (1.0 / sqrt(ss / (double)K + eps));
+        /* an all-zero row has zero codes; its scale is 0 (also when eps = 0) */
+        s_x[m] = s == 0.0f ? 0.0 : (double)s * (1.0 / sqrt(ss / (double)K + eps));
     }
     return ORACLE_OK;
 }

@@ -535,9 +535,10 @@ def test_rmsnorm_quantize_hand_worked():
     assert q.tolist() == [[95, 127]]
     assert Fraction(float(su[0])) == round_to_f32(Fraction(4, 127))
     assert abs(sx[0] - float(su[0]) / 12.5 ** 0.5) <= 1e-16
-    # an all-zero row: zero codes and zero scales (eps > 0 keeps the norm finite)
-    q, su, sx = oracle.rmsnorm_quantize(np.zeros((1, 8), np.float16), np.ones(8, np.float16), 1e-6)
-    assert (q == 0).all() and su[0] == 0 and sx[0] == 0
+    # an all-zero row: zero codes and zero scales, with or without eps
+    for eps in (1e-6, 0.0):
+        q, su, sx = oracle.rmsnorm_quantize(np.zeros((1, 8), np.float16), np.ones(8, np.float16), eps)
+        assert (q == 0).all() and su[0] == 0 and sx[0] == 0
 
 
 def test_rmsnorm_quantize_exact_rational_brute_force():
