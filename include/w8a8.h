@@ -82,6 +82,27 @@ int quantize_per_token(const void *x, int x_dtype, int64_t M, int64_t K, int64_t
                        int8_t *x_q, float *s_x, void *stream);
 
 /*
+ * rmsnorm_quantize -- the producer of a linear layer's input writes the codes itself, so
+ * the per-token quantization (README "Metal Kernel 流水线" step 1; juejin post, "W8A8 对称量化":
+ * it must stay cheap) needs no pass of its own. The producer is RMSNorm with weight gamma:
+ *     n[m,k] = x[m,k] * gamma[k] / sqrt(mean_k x[m,k]^2 + eps).
+ * The row factor cancels in the per-token quantization of n, so the outputs are
+ *   x_q   [M, K] int8, row stride K: the per-token codes of u = x * gamma (one fp32 multiply
+ *         per element), exactly as quantize_per_token would compute them for u
+ *   s_x   [M] fp32: (max_k |u[m,k]| / 127) / sqrt(mean_k x[m,k]^2 + eps); 0 for a zero row
+ * so s_x[m] * x_q[m,k] approximates n[m,k] within half a quantization step, and x_q, s_x feed
+ * w8a8_gemm_pc / w8a8_gemm_pg / w4a8_gemm_pg as the outputs of quantize_per_token do. The
+ * codes are exact; s_x carries the fp32 rounding of the row's sum of squares.
+ *   x      [M, K] fp16 or bf16 (x_dtype), row stride ldx elements
+ *   gamma  [K] fp16 or bf16 (gamma_dtype)
+ *   eps    finite, >= 0
+ * Constraints: M >= 0, K >= 8, K % 8 == 0, ldx >= K, ldx % 8 == 0, all pointers 16-byte
+ * aligned. Inputs finite, sum of x^2 finite in fp32.
+ */
+int rmsnorm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const void *gamma,
+                     int gamma_dtype, float eps, int8_t *x_q, float *s_x, void *stream);
+
+/*
  * quantize_weight -- offline min-max weight quantization (README "说明": min-max
  * by default; "量化": symmetric int8 per channel / per group, int4 zero point 8).
  *   W      [N, K] fp32 (row n = output channel n)

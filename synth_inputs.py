@@ -27,6 +27,7 @@ __all__ = [
     "n_outlier_channels",
     "linear_inputs",
     "qwen3_8b_block_inputs",
+    "rmsnorm_inputs",
     "QWEN3_8B_BLOCK",
 ]
 
@@ -92,3 +93,17 @@ def qwen3_8b_block_inputs(M: int = 2048, seed: int = 0):
         idx = rng.choice(K, n_outlier_channels(K), replace=False)
         inputs[name] = _draw_activation(rng, M, K, idx)
     return inputs, weights
+
+
+def rmsnorm_inputs(M: int, K: int, seed: int = 0):
+    """Input rows and a norm weight for the RMSNorm producer of a linear layer's input.
+
+    ``x`` [M, K] fp16 as in ``linear_inputs`` (standard normal, 1 % outlier channels x 50),
+    drawn after ``idx``; then ``g = 1 + 0.1 * standard_normal(K)`` as fp16 -- a norm weight
+    near one, spread like a trained one. (No trained weights are available; these stand in.)
+    """
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(K, n_outlier_channels(K), replace=False)
+    x = _draw_activation(rng, M, K, idx)
+    g = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+    return x, g

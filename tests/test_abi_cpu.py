@@ -39,7 +39,8 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for required in ("quantize_per_token", "quantize_weight", "w8a8_gemm_pc", "w8a8_gemm_pg",
                      "w4a8_gemm_pg", "w8a8_linear", "w8a8_is_available", "w8a8_last_error",
-                     "w8a8_status_string", "int8_mv", "w8a8_gemm_splitk", "w8a8_gemm_splitk_workspace"):
+                     "w8a8_status_string", "int8_mv", "w8a8_gemm_splitk", "w8a8_gemm_splitk_workspace",
+                     "rmsnorm_quantize", "sdpa_decode", "quantize_weight_clipped"):
         assert required in names, names
 
 
@@ -118,6 +119,23 @@ def test_quantize_validation(w8a8):
     assert lib.quantize_weight(FAKE, 16, 256, 8, 32, FAKE, FAKE, None) == INVALID
     assert lib.quantize_weight(FAKE, 16, 200, 8, 0, FAKE, FAKE, None) == UNSUPPORTED_SHAPE
     assert lib.quantize_weight(FAKE, 0, 256, 8, 0, FAKE, FAKE, None) == INVALID
+
+
+def test_rmsnorm_quantize_validation(w8a8):
+    """Argument checks run on the host before anything is enqueued (no GPU here)."""
+    lib = w8a8.lib()
+    f = lambda *a: lib.rmsnorm_quantize(*a)
+    assert f(FAKE, F32, 4, 64, 64, FAKE, F16, 1e-6, FAKE, FAKE, None) == INVALID      # x dtype
+    assert f(FAKE, F16, 4, 64, 64, FAKE, F32, 1e-6, FAKE, FAKE, None) == INVALID      # gamma dtype
+    assert f(FAKE, F16, 4, 64, 64, FAKE, F16, -1.0, FAKE, FAKE, None) == INVALID      # eps < 0
+    assert f(FAKE, F16, 4, 64, 64, FAKE, F16, float("nan"), FAKE, FAKE, None) == INVALID
+    assert f(FAKE, F16, 4, 64, 64, FAKE, F16, float("inf"), FAKE, FAKE, None) == INVALID
+    assert f(FAKE, F16, -1, 64, 64, FAKE, F16, 1e-6, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, F16, 4, 60, 64, FAKE, F16, 1e-6, FAKE, FAKE, None) == UNSUPPORTED_SHAPE
+    assert f(FAKE, F16, 4, 64, 60, FAKE, F16, 1e-6, FAKE, FAKE, None) == INVALID      # ldx < K
+    assert f(FAKE, F16, 4, 64, 68, FAKE, F16, 1e-6, FAKE, FAKE, None) == INVALID      # ldx % 8
+    assert f(FAKE, F16, 4, 64, 64, None, F16, 1e-6, FAKE, FAKE, None) == INVALID      # null gamma
+    assert f(FAKE, F16, 4, 64, 64, ctypes.c_void_p(0x100002), F16, 1e-6, FAKE, FAKE, None) == INVALID  # misaligned
 
 
 def test_debug_force_config_bounds(w8a8):

@@ -34,6 +34,7 @@ _SIGNATURES = {
     "w8a8_debug_force_config": ([_int], _int),
     "quantize_per_token": ([_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "quantize_weight": ([_vp, _i64, _i64, _int, _int, _vp, _vp, _vp], _int),
+    "rmsnorm_quantize": ([_vp, _int, _i64, _i64, _i64, _vp, _int, ctypes.c_float, _vp, _vp, _vp], _int),
     "w8a8_gemm_pc": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w8a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w4a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
@@ -121,6 +122,27 @@ def quantize_per_token(x: torch.Tensor, x_q: torch.Tensor | None = None,
         s_x = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check(_lib.quantize_per_token(_ptr(x), _DTYPE_CODE[x.dtype], M, K, x.stride(0), _ptr(x_q),
                                    _ptr(s_x), _stream(stream)))
+    return x_q, s_x
+
+
+def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float, x_q: torch.Tensor | None = None,
+                     s_x: torch.Tensor | None = None, stream=None):
+    """x [M, K] fp16/bf16 (row stride x.stride(0)), gamma [K] fp16/bf16 -> (x_q int8 [M, K],
+    s_x fp32 [M]): the per-token codes of x * gamma, and s_x = (max|x * gamma| / 127) /
+    sqrt(mean(x^2) + eps), so s_x * x_q approximates RMSNorm(x) * gamma."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with a contiguous last dimension")
+    if x.dtype not in (torch.float16, torch.bfloat16) or gamma.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("x and gamma must be float16 or bfloat16")
+    M, K = x.shape
+    if gamma.shape != (K,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous [K] tensor")
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(_lib.rmsnorm_quantize(_ptr(x), _DTYPE_CODE[x.dtype], M, K, x.stride(0), _ptr(gamma),
+                                 _DTYPE_CODE[gamma.dtype], float(eps), _ptr(x_q), _ptr(s_x), _stream(stream)))
     return x_q, s_x
 
 

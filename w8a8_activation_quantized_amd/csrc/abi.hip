@@ -229,6 +229,37 @@ int quantize_per_token(const void *x, int x_dtype, int64_t M, int64_t K, int64_t
                     fn);
 }
 
+int rmsnorm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const void *gamma,
+                     int gamma_dtype, float eps, int8_t *x_q, float *s_x, void *stream) {
+    const char *fn = "rmsnorm_quantize";
+    if (x_dtype != W8A8_F16 && x_dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: x_dtype must be F16 or BF16", fn);
+    if (gamma_dtype != W8A8_F16 && gamma_dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: gamma_dtype must be F16 or BF16", fn);
+    if (!(eps >= 0.0f && eps <= 3.0e38f))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+    if (M < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: M = %lld < 0", fn, (long long)M);
+    if (K < 8 || K % 8 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 8", fn,
+                    (long long)K);
+    if (M > INT32_MAX || K > INT32_MAX || M * K > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (ldx < K || ldx % 8 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldx = %lld must be >= K and a multiple of 8", fn,
+                    (long long)ldx);
+    if (M > 0) {
+        if (!x || !gamma || !x_q || !s_x) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if (!aligned16(x) || !aligned16(gamma) || !aligned16(x_q) || !aligned16(s_x))
+            return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    }
+    int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    return launched(w8a8::launch_rmsnorm_quantize(x, x_dtype == W8A8_BF16, ldx, gamma, gamma_dtype == W8A8_BF16,
+                                                  eps, (int)M, (int)K, x_q, s_x, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_size, void *w_q,
                     float *s_w, void *stream) {
     const char *fn = "quantize_weight";

@@ -39,6 +39,8 @@ struct GemmProblem {
 // Activation quantization (fp16 / bf16 rows -> int8 + fp32 scale).
 hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int M, int K,
                                      int8_t *xq, float *sx, hipStream_t stream);
+hipError_t launch_rmsnorm_quantize(const void *x, bool x_bf16, int64_t ldx, const void *g, bool g_bf16, float eps,
+                                   int M, int K, int8_t *xq, float *sx, hipStream_t stream);
 
 // Offline weight quantization.
 hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,

@@ -111,6 +111,143 @@ hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, flo
     return hipGetLastError();
 }
 
+// ---- RMSNorm with the per-token quantization folded in -------------------------------
+// The producer of a linear layer's input writes its codes directly (Cider README
+// "Metal Kernel 流水线" runs the quantization as a dispatch of its own in front of the
+// GEMM; juejin post, "W8A8 对称量化": that online step must stay cheap). The producer is
+// RMSNorm with a per-channel weight g: n[k] = x[k] g[k] / sqrt(mean x^2 + eps). Its row
+// factor is positive and common to the row, so it cancels in n / (max|n| / 127): the
+// codes are those of u = x g (one fp32 multiply) and the factor goes into the scale,
+// s_x = (max|u| / 127) / sqrt(mean x^2 + eps). The row's x chunks are held in
+// registers between the pass that finds max|u| and sum x^2 and the pass that writes
+// codes; g (2 K bytes, read by every row) is read again in the second pass from the
+// caches. The per-element quotient u / s uses
+// the corrected reciprocal of the quantize kernel: with r = RN(1 / s) and the residual
+// taken exactly by an fma, Markstein's theorem gives the correctly rounded quotient for
+// any fp32 u (checked on the CPU against IEEE division on 1e9 products of two halves
+// with quotients at and next to every half-integer; the only difference is the sign of a
+// zero quotient, which makes no difference to the code).
+
+template <bool XBF, bool GBF>
+__device__ __forceinline__ void norm_stats8(uint4 xc, uint4 gc, uint32_t &amax, float &ss) {
+    const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w}, gw[4] = {gc.x, gc.y, gc.z, gc.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float xv = to_float<XBF>(h ? xw[i] >> 16 : xw[i] & 0xffffu);
+            const float u = xv * to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu);
+            const uint32_t ub = __builtin_bit_cast(uint32_t, u) & 0x7fffffffu;
+            amax = amax > ub ? amax : ub;
+            ss = __builtin_fmaf(xv, xv, ss);
+        }
+}
+
+template <bool XBF, bool GBF, bool FAST>
+__device__ __forceinline__ uint2 norm_quant8(uint4 xc, uint4 gc, float s, float r) {
+    const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w}, gw[4] = {gc.x, gc.y, gc.z, gc.w};
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float u = to_float<XBF>(h ? xw[i] >> 16 : xw[i] & 0xffffu) *
+                            to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu);
+            out[i >> 1] |= code_byte(quotient<FAST>(u, s, r)) << (8 * (2 * (i & 1) + h));
+        }
+    return make_uint2(out[0], out[1]);
+}
+
+// A row per 256-thread workgroup: thread t takes the 16-byte chunks t + 256 j, holds the
+// first CPT of them in registers between the two passes and reads the rest again; the
+// four waves combine max|u| and sum x^2 through LDS.
+constexpr int NORM_THREADS = 256;
+
+template <bool XBF, bool GBF, bool FAST, int CPT>
+__device__ __forceinline__ void norm_row_store(const uint4 (&cache)[CPT], const uint16_t *row, const uint16_t *g,
+                                               int8_t *qrow, int tid, int nch, float s, float r) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + NORM_THREADS * j;
+        if (c < nch)
+            *reinterpret_cast<uint2 *>(qrow + 8 * c) =
+                norm_quant8<XBF, GBF, FAST>(cache[j], *reinterpret_cast<const uint4 *>(g + 8 * c), s, r);
+    }
+    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS)
+        *reinterpret_cast<uint2 *>(qrow + 8 * c) = norm_quant8<XBF, GBF, FAST>(
+            *reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c), s, r);
+}
+
+template <int CPT, bool XBF, bool GBF>
+__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const uint16_t *__restrict__ x, int64_t ldx,
+                                                                         const uint16_t *__restrict__ g, float eps,
+                                                                         int K, int8_t *__restrict__ xq,
+                                                                         float *__restrict__ sx) {
+    __shared__ uint32_t wmax[NORM_THREADS / 64];
+    __shared__ float wsum[NORM_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = blockIdx.x;
+    const uint16_t *row = x + (int64_t)m * ldx;
+    int8_t *qrow = xq + (int64_t)m * K;
+    const int nch = K >> 3;
+
+    uint4 cache[CPT];
+    uint32_t amax = 0;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + NORM_THREADS * j;
+        cache[j] = c < nch ? *reinterpret_cast<const uint4 *>(row + 8 * c) : make_uint4(0, 0, 0, 0);
+        if (c < nch) norm_stats8<XBF, GBF>(cache[j], *reinterpret_cast<const uint4 *>(g + 8 * c), amax, ss);
+    }
+    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS)
+        norm_stats8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c),
+                              *reinterpret_cast<const uint4 *>(g + 8 * c), amax, ss);
+    amax = wave_max_u32(amax);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) {
+        wmax[wave] = amax;
+        wsum[wave] = ss;
+    }
+    __syncthreads();
+    amax = wmax[0];
+    ss = wsum[0];
+#pragma unroll
+    for (int w = 1; w < NORM_THREADS / 64; ++w) {
+        amax = amax > wmax[w] ? amax : wmax[w];
+        ss += wsum[w];
+    }
+
+    const float s = __builtin_bit_cast(float, amax) / 127.0f;
+    if (tid == 0) sx[m] = s == 0.0f ? 0.0f : s * (1.0f / __builtin_sqrtf(ss / (float)K + eps));
+    if (s == 0.0f) {
+        for (int c = tid; c < nch; c += NORM_THREADS) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
+        return;
+    }
+    if (s >= kMinFastScale)
+        norm_row_store<XBF, GBF, true, CPT>(cache, row, g, qrow, tid, nch, s, 1.0f / s);
+    else
+        norm_row_store<XBF, GBF, false, CPT>(cache, row, g, qrow, tid, nch, s, 0.f);
+}
+
+template <bool XBF, bool GBF>
+hipError_t launch_norm_rows(const void *x, int64_t ldx, const void *g, float eps, int M, int K, int8_t *xq,
+                            float *sx, hipStream_t stream) {
+    const int per_thread = (K / 8 + NORM_THREADS - 1) / NORM_THREADS;
+    dim3 grid(M), block(NORM_THREADS);
+    const uint16_t *xp = static_cast<const uint16_t *>(x), *gp = static_cast<const uint16_t *>(g);
+#define W8A8_NORM_LAUNCH(C) \
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<C, XBF, GBF>), grid, block, 0, stream, xp, ldx, gp, eps, K, xq, sx)
+    if (per_thread <= 1) W8A8_NORM_LAUNCH(1);
+    else if (per_thread <= 2) W8A8_NORM_LAUNCH(2);
+    else if (per_thread <= 4) W8A8_NORM_LAUNCH(4);
+    else if (per_thread <= 6) W8A8_NORM_LAUNCH(6);
+    else W8A8_NORM_LAUNCH(8);
+#undef W8A8_NORM_LAUNCH
+    return hipGetLastError();
+}
+
 // ---- offline weight quantization ------------------------------------------------------
 // One wavefront per run (a weight row for per-channel, one K-group for per-group).
 // Min-max symmetric (Cider README "说明"): s = max|W| / qdiv, q = clamp(rne(W / s)).
@@ -245,6 +382,14 @@ hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int 
                                      int8_t *xq, float *sx, hipStream_t stream) {
     return bf16 ? launch_rows<true>(x, ldx, M, K, xq, sx, stream)
                 : launch_rows<false>(x, ldx, M, K, xq, sx, stream);
+}
+
+hipError_t launch_rmsnorm_quantize(const void *x, bool x_bf16, int64_t ldx, const void *g, bool g_bf16, float eps,
+                                   int M, int K, int8_t *xq, float *sx, hipStream_t stream) {
+    if (x_bf16) return g_bf16 ? launch_norm_rows<true, true>(x, ldx, g, eps, M, K, xq, sx, stream)
+                              : launch_norm_rows<true, false>(x, ldx, g, eps, M, K, xq, sx, stream);
+    return g_bf16 ? launch_norm_rows<false, true>(x, ldx, g, eps, M, K, xq, sx, stream)
+                  : launch_norm_rows<false, false>(x, ldx, g, eps, M, K, xq, sx, stream);
 }
 
 hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
