@@ -22,7 +22,7 @@ same graph runs up to 20 % slower per step (clocks still ramping), so a short ru
 that transient rather than the kernels.
 
 Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 1000] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1|m1w4|qwen3|mv|mvg128|sdpa] [--copy-ref-mb MB] [--no-graph]
+       [--workload pc|pg64|pg128|w4|m1|m1w4|qwen3|mv|mvg128|sdpa|rmsnorm] [--copy-ref-mb MB] [--no-graph]
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3", "mv", "mvg128", "sdpa"])
+    ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3", "mv", "mvg128", "sdpa", "rmsnorm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle sample")
@@ -233,6 +233,54 @@ def sdpa_bench(args, torch, w8a8):
     return result
 
 
+def rmsnorm_bench(args, torch, w8a8):
+    """RMSNorm producer writing the int8 codes and per-token scale of the next linear layer
+    (rmsnorm_quantize) at M = 4096 token rows of K = 10240, the long-K layer input: one step
+    is one call; x is read once and the codes written once, so the roofline is HBM. x rotates
+    over copies larger than the Infinity Cache, as a producer's output would arrive."""
+    import oracle
+    from synth_inputs import rmsnorm_inputs
+
+    M, K, eps = 4096, 10240, 1e-6
+    x, g = rmsnorm_inputs(M, K, seed=0)
+    copies = max(1, -(-(320 << 20) // x.nbytes))
+    xs = [torch.from_numpy(x).cuda() for _ in range(copies)]
+    gd = torch.from_numpy(g).cuda()
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        w8a8.rmsnorm_quantize(xs[i % copies], gd, eps, xq, sx, stream=torch.cuda.current_stream())
+
+    ms_per_step, event_ms = timed_steps(args, torch, step)
+    kernel_ms = event_ms if event_ms is not None else ms_per_step
+    alg_bytes = M * K * 2 + K * 2 + M * K + M * 4  # x and g in, codes and scales out
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    result = {
+        "metric": f"RMSNorm -> int8 codes + per-token scale (rmsnorm_quantize), M={M} K={K} fp16",
+        "value": alg_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "rmsnorm_quantize: the norm in front of a linear layer writes its int8 input",
+                   "M": M, "K": K, "in": "fp16", "gamma": "fp16", "x_copies": copies, "parallelism": "single GPU"},
+        "step_event_ms": event_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
+                     "kernel": "rmsnorm_quantize_kernel", "launch_ms": kernel_ms, "alg_bytes": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        oracle.build(force=False)
+        rows, t0 = 0, time.perf_counter()
+        while rows < M and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.rmsnorm_quantize(x[rows:rows + 256], g, eps)
+            rows += 256
+        dt = time.perf_counter() - t0
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        result["cpu_baseline"] = {"value": alg_bytes * rows / M / dt / 1e9, "unit": "GB/s", "cores": cores,
+                                  "kind": "oracle", "sample": f"first {rows} of {M} rows; {dt:.2f} s"}
+    return result
+
+
 def timed_steps(args, torch, step):
     """Warmup, then args.steps steps replayed as one captured graph (or issued one by one
     with --no-graph). Returns (ms per step by the host clock, ms per step by events or
@@ -388,6 +436,9 @@ def main():
         return 0
     if args.workload == "sdpa":
         print(json.dumps(sdpa_bench(args, torch, w8a8)), flush=True)
+        return 0
+    if args.workload == "rmsnorm":
+        print(json.dumps(rmsnorm_bench(args, torch, w8a8)), flush=True)
         return 0
     if args.workload in ("mv", "mvg128"):
         print(json.dumps(mv_decode(args, torch, w8a8, 0 if args.workload == "mv" else 128)), flush=True)
