@@ -124,9 +124,9 @@ hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, flo
 // caches. The per-element quotient u / s uses
 // the corrected reciprocal of the quantize kernel: with r = RN(1 / s) and the residual
 // taken exactly by an fma, Markstein's theorem gives the correctly rounded quotient for
-// any fp32 u (checked on the CPU against IEEE division on 1e9 products of two halves
-// with quotients at and next to every half-integer; the only difference is the sign of a
-// zero quotient, which makes no difference to the code).
+// any fp32 u (checked on the CPU against IEEE division on 2.5e8 products of two halves,
+// a quarter of them with quotients at and next to a half-integer; the only difference is
+// the sign of a zero quotient, which makes no difference to the code).
 
 template <bool XBF, bool GBF>
 __device__ __forceinline__ void norm_stats8(uint4 xc, uint4 gc, uint32_t &amax, float &ss) {
