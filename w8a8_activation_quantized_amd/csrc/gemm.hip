@@ -1998,6 +1998,7 @@ constexpr Config kConfigs[] = {
     {64, 64, 4},    // 12: direct-to-LDS, BN=64 BM=64, 4 stages, 4 waves (32 n x 32 m each); small M
     {256, 320, 8},  // 13: direct-to-LDS, BN=320 BM=256, 4 stages of 64, two wave groups in alternation
     {128, 128, 4},  // 14: direct-to-LDS, BN=128 BM=128, 4 stages, 4 waves (64 n x 64 m each)
+    {128, 64, 4},   // 15: direct-to-LDS, BN=64 BM=128, 6 stages, 8 waves (32 n x 32 m each); mid M
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2099,6 +2100,20 @@ int choose_config(const GemmProblem &p) {
         return p.M <= (p.wkind == W_INT4 ? 1024 : 512) ? 12 : 4;
     }
     if (!dma || p.wkind != W_INT8) return p.M <= 128 ? 4 : 1;
+    // 16 < M <= 2048 (too few tiles for the large shapes): the largest of 128 x 128,
+    // 64 x 128 and 64 x 64 whose full tiles make one round of workgroups that fills more
+    // than half of the chip; measured on MI355X at M = 64 .. 2048, N = 1024 .. 10240,
+    // K = 2560 .. 10240 (e.g. M = 128, N = 10240: 64 x 128 14.8 us against 16.2 for 64 x 64;
+    // M = 256: 128 x 128 18.7 against 21.4; M = 768, N = 2560, K = 10240: 64 x 128 36.7
+    // against 46.0; M = 1536: 128 x 128 53.9 against 71.5; M = 2048, N = 1024, K = 4096:
+    // 64 x 128 16.6 against 19.2)
+    if (p.M <= 2048) {
+        const struct { int id, bm, bn; } one_round[] = {{14, 128, 128}, {15, 128, 64}, {12, 64, 64}};
+        for (const auto &c : one_round) {
+            const int64_t t = (int64_t)((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn);
+            if (p.M % c.bm == 0 && t > cus / 2 && t <= cus) return c.id;
+        }
+    }
     // per-channel: among the DMA kernels, the fewest chip-wide rounds of tiles times tile
     // area over the kernel's work rate per unit area (320 x 256 in alternating wave
     // groups: 1.05, 160 x 256: 1.0, 128 x 256: 0.9, 64 x 64: 0.4); partial tiles and a
@@ -2258,6 +2273,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 12: return launch_ms<64, 64, 4, 2, 2>(p, gm, stream);
         case 13: return launch_pp<320, 256, 4>(p, gm, stream);
         case 14: return launch_ms<128, 128, 4, 2, 2>(p, gm, stream);
+        case 15: return launch_ms<64, 128, 6, 2, 4>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
         case 6: return launch_ms<160, 256, 3, 2, 4>(p, gm, stream);
         case 7: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
