@@ -40,6 +40,7 @@
 //    loaded from a clamped address and replaced by zero codes (int4: nibble 8),
 //    which add nothing to the integer sums.
 #include <atomic>
+#include <type_traits>
 
 #include "act_quant.h"
 #include "device_common.h"
@@ -934,17 +935,21 @@ __device__ __forceinline__ int mg_ops_per_stage(int wave) {
     return n + (wave < S::NSD ? 1 : 0);
 }
 
+// Weight fragments as read from LDS: int8 codes (v4i), or for int4 the lane's 16 packed
+// nibbles (uint2), unpacked by mg_unpack once the read has landed.
+template <class S>
+using MgRawA = typename std::conditional<S::WK == W_INT4, uint2, v4i>::type;
+
 template <class S>
 __device__ __forceinline__ void mg_frags(const int8_t *st, int ks, int wm, int wn, int frow, int fchunk,
-                                         v4i (&a)[S::FN], v4i (&b)[S::FM]) {
+                                         MgRawA<S> (&a)[S::FN], v4i (&b)[S::FM]) {
 #pragma unroll
     for (int fn = 0; fn < S::FN; ++fn) {
         const int r = wn * S::WN + fn * 16 + frow;
         if constexpr (S::WK == W_INT4) {
             const int byte = ks * 32 + fchunk * 8;  // 16 int4 values of this lane
-            const uint2 w = *reinterpret_cast<const uint2 *>(st + r * 64 + (((byte >> 4) ^ ((r >> 2) & 3)) << 4) +
-                                                             (byte & 15));
-            a[fn] = __builtin_bit_cast(v4i, unpack_nibbles_x16(w.x, w.y));
+            const v4i q = *reinterpret_cast<const v4i *>(st + r * 64 + (((byte >> 4) ^ ((r >> 2) & 3)) << 4));
+            a[fn] = (byte & 8) ? make_uint2(q[2], q[3]) : make_uint2(q[0], q[1]);
         } else {
             a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(r, ks * 4 + fchunk));
         }
@@ -952,6 +957,17 @@ __device__ __forceinline__ void mg_frags(const int8_t *st, int ks, int wm, int w
 #pragma unroll
     for (int fm = 0; fm < S::FM; ++fm)
         b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<128>(wm * S::WM + fm * 16 + frow, ks * 4 + fchunk));
+}
+
+template <class S>
+__device__ __forceinline__ void mg_unpack(const MgRawA<S> (&raw)[S::FN], v4i (&a)[S::FN]) {
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn) {
+        if constexpr (S::WK == W_INT4)
+            a[fn] = __builtin_bit_cast(v4i, unpack_nibbles_x16(raw[fn].x, raw[fn].y));
+        else
+            a[fn] = raw[fn];
+    }
 }
 
 // MFMAs of one K-step; FIRST: the step opens a group (accumulate from zero).
@@ -1050,12 +1066,14 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
     lds_barrier();
 
     v4i a0[FN], b0[FM], a1[FN], b1[FM];
+    MgRawA<S> r0[FN], r1[FN];  // weight fragments as read (int4: packed until unpacked)
     // scales of the group acc holds (zero before the first group, whose fold adds +0 to t = +0)
     float4 sw0[FN], sw1[FN];
 #pragma unroll
     for (int i = 0; i < FN; ++i) sw0[i] = sw1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    mg_frags<S>(smem, 0, wm, wn, frow, fchunk, a0, b0);
+    mg_frags<S>(smem, 0, wm, wn, frow, fchunk, r0, b0);
     wait_lgkmcnt0();
+    mg_unpack<S>(r0, a0);
     int cur = 0;
     for (int kt = 0; kt < KT; ++kt) {
         const int fill = kt + STAGES - 1;
@@ -1066,18 +1084,20 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
         }
         const int8_t *st = smem + cur * S::STAGE;
         // everything this wave still needs from stage kt is read before its barrier
-        mg_frags<S>(st, 1, wm, wn, frow, fchunk, a1, b1);
+        mg_frags<S>(st, 1, wm, wn, frow, fchunk, r1, b1);
         // K-step 0 opens group kt (gs 128) or 2 kt (gs 64) while the previous group is folded
         mg_fold_mma<S>(acc, S::GPK == 2 ? sw1 : sw0, t, a0, b0);
         mg_scales<S>(st, 0, wn, fchunk, sw0);
         if constexpr (S::GPK == 2) mg_scales<S>(st, 1, wn, fchunk, sw1);
         wait_lgkmcnt0();
+        mg_unpack<S>(r1, a1);
         if (kt + 1 < KT) {
             wait_vmcnt_rt(OPS * min(STAGES - 2, KT - 2 - kt));
             lds_barrier();
             int nb = cur + 1;
             nb -= nb >= STAGES ? STAGES : 0;
-            mg_frags<S>(smem + nb * S::STAGE, 0, wm, wn, frow, fchunk, a0, b0);
+            // read now, unpacked after the MFMAs below are issued
+            mg_frags<S>(smem + nb * S::STAGE, 0, wm, wn, frow, fchunk, r0, b0);
             cur = nb;
         }
         if constexpr (S::GPK == 2) {
@@ -1086,6 +1106,7 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
             mg_mma<S, false>(acc, a1, b1);  // K-step 1 closes group kt
         }
         wait_lgkmcnt0();
+        mg_unpack<S>(r0, a0);
     }
     mg_fold<S>(acc, S::GPK == 2 ? sw1 : sw0, t);  // the last group
 
