@@ -55,6 +55,18 @@ __device__ __forceinline__ void dma_4B(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)l, 4, 0, 0);
 }
 
+// A 16-byte LDS read of data written by an earlier LDS DMA that the caller's own vmcnt wait
+// has already retired, issued in inline asm and retired inside the same block. As an
+// ordinary load the compiler cannot tell that region from the DMA targets still in flight
+// and puts a wait for all of them in front of the read.
+__device__ __forceinline__ float4 lds_read_f4_now(const float *p) {
+    typedef float v4f_t __attribute__((ext_vector_type(4)));
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float *)p;
+    v4f_t v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding). The waits and
 // the barrier are fenced with sched_barrier(0): the instruction scheduler otherwise moves
 // MFMAs (which touch no memory) across them, so a wait meant to trail a run of MFMAs ends

@@ -1578,18 +1578,6 @@ __device__ __forceinline__ void gv_wait_tail(int after) {
     }
 }
 
-// Group scale from the LDS table, read in inline asm and retired inside the same block. As
-// an ordinary load the compiler puts a wait for every weight DMA in flight in front of it
-// (it cannot tell the table from the ring slots), which drains the ring at each group end;
-// the table's own DMA is retired by the first chunk wait, which precedes every read.
-__device__ __forceinline__ float4 lds_read_f4_now(const float *p) {
-    typedef float v4f_t __attribute__((ext_vector_type(4)));
-    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float *)p;
-    v4f_t v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-
 template <int GS, int WK, bool XL, int FQ>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProblem p, int seg_chunks, int slots,
                                                                         int table_groups) {
@@ -1704,6 +1692,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
                 const int ks = (c0 + j) * SPC + t;  // global K-step
                 acc = mfma_i8(a, bx, (ks % S::SPG) == 0 ? v4i{0, 0, 0, 0} : acc);
                 if ((ks % S::SPG) == S::SPG - 1) {
+                    // (the table's DMA was retired by the first chunk wait)
                     const float4 sw = lds_read_f4_now(table + (ks / S::SPG - g0) * 16 + 4 * fchunk);
                     facc[0] = __builtin_fmaf((float)acc[0], sw.x, facc[0]);
                     facc[1] = __builtin_fmaf((float)acc[1], sw.y, facc[1]);

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(64 * MV_MAX_WAVES) void mv_kernel(GemmProblem p, in
             if constexpr (GROUPED) {
                 if (GS == 64 ? (t & 1) == 1 : t == 3) {
                     const int g = (c0 + j) * GPC + (GS == 64 ? (t >> 1) : 0);
-                    const float4 sw = *reinterpret_cast<const float4 *>(table + (g - g0) * 16 + 4 * fq);
+                    // (the table's DMA was retired by the first chunk wait)
+                    const float4 sw = lds_read_f4_now(table + (g - g0) * 16 + 4 * fq);
                     facc[0] = __builtin_fmaf(acc[0], sw.x, facc[0]);
                     facc[1] = __builtin_fmaf(acc[1], sw.y, facc[1]);
                     facc[2] = __builtin_fmaf(acc[2], sw.z, facc[2]);
