@@ -2115,13 +2115,14 @@ int choose_config(const GemmProblem &p) {
     const int64_t cus = num_cus();
     if (p.gs > 0 && p.out != OUT_I32) {
         // per-group: the 128 x 256 DMA kernel once it has enough tiles to spread over the
-        // chip (the group fold is VALU work it does not overlap), else 64 x 64 DMA tiles up
-        // to M = 512 (int8) / 1024 (int4), else the register-staged 64 x 64 kernel; without
-        // 128-value K-tiles the register-staged kernels
+        // chip, else 64 x 64 DMA tiles up to M = 768 (int8) / 1024 (int4), else the
+        // register-staged 64 x 64 kernel (measured at N = 2560, K = 10240: M = 768 gs 128
+        // 76.7 us against 86.6, M = 1024 148 against 95.6); without 128-value K-tiles the
+        // register-staged kernels
         if (!dma) return p.M <= 128 ? 4 : 0;
         const int64_t t11 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
         if (t11 >= cus / 2) return 11;
-        return p.M <= (p.wkind == W_INT4 ? 1024 : 512) ? 12 : 4;
+        return p.M <= (p.wkind == W_INT4 ? 1024 : 768) ? 12 : 4;
     }
     if (!dma || p.wkind != W_INT8) return p.M <= 128 ? 4 : 1;
     // 16 < M <= 2048 (too few tiles for the large shapes): the largest of 128 x 128,
