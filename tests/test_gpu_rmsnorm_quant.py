@@ -77,6 +77,12 @@ def test_rmsnorm_quantize_parity(w8a8, M, K):
                 check(w8a8, x, g, eps, x_bf16, g_bf16, f"rmsnorm_quantize {M}x{K} bf16x={x_bf16} bf16g={g_bf16} eps={eps}")
 
 
+def test_rmsnorm_quantize_benchmark_size(w8a8):
+    """The benchmark's workload (M = 4096 rows of K = 10240, fp16, eps 1e-6), every row."""
+    x, g = rmsnorm_inputs(4096, 10240, seed=0)
+    check(w8a8, x, g, 1e-6, False, False, "rmsnorm_quantize 4096x10240 (benchmark workload)")
+
+
 def test_rmsnorm_quantize_special_rows_and_stride(w8a8):
     K = 1024
     x, g = rmsnorm_inputs(8, K, seed=5)
