@@ -267,6 +267,9 @@ def sample_rows(M, n=40, seed=0):
     ("pc", 8192, 2560, 10240),
     ("pc", 1, 10240, 2560),
     ("pc", 1024, 2560, 10240),
+    ("pc", 2048, 1024, 4096),     # 64 x 128 tiles, one round (Qwen3 k/v shape)
+    ("pc", 1536, 2560, 10240),    # 128 x 128 tiles, one round
+    ("pg128", 768, 2560, 10240),  # 64 x 64 per-group DMA tiles
     ("pg128", 4096, 10240, 2560),
     ("pg64", 8192, 2560, 10240),
     ("pg64", 128, 10240, 2560),
