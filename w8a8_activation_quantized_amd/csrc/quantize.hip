@@ -180,64 +180,65 @@ hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, flo
 // RMSNorm with a per-channel weight g: n[k] = x[k] g[k] / sqrt(mean x^2 + eps). Its row
 // factor is positive and common to the row, so it cancels in n / (max|n| / 127): the
 // codes are those of u = x g (one fp32 multiply) and the factor goes into the scale,
-// s_x = (max|u| / 127) / sqrt(mean x^2 + eps). The row's x chunks are held in
+// s_x = (max|u| / 127) / sqrt(mean x^2 + eps). The row's products u = x g are held in
 // registers between the pass that finds max|u| and sum x^2 and the pass that writes
-// codes; g (2 K bytes, read by every row) is read again in the second pass from the
-// caches. The per-element quotient u / s uses
+// codes, so x and g are read once (rows longer than the registers hold recompute the
+// rest). The per-element quotient u / s uses
 // the corrected reciprocal of the quantize kernel: with r = RN(1 / s) and the residual
 // taken exactly by an fma, Markstein's theorem gives the correctly rounded quotient for
 // any fp32 u (checked on the CPU against IEEE division on 2.5e8 products of two halves,
 // a quarter of them with quotients at and next to a half-integer; the only difference is
 // the sign of a zero quotient, which makes no difference to the code).
 
+// u = x g for the eight values of one 16-byte chunk of x and of g (element e = 2 i + h of
+// dword i), one fp32 multiply each.
 template <bool XBF, bool GBF>
-__device__ __forceinline__ void norm_stats8(uint4 xc, uint4 gc, uint32_t &amax, float &ss) {
+__device__ __forceinline__ void norm_u8(uint4 xc, uint4 gc, float (&u)[8], float (&xv)[8]) {
     const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w}, gw[4] = {gc.x, gc.y, gc.z, gc.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const float xv = to_float<XBF>(h ? xw[i] >> 16 : xw[i] & 0xffffu);
-            const float u = xv * to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu);
-            const uint32_t ub = __builtin_bit_cast(uint32_t, u) & 0x7fffffffu;
-            amax = amax > ub ? amax : ub;
-            ss = __builtin_fmaf(xv, xv, ss);
+            xv[2 * i + h] = to_float<XBF>(h ? xw[i] >> 16 : xw[i] & 0xffffu);
+            u[2 * i + h] = xv[2 * i + h] * to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu);
         }
 }
 
-template <bool XBF, bool GBF, bool FAST>
-__device__ __forceinline__ uint2 norm_quant8(uint4 xc, uint4 gc, float s, float r) {
-    const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w}, gw[4] = {gc.x, gc.y, gc.z, gc.w};
+__device__ __forceinline__ void norm_stats8(const float (&u)[8], const float (&xv)[8], uint32_t &amax, float &ss) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t ub = __builtin_bit_cast(uint32_t, u[e]) & 0x7fffffffu;
+        amax = amax > ub ? amax : ub;
+        ss = __builtin_fmaf(xv[e], xv[e], ss);
+    }
+}
+
+template <bool FAST>
+__device__ __forceinline__ uint2 norm_quant8(const float (&u)[8], float s, float r) {
     uint32_t out[2] = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float u = to_float<XBF>(h ? xw[i] >> 16 : xw[i] & 0xffffu) *
-                            to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu);
-            out[i >> 1] |= code_byte(quotient<FAST>(u, s, r)) << (8 * (2 * (i & 1) + h));
-        }
+    for (int e = 0; e < 8; ++e) out[e >> 2] |= code_byte(quotient<FAST>(u[e], s, r)) << (8 * (e & 3));
     return make_uint2(out[0], out[1]);
 }
 
-// A row per 256-thread workgroup: thread t takes the 16-byte chunks t + 256 j, holds the
-// first CPT of them in registers between the two passes and reads the rest again; the
-// four waves combine max|u| and sum x^2 through LDS.
+// A row per 256-thread workgroup: thread t takes the 16-byte chunks t + 256 j, holds u = x g
+// of the first CPT of them in registers between the two passes and recomputes the rest;
+// the four waves combine max|u| and sum x^2 through LDS.
 constexpr int NORM_THREADS = 256;
 
 template <bool XBF, bool GBF, bool FAST, int CPT>
-__device__ __forceinline__ void norm_row_store(const uint4 (&cache)[CPT], const uint16_t *row, const uint16_t *g,
+__device__ __forceinline__ void norm_row_store(const float (&uc)[CPT][8], const uint16_t *row, const uint16_t *g,
                                                int8_t *qrow, int tid, int nch, float s, float r) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + NORM_THREADS * j;
-        if (c < nch)
-            *reinterpret_cast<uint2 *>(qrow + 8 * c) =
-                norm_quant8<XBF, GBF, FAST>(cache[j], *reinterpret_cast<const uint4 *>(g + 8 * c), s, r);
+        if (c < nch) *reinterpret_cast<uint2 *>(qrow + 8 * c) = norm_quant8<FAST>(uc[j], s, r);
     }
-    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS)
-        *reinterpret_cast<uint2 *>(qrow + 8 * c) = norm_quant8<XBF, GBF, FAST>(
-            *reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c), s, r);
+    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS) {
+        float u[8], xv[8];
+        norm_u8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c), u, xv);
+        *reinterpret_cast<uint2 *>(qrow + 8 * c) = norm_quant8<FAST>(u, s, r);
+    }
 }
 
 template <int CPT, bool XBF, bool GBF>
@@ -253,18 +254,24 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
     int8_t *qrow = xq + (int64_t)m * K;
     const int nch = K >> 3;
 
-    uint4 cache[CPT];
+    float uc[CPT][8];
     uint32_t amax = 0;
     float ss = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + NORM_THREADS * j;
-        cache[j] = c < nch ? *reinterpret_cast<const uint4 *>(row + 8 * c) : make_uint4(0, 0, 0, 0);
-        if (c < nch) norm_stats8<XBF, GBF>(cache[j], *reinterpret_cast<const uint4 *>(g + 8 * c), amax, ss);
+        float xv[8];
+        if (c < nch) {
+            norm_u8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c),
+                              uc[j], xv);
+            norm_stats8(uc[j], xv, amax, ss);
+        }
     }
-    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS)
-        norm_stats8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c),
-                              *reinterpret_cast<const uint4 *>(g + 8 * c), amax, ss);
+    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS) {
+        float u[8], xv[8];
+        norm_u8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c), u, xv);
+        norm_stats8(u, xv, amax, ss);
+    }
     amax = wave_max_u32(amax);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
@@ -288,9 +295,9 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
         return;
     }
     if (s >= kMinFastScale)
-        norm_row_store<XBF, GBF, true, CPT>(cache, row, g, qrow, tid, nch, s, 1.0f / s);
+        norm_row_store<XBF, GBF, true, CPT>(uc, row, g, qrow, tid, nch, s, 1.0f / s);
     else
-        norm_row_store<XBF, GBF, false, CPT>(cache, row, g, qrow, tid, nch, s, 0.f);
+        norm_row_store<XBF, GBF, false, CPT>(uc, row, g, qrow, tid, nch, s, 0.f);
 }
 
 template <bool XBF, bool GBF>
