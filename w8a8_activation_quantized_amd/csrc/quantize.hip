@@ -50,9 +50,12 @@ __device__ __forceinline__ void quant_row_store(const uint4 (&cache)[CPL], const
 
 // Rows of at least this many values go to the workgroup-per-row kernel (measured on MI355X,
 // x streamed from HBM: K = 10240, M = 4096: 21.3 against 26.2 us; K = 12288, M = 2048: 14.7
-// against 17.6; K = 4096: 7.2 against 7.6; at K = 2560 the wave-per-row kernel is faster,
-// 8.3 against 8.8 us at M = 4096).
+// against 17.6; K = 4096: 7.2 against 7.6; at K = 2560 four waves per row are slower than
+// one, 8.8 against 8.3 us at M = 4096).
 constexpr int kRowsPerWorkgroupK = 4096;
+// Rows of 2048 .. 4095 values: a workgroup of two waves per row (M = 4096, K = 2560: 8.2
+// against 8.4 us; M = 8192: 12.8 against 13.8 us); shorter rows keep a wave per row.
+constexpr int kRowsPerPairK = 2048;
 
 // CPL = chunks per lane kept in registers; rows with more chunks than 64*CPL take
 // a second read pass for the remainder.
@@ -97,10 +100,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
 
 // Long rows: a row per 256-thread workgroup (thread t takes the chunks t + 256 j, up to CPT
 // of them held in registers), the four waves' maxima combined through LDS; the same codes.
-template <int CPT, bool BF16>
-__global__ __launch_bounds__(256) void quantize_rows_wg_kernel(const uint16_t *__restrict__ x, int64_t ldx, int K,
-                                                                int8_t *__restrict__ xq, float *__restrict__ sx) {
-    __shared__ uint32_t wmax[4];
+template <int CPT, bool BF16, int NT>
+__global__ __launch_bounds__(NT) void quantize_rows_wg_kernel(const uint16_t *__restrict__ x, int64_t ldx, int K,
+                                                               int8_t *__restrict__ xq, float *__restrict__ sx) {
+    __shared__ uint32_t wmax[NT / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = blockIdx.x;
     const uint16_t *row = x + (int64_t)m * ldx;
@@ -111,31 +114,32 @@ __global__ __launch_bounds__(256) void quantize_rows_wg_kernel(const uint16_t *_
     u16x2 m2 = {0, 0};
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const int c = tid + 256 * j;
+        const int c = tid + NT * j;
         cache[j] = c < nch ? *reinterpret_cast<const uint4 *>(row + 8 * c) : make_uint4(0, 0, 0, 0);
         m2 = absmax8(cache[j], m2);
     }
-    for (int c = tid + 256 * CPT; c < nch; c += 256) m2 = absmax8(*reinterpret_cast<const uint4 *>(row + 8 * c), m2);
+    for (int c = tid + NT * CPT; c < nch; c += NT) m2 = absmax8(*reinterpret_cast<const uint4 *>(row + 8 * c), m2);
     uint32_t amax = wave_max_u32(m2.x > m2.y ? m2.x : m2.y);
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
-    amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) amax = max(amax, wmax[w]);
 
     const float s = row_scale<BF16>(amax);
     if (tid == 0) sx[m] = s;
     if (s == 0.0f) {
-        for (int c = tid; c < nch; c += 256) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
+        for (int c = tid; c < nch; c += NT) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
         return;
     }
     const bool fast = s >= kMinFastScale;
     const float r = fast ? 1.0f / s : 0.f;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const int c = tid + 256 * j;
+        const int c = tid + NT * j;
         if (c < nch)
             *reinterpret_cast<uint2 *>(qrow + 8 * c) = fast ? quant8<BF16, true>(cache[j], s, r) : quant8<BF16, false>(cache[j], s, r);
     }
-    for (int c = tid + 256 * CPT; c < nch; c += 256) {
+    for (int c = tid + NT * CPT; c < nch; c += NT) {
         const uint4 v = *reinterpret_cast<const uint4 *>(row + 8 * c);
         *reinterpret_cast<uint2 *>(qrow + 8 * c) = fast ? quant8<BF16, true>(v, s, r) : quant8<BF16, false>(v, s, r);
     }
@@ -149,11 +153,16 @@ hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, flo
     if (K >= kRowsPerWorkgroupK) {
         const int per_thread = (nch + 255) / 256;
         if (per_thread <= 4)
-            hipLaunchKernelGGL((quantize_rows_wg_kernel<4, BF16>), dim3(M), dim3(256), 0, stream, xp, ldx, K, xq, sx);
+            hipLaunchKernelGGL((quantize_rows_wg_kernel<4, BF16, 256>), dim3(M), dim3(256), 0, stream, xp, ldx, K, xq, sx);
         else if (per_thread <= 6)
-            hipLaunchKernelGGL((quantize_rows_wg_kernel<6, BF16>), dim3(M), dim3(256), 0, stream, xp, ldx, K, xq, sx);
+            hipLaunchKernelGGL((quantize_rows_wg_kernel<6, BF16, 256>), dim3(M), dim3(256), 0, stream, xp, ldx, K, xq, sx);
         else
-            hipLaunchKernelGGL((quantize_rows_wg_kernel<8, BF16>), dim3(M), dim3(256), 0, stream, xp, ldx, K, xq, sx);
+            hipLaunchKernelGGL((quantize_rows_wg_kernel<8, BF16, 256>), dim3(M), dim3(256), 0, stream, xp, ldx, K, xq, sx);
+        return hipGetLastError();
+    }
+    if (K >= kRowsPerPairK) {
+        // two waves per row
+        hipLaunchKernelGGL((quantize_rows_wg_kernel<4, BF16, 128>), dim3(M), dim3(128), 0, stream, xp, ldx, K, xq, sx);
         return hipGetLastError();
     }
     const int per_lane = (nch + 63) / 64;
