@@ -307,18 +307,20 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
 }
 
 constexpr int SD_COMBINE_THREADS = 1024;
+constexpr int SD_COMBINE_SPLIT = 4;  // workgroups per head in the merge (4: GQA 32/4, N = 32768: 17.7 against 18.6 us with 1)
 
 // Second pass: merge the slices of one (b, h). Thread (d, part) of 1024 merges every PARTS-th
 // slice's (m, l, o[d]) into a running (M, L, A), eight slices at a time: their loads go out
 // together, then the running sums are rescaled once to the new maximum. The PARTS states then
 // meet in LDS.
-template <int D>
-__global__ __launch_bounds__(SD_COMBINE_THREADS) void sdpa_combine_kernel(const float *part, void *o, int slices,
-                                                                          int out) {
-    constexpr int PARTS = SD_COMBINE_THREADS / D;
-    __shared__ float st[3][PARTS][D];
+template <int D, int SPLIT>
+__global__ __launch_bounds__(SD_COMBINE_THREADS / SPLIT) void sdpa_combine_kernel(const float *part, void *o,
+                                                                                  int slices, int out) {
+    // SPLIT workgroups per head, each merging D / SPLIT columns with PARTS slice streams
+    constexpr int PARTS = SD_COMBINE_THREADS / D, DC = D / SPLIT;
+    __shared__ float st[3][PARTS][DC];
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const int d = tid % D, pt = tid / D;
+    const int dc = tid % DC, pt = tid / DC, d = blockIdx.y * DC + dc;
     const float *pp = part + (int64_t)bh * slices * (D + 4);
     float M = -INFINITY, L = 0.f, A = 0.f;
     for (int s0 = pt; s0 < slices; s0 += 8 * PARTS) {
@@ -349,21 +351,21 @@ __global__ __launch_bounds__(SD_COMBINE_THREADS) void sdpa_combine_kernel(const 
         }
         M = mx;
     }
-    st[0][pt][d] = M;
-    st[1][pt][d] = L;
-    st[2][pt][d] = A;
+    st[0][pt][dc] = M;
+    st[1][pt][dc] = L;
+    st[2][pt][dc] = A;
     __syncthreads();
     if (pt != 0) return;
     float Mx = M;
 #pragma unroll
-    for (int q = 1; q < PARTS; ++q) Mx = fmaxf(Mx, st[0][q][d]);
+    for (int q = 1; q < PARTS; ++q) Mx = fmaxf(Mx, st[0][q][dc]);
     float Lt = 0.f, At = 0.f;
 #pragma unroll
     for (int q = 0; q < PARTS; ++q) {
-        const float mq = st[0][q][d];
+        const float mq = st[0][q][dc];
         const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - Mx);
-        Lt += st[1][q][d] * f;
-        At += st[2][q][d] * f;
+        Lt += st[1][q][dc] * f;
+        At += st[2][q][dc] * f;
     }
     const float y = At / Lt;
     const int64_t off = (int64_t)bh * D + d;
@@ -380,8 +382,8 @@ hipError_t launch_sdpa_t(const SdpaArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((sdpa_kernel<D, BF16>), dim3(a.slices, a.B * a.Hkv), dim3(64 * SD_WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.slices == 1) return e;
-    hipLaunchKernelGGL((sdpa_combine_kernel<D>), dim3(a.B * a.Hq), dim3(SD_COMBINE_THREADS), 0, stream, a.part, a.o,
-                       a.slices, a.out);
+    hipLaunchKernelGGL((sdpa_combine_kernel<D, SD_COMBINE_SPLIT>), dim3(a.B * a.Hq, SD_COMBINE_SPLIT),
+                       dim3(SD_COMBINE_THREADS / SD_COMBINE_SPLIT), 0, stream, a.part, a.o, a.slices, a.out);
     return hipGetLastError();
 }
 
