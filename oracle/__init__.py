@@ -51,13 +51,15 @@ def _load():
         lib.oracle_group_acc.argtypes = [vp, vp, i64, i64, i64, i32, vp]
         lib.oracle_dequant_pc.argtypes = [vp, vp, vp, i64, i64, vp]
         lib.oracle_dequant_pg.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.oracle_dequant_pc_f32.argtypes = [vp, vp, vp, i64, i64, vp]
+        lib.oracle_dequant_pg_f32.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         lib.oracle_mv.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, i32, vp, vp]
         lib.oracle_quantize_weight_clipped.argtypes = [vp, i64, i64, i32, i32, ctypes.c_float, vp, vp]
         lib.oracle_sdpa_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, ctypes.c_double, vp, vp, vp]
         lib.oracle_rmsnorm_quantize.argtypes = [vp, i32, vp, i32, ctypes.c_double, i64, i64, i64, vp, vp, vp]
         for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
                   lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
-                  lib.oracle_dequant_pg, lib.oracle_mv, lib.oracle_quantize_weight_clipped,
+                  lib.oracle_dequant_pg, lib.oracle_dequant_pc_f32, lib.oracle_dequant_pg_f32, lib.oracle_mv, lib.oracle_quantize_weight_clipped,
                   lib.oracle_sdpa_decode, lib.oracle_rmsnorm_quantize):
             f.restype = ctypes.c_int
         _lib = lib
@@ -207,30 +209,59 @@ def dequant_pg(acc_g: np.ndarray, s_x: np.ndarray, s_w: np.ndarray):
     return y, mag
 
 
+def dequant_pc_f32(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray):
+    """fp32 y32 [M, N] = ((float)acc * s_x[m]) * s_w[n], each product rounded to fp32."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    M, N = acc.shape
+    y = np.empty((M, N), np.float32)
+    _check(_load().oracle_dequant_pc_f32(_p(acc), _p(s_x), _p(s_w), M, N, _p(y)), "dequant_pc_f32")
+    return y
+
+
+def dequant_pg_f32(acc_g: np.ndarray, s_x: np.ndarray, s_w: np.ndarray):
+    """fp32 y32 [M, N]: t = fmaf((float)acc_g, s_w[n, g], t) over g ascending from +0, then t * s_x[m]."""
+    acc_g = np.ascontiguousarray(acc_g, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    M, N, G = acc_g.shape
+    y = np.empty((M, N), np.float32)
+    _check(_load().oracle_dequant_pg_f32(_p(acc_g), _p(s_x), _p(s_w), M, N, G, _p(y)), "dequant_pg_f32")
+    return y
+
+
 # ---- whole-path conveniences (the steps above, in the pages' order) --------------------
 
 def linear_pc(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray):
     """Per-channel W8A8 linear: quantize x per token, int GEMM, dequant.
 
-    Returns dict with x_q, s_x, acc (int32) and y (fp64).
+    Returns dict with x_q, s_x, acc (int32), y (fp64) and y32 (the fp32 evaluation the
+    output format is rounded from).
     """
     x_q, s_x = quantize_per_token(x)
     acc = gemm_i32(x_q, w_q)
-    return {"x_q": x_q, "s_x": s_x, "acc": acc, "y": dequant_pc(acc, s_x, s_w)}
+    return {"x_q": x_q, "s_x": s_x, "acc": acc, "y": dequant_pc(acc, s_x, s_w),
+            "y32": dequant_pc_f32(acc, s_x, s_w)}
 
 
 def linear_pg(x: np.ndarray, w_q: np.ndarray, s_w: np.ndarray, group_size: int):
-    """Per-group W8A8 linear. Returns x_q, s_x, acc (sum of group accumulators), y, mag."""
+    """Per-group W8A8 linear. Returns x_q, s_x, acc (sum of group accumulators), y (fp64),
+    mag and y32 (the fp32 fold in K order the output format is rounded from)."""
     x_q, s_x = quantize_per_token(x)
     acc_g = group_acc(x_q, w_q, group_size)
     y, mag = dequant_pg(acc_g, s_x, s_w)
     acc = acc_g.astype(np.int64).sum(axis=2).astype(np.int32)
-    return {"x_q": x_q, "s_x": s_x, "acc": acc, "acc_g": acc_g, "y": y, "mag": mag}
+    return {"x_q": x_q, "s_x": s_x, "acc": acc, "acc_g": acc_g, "y": y, "mag": mag,
+            "y32": dequant_pg_f32(acc_g, s_x, s_w)}
 
 
 def linear_w4(x: np.ndarray, w_packed: np.ndarray, s_w: np.ndarray, group_size: int):
-    """W4A8 per-group linear: unpack the int4 codes, then the per-group path."""
+    """W4A8 linear: unpack the int4 codes, then the per-group path (group_size 64 / 128) or,
+    for group_size 0 (one scale per output channel), the per-channel path."""
     K = x.shape[1]
+    if group_size == 0:
+        return linear_pc(x, unpack_int4(w_packed, K), s_w)
     return linear_pg(x, unpack_int4(w_packed, K), s_w, group_size)
 
 

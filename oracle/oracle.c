@@ -31,9 +31,13 @@
  *    two per byte, even k in the low nibble;
  *  - the int8 GEMM is exact integer arithmetic (accumulated here in int64 and
  *    checked to fit in int32);
- *  - dequantization is evaluated in fp64 (the exact value to within fp64
- *    rounding); per-channel as (acc * s_x) * s_w, per-group as
- *    s_x * sum_g s_w[n,g] * acc_g with acc_g the int32 sum over group g.
+ *  - dequantization is given twice: in fp64 (the exact value to within fp64
+ *    rounding; per-channel (acc * s_x) * s_w, per-group s_x * sum_g s_w[n,g] * acc_g
+ *    with acc_g the int32 sum over group g), and in the pages' fp32 arithmetic
+ *    (per-channel two fp32 products left to right; per-group one fp32 fused
+ *    multiply-add per group in K order, then the token scale), the value an fp16 /
+ *    bf16 output is rounded from;
+ *  - int4 weights are per group or, with group size 0, per output channel.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  * Parallelism: an OpenMP "parallel for" over independent rows only.
@@ -140,6 +144,8 @@ int oracle_quantize_per_token(const uint16_t *x, int x_is_bf16, int64_t M, int64
  *  bits 8, group_size g>0  : s_w [N, K/g],   w_q int8 [N, K]   (groups along K)
  *  bits 4, group_size g>0  : s_w [N, K/g],   w_q uint8 [N, K/2]; u = q + 8,
  *                            byte j = u[2j] | u[2j+1] << 4 (even k low nibble)
+ *  bits 4, group_size 0    : s_w [N],        w_q uint8 [N, K/2]; the per-column int4 of
+ *                            P5 "量化" (one scale per output channel), same packing
  */
 int oracle_quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_size,
                            void *w_q, float *s_w)
@@ -147,7 +153,7 @@ int oracle_quantize_weight(const float *W, int64_t N, int64_t K, int bits, int g
     if (N < 0 || K <= 0) return ORACLE_BAD_ARG;
     if (bits != 8 && bits != 4) return ORACLE_BAD_ARG;
     if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return ORACLE_BAD_ARG;
-    if (bits == 4 && (group_size == 0 || group_size % 2 != 0)) return ORACLE_BAD_ARG;
+    if (bits == 4 && (K % 2 != 0 || group_size % 2 != 0)) return ORACLE_BAD_ARG;
     const int64_t run = group_size ? group_size : K;
     const int64_t G = K / run;
     const float qdiv = bits == 8 ? 127.0f : 7.0f;
@@ -276,6 +282,50 @@ int oracle_dequant_pg(const int32_t *acc_g, const float *s_x, const float *s_w, 
 }
 
 /*
+ * Per-channel dequant in the pages' own precision [P5 "量化": fp32 scales, INT32 accumulation,
+ * C = C_int32 * s_act * s_weight, read left to right]: the int32 sum is converted to fp32
+ * (round to nearest even), then multiplied by s_x[m] and by s_w[n], each product rounded to
+ * fp32 on its own:
+ *   y32[m, n] = ((float)acc[m, n] * s_x[m]) * s_w[n]
+ * This is the fp32 value an fp16 / bf16 output is rounded from (once, to nearest even).
+ */
+int oracle_dequant_pc_f32(const int32_t *acc, const float *s_x, const float *s_w, int64_t M, int64_t N,
+                          float *y32)
+{
+    if (M < 0 || N < 0) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const float a = (float)acc[m * N + n];
+            const float t = a * s_x[m];
+            y32[m * N + n] = t * s_w[n];
+        }
+    return ORACLE_OK;
+}
+
+/*
+ * Per-group dequant in fp32 [P2 "三种量化粒度的实现": per group its own weight scale, so the
+ * dequantization is a segmented multiplication; P5 "量化": fp32 scales]. The segments are
+ * folded in K order, each with one correctly rounded fused multiply-add, and the token scale
+ * is applied last:
+ *   t = +0; for g = 0 .. G-1: t = fmaf((float)acc_g[m, n, g], s_w[n, g], t);  y32 = t * s_x[m]
+ */
+int oracle_dequant_pg_f32(const int32_t *acc_g, const float *s_x, const float *s_w, int64_t M, int64_t N,
+                          int64_t G, float *y32)
+{
+    if (M < 0 || N < 0 || G <= 0) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float t = 0.0f;
+            for (int64_t g = 0; g < G; ++g)
+                t = fmaf((float)acc_g[(m * N + n) * G + g], s_w[n * G + g], t);
+            y32[m * N + n] = t * s_x[m];
+        }
+    return ORACLE_OK;
+}
+
+/*
  * Decode matrix-vector product with the activations as they are [P5 "Metal Kernel 流水线",
  * decode (M = 1): the int8 matrix-vector kernel dequantizes the weights as it goes and
  * quantizes no activation; P2 "INT8 TensorOps 内核设计", the two paths: seq_len = 1 takes
@@ -333,7 +383,7 @@ int oracle_quantize_weight_clipped(const float *W, int64_t N, int64_t K, int bit
     if (N < 0 || K <= 0) return ORACLE_BAD_ARG;
     if (bits != 8 && bits != 4) return ORACLE_BAD_ARG;
     if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return ORACLE_BAD_ARG;
-    if (bits == 4 && (group_size == 0 || group_size % 2 != 0)) return ORACLE_BAD_ARG;
+    if (bits == 4 && (K % 2 != 0 || group_size % 2 != 0)) return ORACLE_BAD_ARG;
     if (!(pct > 0.0f && pct <= 100.0f)) return ORACLE_BAD_ARG;
     const int64_t run = group_size ? group_size : K;
     const int64_t G = K / run;

@@ -313,6 +313,101 @@ def test_w4_path_equals_pg_on_unpacked_codes():
     assert (r4["acc"] == r8["acc"]).all() and (r4["y"] == r8["y"]).all()
 
 
+def test_golden_w4_per_column():
+    """Per-column int4 (group size 0): one scale per output channel, the same nibble packing."""
+    d = _golden("w4_per_column.json")
+    W = np.array(d["W"], np.float32)
+    packed, s = oracle.quantize_weight(W, 4, 0)
+    assert s.tolist() == d["scale"]
+    assert packed.tolist() == d["packed"]
+    assert oracle.unpack_int4(packed, W.shape[1]).tolist() == d["codes"]
+
+
+def test_w4_per_column_against_exact_rows_and_pc_path():
+    rng = np.random.default_rng(13)
+    W = (rng.standard_normal((6, 320)) * 0.02).astype(np.float32)
+    W[2, 17] = 0.3  # an outlier sets its whole row's scale
+    W[4] = 0.0      # an all-zero row: scale 0, codes 0
+    packed, sw = oracle.quantize_weight(W, 4, 0)
+    codes = oracle.unpack_int4(packed, 320)
+    assert sw.shape == (6,) and codes.min() >= -7 and codes.max() <= 7
+    for n in range(6):
+        es, ec = exact_quantize(W[n], qdiv=7, lo=-8, hi=7)
+        assert float(sw[n]) == es and codes[n].tolist() == ec
+    # the per-column W4 linear is the per-channel path on the unpacked codes: integer sums
+    # against numpy's int64 product, outputs against an fp64 fake-quant matmul
+    x = rng.standard_normal((5, 320)).astype(np.float16)
+    r = oracle.linear_w4(x, packed, sw, 0)
+    assert (r["acc"] == r["x_q"].astype(np.int64) @ codes.astype(np.int64).T).all()
+    fq = (r["s_x"][:, None].astype(np.float64) * r["x_q"]) @ (sw[:, None].astype(np.float64) * codes).T
+    np.testing.assert_allclose(r["y"], fq, rtol=1e-12, atol=1e-12)
+
+
+# ---- dequantization in the pages' fp32 arithmetic ---------------------------------------
+# Plausible mistakes caught: a swapped multiply order or a fused (single-rounding) product
+# in the per-channel epilogue, an int32 -> fp32 conversion that truncates, a per-group fold
+# in another order or with separate multiply and add roundings, a missing token scale.
+
+def test_dequant_pc_f32_exact_rational_model():
+    rng = np.random.default_rng(21)
+    acc = rng.integers(-2 ** 30, 2 ** 30, (9, 11)).astype(np.int32)  # most need rounding to fp32
+    acc[0, :4] = [0, 1, -(2 ** 24) - 1, 2 ** 24 + 3]
+    sx = (rng.random(9) * np.exp2(rng.integers(-20, 4, 9))).astype(np.float32)
+    sw = (rng.random(11) * np.exp2(rng.integers(-12, 2, 11))).astype(np.float32)
+    y32 = oracle.dequant_pc_f32(acc, sx, sw)
+    assert y32.dtype == np.float32
+    swapped = 0
+    for m in range(9):
+        for n in range(11):
+            a = round_to_f32(Fraction(int(acc[m, n])))
+            t = round_to_f32(a * Fraction(float(sx[m])))
+            ref = round_to_f32(t * Fraction(float(sw[n])))
+            assert Fraction(float(y32[m, n])) == ref, (m, n)
+            swapped += round_to_f32(round_to_f32(a * Fraction(float(sw[n]))) * Fraction(float(sx[m]))) != ref
+    assert swapped > 0  # the inputs tell the two multiply orders apart
+
+
+def _fma_chain_exact(accs, scales, sx):
+    t = Fraction(0)
+    for a, s in zip(accs, scales):
+        t = round_to_f32(round_to_f32(Fraction(int(a))) * Fraction(float(s)) + t)  # one rounding per fma
+    return round_to_f32(t * Fraction(float(sx)))
+
+
+def test_dequant_pg_f32_exact_rational_chain():
+    rng = np.random.default_rng(22)
+    G = 7
+    accg = rng.integers(-2 ** 27, 2 ** 27, (4, 5, G)).astype(np.int32)
+    sx = (rng.random(4) + 0.05).astype(np.float32)
+    sw = (rng.random((5, G)) * 1e-3).astype(np.float32)
+    sw[1, 3] = 0.0  # an all-zero group's scale
+    y32 = oracle.dequant_pg_f32(accg, sx, sw)
+    for m in range(4):
+        for n in range(5):
+            assert Fraction(float(y32[m, n])) == _fma_chain_exact(accg[m, n], sw[n], sx[m]), (m, n)
+
+
+def test_dequant_pg_f32_folds_in_k_order_and_stays_in_the_fp32_bound():
+    # groups [2^24, 1, -2^24] at unit scales: ascending, 2^24 + 1 rounds to 2^24 (ties to even)
+    # and the last group cancels it (0); descending would give -2^24 + 1 + 2^24 = 1
+    accg = np.array([[[2 ** 24, 1, -(2 ** 24)]]], np.int32)
+    assert oracle.dequant_pg_f32(accg, np.ones(1, np.float32), np.ones((1, 3), np.float32))[0, 0] == 0.0
+    # on the workload's distributions: within the fp32 evaluation bound (G fmas and one
+    # multiply, each a relative 2^-24 of the running magnitude) of the fp64 value
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((16, 512)) * 2).astype(np.float16)
+    W = (rng.standard_normal((24, 512)) * 0.02).astype(np.float32)
+    for gs in (64, 128):
+        wq, sw = oracle.quantize_weight(W, 8, gs)
+        r = oracle.linear_pg(x, wq, sw, gs)
+        G = 512 // gs
+        assert (np.abs(r["y32"].astype(np.float64) - r["y"]) <= (G + 1) * 2.0 ** -24 * r["mag"] + 1e-300).all()
+    # per channel: three roundings (conversion and two products) of the exact value
+    wq, sw = oracle.quantize_weight(W, 8, 0)
+    r = oracle.linear_pc(x, wq, sw)
+    assert (np.abs(r["y32"].astype(np.float64) - r["y"]) <= 3 * 2.0 ** -24 * np.abs(r["y"])).all()
+
+
 # ---- decode matrix-vector product without activation quantization (linear_mv) ----------
 # Plausible mistakes caught: a quantized activation slipping in (one-hot and exact
 # rational sums), a wrong group index for the weight scale (per-slice rational brute
@@ -596,3 +691,30 @@ def test_rmsnorm_quantize_reconstructs_the_normalized_row():
     # half a step, plus the fp32 roundings of x g and of the quotient (each <= 127 * 2^-24 steps)
     assert (err <= sx[:, None] * (0.5 + 2 * 127 * 2.0 ** -24)).all()
     assert (np.abs(q).max(axis=1) == 127).all()
+
+
+def test_rmsnorm_quantize_codes_equal_quantize_of_the_fp64_norm():
+    """Pins the fold itself against the unfolded definition: numpy's fp64 RMSNorm
+    n = x g / sqrt(mean x^2 + eps), quantized per token in fp64 (s = max|n| / 127,
+    q = rint(n / s)), gives the oracle's codes on every row where no quotient n / s lies
+    within 2^-13 of a half-integer. The oracle's quotient u / s_u (u = x g is exact in fp32
+    for fp16 or bf16 factors: at most 22 significant bits) carries two fp32 roundings of
+    relative size 2^-24 each, so it moves a quotient of magnitude <= 127 by less than
+    2^-16; outside the band both round to the same integer."""
+    rng = np.random.default_rng(41)
+    M, K = 300, 256
+    x = rng.standard_normal((M, K))
+    x[:, rng.choice(K, 3, replace=False)] *= 50  # outlier channels
+    x = (x * np.exp2(rng.integers(-6, 6, (M, 1)))).astype(np.float16)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+    for eps in (0.0, 1e-6, 0.5):
+        xq, su, sx = oracle.rmsnorm_quantize(x, g, eps)
+        xf = x.astype(np.float64)
+        n = xf * g.astype(np.float64) / np.sqrt((xf * xf).mean(axis=1, keepdims=True) + eps)
+        s = np.abs(n).max(axis=1) / 127.0
+        t = n / s[:, None]
+        near = np.abs(np.abs(t - np.floor(t)) - 0.5) < 2.0 ** -13
+        ok = ~near.any(axis=1)
+        assert ok.sum() >= 0.8 * M
+        assert (xq[ok] == np.rint(t[ok])).all()
+        np.testing.assert_allclose(sx, s, rtol=2.0 ** -20)
