@@ -53,3 +53,28 @@ def check_output(y_gpu: np.ndarray, fmt: str, y64: np.ndarray, mag: np.ndarray, 
         exact = (y_gpu == y64.astype(np.float16)).mean()
         assert exact >= 0.99, f"{what}: only {exact:.4f} of fp16 outputs are RNE(y64)"
     return float(err.max()) if err.size else 0.0
+
+
+def bf16_rne_bits(f32: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def check_exact(y_gpu: np.ndarray, fmt: str, y32: np.ndarray, what: str = ""):
+    """Bit-for-bit equality with the oracle's fp32 evaluation rounded once to the output
+    format (fp16 by numpy's round-to-nearest-even conversion, bf16 by bf16_rne_bits, fp32
+    as is). y_gpu: float16 (f16), uint16 bf16 bits (bf16) or float32 (f32)."""
+    if fmt == "f16":
+        got, ref = y_gpu.view(np.uint16), y32.astype(np.float16).view(np.uint16)
+    elif fmt == "bf16":
+        got, ref = y_gpu.view(np.uint16), bf16_rne_bits(y32)
+    elif fmt == "f32":
+        got, ref = y_gpu.view(np.uint32), np.ascontiguousarray(y32, dtype=np.float32).view(np.uint32)
+    else:
+        raise ValueError(fmt)
+    bad = got != ref
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outputs differ from the oracle's fp32 "
+                             f"evaluation; first at {i}: gpu bits {int(got[i]):#x}, oracle {int(ref[i]):#x}")

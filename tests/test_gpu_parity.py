@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import oracle
-from synth_inputs import linear_inputs, qwen3_8b_block_inputs, QWEN3_8B_BLOCK, QWEN3_8B_BLOCK_INPUTS
-from _parity import check_output
+from synth_inputs import linear_inputs
+from _parity import check_exact, check_output
 
 pytestmark = pytest.mark.gpu
 
@@ -173,11 +173,18 @@ def oracle_mode(mode, x, W):
 
 
 def compare(yt, r, what):
+    """int32 sums bit-exact; outputs within the fp32 evaluation bound of the fp64 value and,
+    for every kernel that folds in the pages' fp32 order (all but the per-group GEMV that
+    M <= 16 runs, which splits a row's K range over waves), bit-exact against the oracle's
+    fp32 evaluation rounded once to the output format."""
     if yt.dtype == torch.int32:
         got = host(yt)
         assert (got == r["acc"]).all(), f"{what}: int32 accumulators differ"
         return
-    check_output(host(yt), OUT_FMT[yt.dtype], r["y"], r["mag"], r["G"], what)
+    got = host(yt)
+    check_output(got, OUT_FMT[yt.dtype], r["y"], r["mag"], r["G"], what)
+    if r["G"] == 1 or got.shape[0] > 16:
+        check_exact(got, OUT_FMT[yt.dtype], r["y32"], what)
 
 
 SHAPES = [(37, 272, 384), (300, 1040, 2560), (128, 512, 640), (1, 16, 128), (65, 48, 256), (513, 272, 1280),
@@ -252,46 +259,23 @@ def test_every_config_identical(w8a8, mode):
             assert (y.view(np.uint8) == ys[0].view(np.uint8)).all(), f"configs differ ({out})"
 
 
-# ---- full workload sizes (the benchmark's launch configuration), sampled -------------------
-
-def sample_rows(M, n=40, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = {0, M - 1, M // 2}
-    rows.update(rng.choice(M, min(n, M), replace=False).tolist())
-    return np.array(sorted(rows))
-
+# ---- shapes that route to specific tile configurations, at full size, every row --------
+# (the points of the workload definitions themselves are in test_gpu_fullsize.py)
 
 @pytest.mark.parametrize("mode,M,N,K", [
-    ("pc", 128, 10240, 2560),
-    ("pc", 4096, 10240, 2560),
-    ("pc", 8192, 2560, 10240),
-    ("pc", 1, 10240, 2560),
-    ("pc", 1024, 2560, 10240),
     ("pc", 2048, 1024, 4096),     # 64 x 128 tiles, one round (Qwen3 k/v shape)
     ("pc", 1536, 2560, 10240),    # 128 x 128 tiles, one round
     ("pg128", 768, 2560, 10240),  # 64 x 64 per-group DMA tiles
-    ("pg128", 4096, 10240, 2560),
-    ("pg64", 8192, 2560, 10240),
-    ("pg64", 128, 10240, 2560),
-    ("w4_128", 1, 10240, 2560),
-    ("w4_128", 1024, 10240, 2560),
-    ("w4_128", 4096, 10240, 2560),
 ])
-def test_full_size_sampled(w8a8, mode, M, N, K):
+def test_full_size_config_shapes(w8a8, mode, M, N, K):
     note(f"full size {mode} M={M} N={N} K={K}")
     x, W = linear_inputs(M, N, K, seed=0)
-    rows = sample_rows(M)
-    # codes and scales of every row
     xq, sx = gpu_quantize(w8a8, x)
     rq, rs = oracle.quantize_per_token(x)
     assert (xq == rq).all() and (sx.view(np.uint32) == rs.view(np.uint32)).all()
-    r = oracle_mode(mode, x[rows], W)
+    r = oracle_mode(mode, x, W)
     for out in (torch.float16, torch.int32):
-        y = host(run_mode(w8a8, mode, x, W, out))
-        if out == torch.int32:
-            assert (y[rows] == r["acc"]).all(), "int32 accumulators differ"
-        else:
-            check_output(y[rows], "f16", r["y"], r["mag"], r["G"], f"{mode} {M}x{N}x{K}")
+        compare(run_mode(w8a8, mode, x, W, out), r, f"{mode} {M}x{N}x{K} {out}")
 
 
 def _bf16_rne_bits(f32: np.ndarray) -> np.ndarray:
@@ -325,26 +309,6 @@ def test_pc_epilogue_rounding_exact(w8a8, M, N, K, cfgs):
             assert (yf.view(np.uint32) == y32.view(np.uint32)).all(), f"config {cfg}: fp32 output differs"
     finally:
         w8a8.w8a8_debug_force_config(-1)
-
-
-def test_qwen3_block_sampled(w8a8):
-    """One Qwen3-8B-shaped block's seven linears at M=2048, per-channel, bf16 output."""
-    inputs, weights = qwen3_8b_block_inputs(M=2048, seed=0)
-    rows = sample_rows(2048, n=24)
-    for in_name, K, projs in QWEN3_8B_BLOCK_INPUTS:
-        x = inputs[in_name]
-        xq, sx = w8a8.quantize_per_token(dev(x))
-        xq_o, sx_o = oracle.quantize_per_token(x)
-        assert (host(xq) == xq_o).all() and (host(sx) == sx_o).all()
-        for name in projs:
-            note(f"qwen3 block {name}")
-            W = weights[name]
-            wq, sw = w8a8.quantize_weight(dev(W), 8, 0)
-            y = host(w8a8.w8a8_gemm_pc(xq, sx, wq, sw, torch.bfloat16))
-            torch.cuda.synchronize()
-            owq, osw = oracle.quantize_weight(W, 8, 0)
-            r = oracle.linear_pc(x[rows], owq, osw)
-            check_output(y[rows], "bf16", r["y"], np.abs(r["y"]), 1, f"qwen3 {name}")
 
 
 def test_concatenated_projections_equal_separate(w8a8):
