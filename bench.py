@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="pc", choices=sorted(WORKLOADS) + ["qwen3", "mv", "mvg128", "sdpa", "rmsnorm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-m1", action="store_true", help="leave the fused M=1 results out of the default line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle sample")
     ap.add_argument("--copy-ref-mb", type=int, default=0,
@@ -281,12 +282,56 @@ def rmsnorm_bench(args, torch, w8a8):
     return result
 
 
-def timed_steps(args, torch, step):
+CLOCK = {}  # engine clock over the last timed region (clock_record), for the JSON line
+
+
+def clock_record(torch, before, after):
+    """Mean engine clock (MHz) between two clock probes, per compute unit that both probes
+    visited (both counters of a pair read on one compute unit): 100 MHz times the ratio of the
+    shader-clock and 100 MHz counter differences; median, p10 and p90 over those units."""
+    def firsts(t):
+        a = t.cpu().numpy().reshape(-1, 4)
+        d = {}
+        for loc, sclk, ref, _ in a:
+            # XCC id and the HW_ID fields that name a compute unit (CU, shader array, engine)
+            key = (int(loc) >> 32, (int(loc) >> 8) & 0xFF)
+            d.setdefault(key, (int(sclk), int(ref)))
+        return d
+    b, a = firsts(before), firsts(after)
+    mhz = [100.0 * (a[k][0] - b[k][0]) / (a[k][1] - b[k][1]) for k in b if k in a and a[k][1] > b[k][1]]
+    if not mhz:
+        return None
+    return {"median_mhz": float(np.median(mhz)), "p10_mhz": float(np.percentile(mhz, 10)),
+            "p90_mhz": float(np.percentile(mhz, 90)), "units": len(mhz),
+            "interval_us": float(np.median([a[k][1] - b[k][1] for k in b if k in a])) / 100.0,
+            "how": "s_memtime against s_memrealtime on each compute unit, probes right before and after "
+                   "the host-timed replay"}
+
+
+def step_distribution(torch, step, n, first):
+    """Per-step times (ms) of n steps issued one by one, an event recorded after each: p10,
+    median and p90. A second pass after the timed replay, not the timed steps themselves."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        step(first + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    return {"p10_ms": float(np.percentile(d, 10)), "p50_ms": float(np.percentile(d, 50)),
+            "p90_ms": float(np.percentile(d, 90)), "n": n,
+            "how": "events between eagerly issued steps, after the timed replay"}
+
+
+def timed_steps(args, torch, step, w8a8=None):
     """Warmup, then args.steps steps replayed as one captured graph (or issued one by one
     with --no-graph). Returns (ms per step by the host clock, ms per step by events or
     None). The graph is captured after the first few warmup steps (the rest run right
     before the timed replay, so the GPU does not sit idle during the capture between the
-    warmup and the timed steps)."""
+    warmup and the timed steps). With w8a8 given, clock probes on the replay's stream
+    bracket the timed region and CLOCK holds the engine clock over it."""
+    CLOCK.clear()
     if args.no_graph:
         for i in range(args.warmup):
             step(i)
@@ -308,14 +353,26 @@ def timed_steps(args, torch, step):
     for i in range(first, args.warmup):
         step(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probes = [torch.zeros(4096, dtype=torch.int64, device="cuda") for _ in range(2)] if w8a8 else None
+    if probes:
+        w8a8.w8a8_debug_clock_probe(probes[1], stream=side)  # first launch (code load) outside the timing
     torch.cuda.synchronize()
+    if probes:
+        w8a8.w8a8_debug_clock_probe(probes[0], stream=side)  # enqueued before the host clock starts
     t0 = time.perf_counter()
     with torch.cuda.stream(side):
         e0.record()
         graph.replay()
         e1.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / args.steps, e0.elapsed_time(e1) / args.steps
+    host_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if probes:
+        w8a8.w8a8_debug_clock_probe(probes[1], stream=side)  # after the host clock stopped
+        torch.cuda.synchronize()
+        rec = clock_record(torch, probes[0], probes[1])
+        if rec:
+            CLOCK.update(rec)
+    return host_ms, e0.elapsed_time(e1) / args.steps
 
 
 def qwen3_block(args, torch, w8a8):
@@ -444,7 +501,33 @@ def main():
         print(json.dumps(mv_decode(args, torch, w8a8, 0 if args.workload == "mv" else 128)), flush=True)
         return 0
 
-    M, N, K, bits, gs = WORKLOADS[args.workload]
+    result = linear_bench(args, torch, w8a8, args.workload)
+    if args.workload == "pc" and not args.no_m1:
+        # the second bar of the target: the fused M = 1 layer (one kernel per step), weights
+        # streamed from HBM, int8 and int4 (gs = 128) weights
+        result["m1"] = {}
+        for name in ("m1", "m1w4"):
+            r = linear_bench(args, torch, w8a8, name)
+            ro = r["roofline"]
+            result["m1"][name] = {"M": 1, "N": r["config"]["N"], "K": r["config"]["K"],
+                                  "weight_bits": r["config"]["weight_bits"], "group_size": r["config"]["group_size"],
+                                  "us_per_step": r["ms_per_step"] * 1e3, "kernel_us": ro["launch_ms"] * 1e3,
+                                  "gbs": ro["achieved"], "frac_of_hbm": ro["frac"], "alg_bytes": ro["alg_bytes"],
+                                  "sclk": r.get("sclk")}
+    if not args.no_cpu_baseline:
+        M, N, K, bits, gs = WORKLOADS[args.workload]
+        x_np, W_np = linear_inputs(M, N, K, seed=0)
+        result["cpu_baseline"] = cpu_baseline(x_np, W_np, bits, gs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def linear_bench(args, torch, w8a8, workload):
+    """One w8a8 linear workload (quantize + GEMM, or the one-kernel layer for M <= 16):
+    the timed steps, the per-kernel launch times and the roofline of the dominant kernel."""
+    from synth_inputs import linear_inputs
+
+    M, N, K, bits, gs = WORKLOADS[workload]
     x_np, W_np = linear_inputs(M, N, K, seed=0)
     x = torch.from_numpy(x_np).cuda()
     Wd = torch.from_numpy(W_np).cuda()
@@ -495,7 +578,9 @@ def main():
     # loop); then the warmup and timed steps
     for i in range(len(copies) if len(copies) > 1 else 0):
         step(i)
-    ms_per_step, step_event_ms = timed_steps(args, torch, step)
+    ms_per_step, step_event_ms = timed_steps(args, torch, step, w8a8)
+    sclk = dict(CLOCK) or None
+    dist = None if fused else step_distribution(torch, step, min(args.steps, 200), args.warmup)
     if fused:
         quant_ms = gemm_ms = step_event_ms if step_event_ms is not None else launch_ms(step, stream)
     else:
@@ -516,13 +601,13 @@ def main():
         alg_bytes = wbytes + sw.numel() * 4 + M * K * 2 + M * N * 2  # weights + scales, x in, y out
         achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(workload),
                     "kernel": "fused quantize + GEMV + dequant (w8a8_linear, M <= 16)",
                     "launch_ms": kernel_ms, "alg_bytes": alg_bytes}
     else:
         achieved = ops / (gemm_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                    "frac": achieved / PEAK_INT8_TOPS, "traffic": measured_traffic(args.workload),
+                    "frac": achieved / PEAK_INT8_TOPS, "traffic": measured_traffic(workload),
                     "kernel": "gemm (int8 MFMA, fused per-channel dequant)", "launch_ms": gemm_ms}
 
     result = {
@@ -538,7 +623,7 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": f"w8a8 linear ({args.workload}): per-token quantize + int8 GEMM + fused dequant"
+        "config": {"workload": f"w8a8 linear ({workload}): per-token quantize + int8 GEMM + fused dequant"
                                + (" in one kernel" if fused else ""),
                    "M": M, "N": N, "K": K, "weight_bits": bits, "group_size": gs, "out": "fp16",
                    "parallelism": "single GPU"},
@@ -549,12 +634,13 @@ def main():
         "fused_ms": quant_ms if fused else None,
         "quantize_gbs": None if fused else (3.0 * M * K + 4 * M) / (quant_ms * 1e-3) / 1e9,
         "weight_copies": len(copies),
+        "sclk": sclk,
+        "step_times": dist,
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(x_np, W_np, bits, gs, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
-    return 0
+    return result
+
+
 
 
 if __name__ == "__main__":

@@ -281,6 +281,17 @@ int sdpa_decode(const void *q, const void *k, const void *v, int dtype, void *o,
 int w8a8_debug_force_splitk(int slices);
 
 /*
+ * Measurement aid: enqueues 1024 small workgroups; workgroup b stores where it ran,
+ * (XCC_ID << 32) | HW_ID (the XCD, and the compute unit, shader array and engine), the
+ * shader-clock counter (s_memtime, counting at the current engine clock) and the constant
+ * 100 MHz counter (s_memrealtime) to out[4 b], out[4 b + 1], out[4 b + 2] (out: device memory,
+ * 4096 uint64, 16-byte aligned, caller-owned; out[4 b + 3] is not written). Two probes on
+ * one stream around some work give the mean engine clock over it on each compute unit that
+ * both visited: 100 MHz * (shader-clock difference) / (100 MHz counter difference).
+ */
+int w8a8_debug_clock_probe(uint64_t *out, void *stream);
+
+/*
  * Debug knob: force the GEMM tile configuration (-1 = automatic choice by shape).
  * Every configuration computes identical results; tests use this to run each one.
  * Returns the number of configurations, or W8A8_ERR_INVALID_ARGUMENT (negated)

@@ -340,3 +340,10 @@ def test_sdpa_forced_unavailable_and_workspace_query(w8a8, unavailable):
     n = lib.sdpa_decode_workspace(1, 32, 4, 32768, 128)
     assert n > 0 and n % (32 * 132 * 4) == 0
     assert lib.sdpa_decode_workspace(1, 32, 3, 1024, 128) < 0
+
+
+def test_clock_probe_validation(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert lib.w8a8_debug_clock_probe(None, None) == INVALID
+    assert lib.w8a8_debug_clock_probe(ctypes.c_void_p(0x100008), None) == INVALID
+    assert lib.w8a8_debug_clock_probe(FAKE, None) == UNSUPPORTED_DEVICE

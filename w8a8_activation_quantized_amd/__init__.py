@@ -44,6 +44,7 @@ _SIGNATURES = {
     "w8a8_gemm_splitk": ([_vp, _vp, _vp, _vp, _int, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _vp],
                          _int),
     "w8a8_debug_force_splitk": ([_int], _int),
+    "w8a8_debug_clock_probe": ([_vp, _vp], _int),
     "int8_mv": ([_vp, _int, _i64, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "quantize_weight_clipped": ([_vp, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp, _vp], _int),
     "sdpa_decode_workspace": ([_i64, _i64, _i64, _i64, _i64], _i64),
@@ -106,6 +107,14 @@ def w8a8_debug_force_splitk(slices: int) -> None:
     rc = _lib.w8a8_debug_force_splitk(slices)
     if rc != 0:
         raise W8A8Error(-rc, f"bad slice count {slices}")
+
+
+def w8a8_debug_clock_probe(out: torch.Tensor, stream=None) -> None:
+    """Enqueue the clock probe: out (int64 [4096], device) receives per workgroup b its location
+    (XCC_ID << 32 | HW_ID), shader-clock and 100 MHz counters at out[4 b .. 4 b + 2]."""
+    if out.dtype != torch.int64 or out.numel() < 4096 or not out.is_cuda:
+        raise ValueError("out must be a device int64 tensor of at least 4096 elements")
+    _check(_lib.w8a8_debug_clock_probe(_ptr(out), _stream(stream)))
 
 
 def quantize_per_token(x: torch.Tensor, x_q: torch.Tensor | None = None,

@@ -338,7 +338,7 @@ int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, c
 }
 
 // Validation shared by the split-K query and call: weight_bits / group_size as for w8a8_linear.
-int check_split_kind(const char *fn, int weight_bits, int group_size) {
+static int check_split_kind(const char *fn, int weight_bits, int group_size) {
     if (weight_bits != 8 && weight_bits != 4)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: weight_bits must be 8 or 4", fn);
     if (group_size != 0 && group_size != 64 && group_size != 128)
@@ -348,7 +348,7 @@ int check_split_kind(const char *fn, int weight_bits, int group_size) {
     return W8A8_OK;
 }
 
-w8a8::SplitPlan current_split_plan(const w8a8::GemmProblem &p) {
+static w8a8::SplitPlan current_split_plan(const w8a8::GemmProblem &p) {
     return w8a8::splitk_plan(p, g_force_cfg.load(std::memory_order_relaxed),
                              g_force_slices.load(std::memory_order_relaxed));
 }
@@ -438,7 +438,7 @@ int int8_mv(const void *x, int x_dtype, int64_t ldx, const int8_t *w_q, const fl
 
 namespace {
 
-int check_sdpa(const char *fn, int dtype, int o_dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap,
+static int check_sdpa(const char *fn, int dtype, int o_dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap,
                int64_t D, float scale) {
     if (dtype != W8A8_F16 && dtype != W8A8_BF16)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: dtype must be F16 or BF16", fn);
@@ -526,6 +526,14 @@ int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const f
         return launched(w8a8::launch_gemm_splitk(p, plan, st), fn);
     }
     return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed), st), fn);
+}
+
+int w8a8_debug_clock_probe(uint64_t *out, void *stream) {
+    const char *fn = "w8a8_debug_clock_probe";
+    if (!out || !aligned16(out)) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: out must be a 16-byte aligned pointer", fn);
+    const int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    return launched(w8a8::launch_clock_probe(out, 1024, static_cast<hipStream_t>(stream)), fn);
 }
 
 int w8a8_debug_force_splitk(int slices) {

@@ -71,6 +71,10 @@ hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool 
                               int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes,
                               hipStream_t stream);
 
+// Measurement aid: `blocks` workgroups each store, at out[4 b .. 4 b + 2], where they ran
+// (XCC_ID << 32 | HW_ID), the shader-clock counter and the 100 MHz counter.
+hipError_t launch_clock_probe(uint64_t *out, int blocks, hipStream_t stream);
+
 // Compute units of the current device (cached after the first call; 256 when no device
 // answers, which is the MI355X count).
 int num_cus();
