@@ -20,7 +20,9 @@
  *
  * Conventions for every entry point below:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates and frees nothing and keeps no per-call state (reentrant).
+ *    allocates and frees nothing and keeps no per-call state (reentrant). The one
+ *    piece of device memory it holds is the static scratch array of
+ *    w8a8_gemm_splitk_noalloc (see there).
  *  - All tensors are row-major with the last index contiguous. Base pointers must
  *    be 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the null stream) on the current device.
@@ -246,6 +248,26 @@ int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const f
                      int weight_bits, int group_size, void *y, int y_dtype, int64_t M, int64_t N,
                      int64_t K, int64_t ldy, void *workspace, int64_t workspace_bytes,
                      void *stream);
+
+/*
+ * w8a8_gemm_splitk_noalloc -- w8a8_gemm_splitk for callers that cannot allocate device
+ * memory (code under stream / graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the slices' partial results go to a scratch array that the library holds in
+ * each device's memory from its first use there until the process ends (32 MiB per device,
+ * a file-scope device array), so the call takes no workspace and allocates nothing.
+ * Operands, layouts, constraints and results are those of w8a8_gemm_splitk with a
+ * sufficient workspace (the same plan and kernels, so the same bits). When the plan for the
+ * problem does not split, the single-pass kernels run and the scratch is not touched.
+ * Errors: W8A8_ERR_UNSUPPORTED_SHAPE, with nothing enqueued, when the plan's partial results
+ * need more than the 32 MiB scratch (slices * M * N * 4 bytes; w8a8_gemm_splitk_workspace
+ * gives that size): call w8a8_gemm_splitk with a workspace instead.
+ * Every call on one device shares that device's scratch: two calls whose executions
+ * overlap on a device (different streams, no ordering between them) race on it and give
+ * undefined results. Calls ordered on one stream are safe.
+ */
+int w8a8_gemm_splitk_noalloc(const int8_t *x_q, const float *s_x, const void *w, const float *s_w,
+                             int weight_bits, int group_size, void *y, int y_dtype, int64_t M, int64_t N,
+                             int64_t K, int64_t ldy, void *stream);
 
 /*
  * sdpa_decode -- attention for one decode step (Cider README "优化 SDPA（解码注意力）": one

@@ -215,6 +215,31 @@ def test_splitk_forced_unavailable(w8a8, unavailable):
     assert _splitk(lib, ws=None, ws_bytes=0) == UNSUPPORTED_DEVICE
 
 
+def _noalloc(lib, x_q=FAKE, bits=8, gs=0, y_dtype=F16, M=128, N=2560, K=10240, ldy=2560):
+    return lib.w8a8_gemm_splitk_noalloc(x_q, FAKE, FAKE, FAKE, bits, gs, FAKE, y_dtype, M, N, K, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(bits=2), INVALID, "weight_bits"),
+    (dict(gs=32), INVALID, "group_size"),
+    (dict(y_dtype=7), INVALID, "y_dtype"),
+    (dict(N=250, ldy=256), UNSUPPORTED_SHAPE, "N"),
+    (dict(K=100), UNSUPPORTED_SHAPE, "K"),
+    (dict(ldy=2500), INVALID, "ldy"),
+    (dict(x_q=None), INVALID, "null"),
+])
+def test_splitk_noalloc_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _noalloc(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_splitk_noalloc_forced_unavailable(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert _noalloc(lib) == UNSUPPORTED_DEVICE
+    assert _noalloc(lib, M=0) == UNSUPPORTED_DEVICE
+
+
 def test_splitk_workspace_query(w8a8):
     """The query is host-only arithmetic: slices * M * N * 4 bytes, or 0 where no split runs."""
     lib = w8a8.lib()

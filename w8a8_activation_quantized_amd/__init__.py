@@ -45,6 +45,7 @@ _SIGNATURES = {
                          _int),
     "w8a8_debug_force_splitk": ([_int], _int),
     "w8a8_debug_clock_probe": ([_vp, _vp], _int),
+    "w8a8_gemm_splitk_noalloc": ([_vp, _vp, _vp, _vp, _int, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "int8_mv": ([_vp, _int, _i64, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "quantize_weight_clipped": ([_vp, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp, _vp], _int),
     "sdpa_decode_workspace": ([_i64, _i64, _i64, _i64, _i64], _i64),
@@ -269,6 +270,19 @@ def w8a8_gemm_splitk(x_q, s_x, w, s_w, weight_bits=8, group_size=0, out_dtype=to
     _check(_lib.w8a8_gemm_splitk(_ptr(x_q), _ptr(s_x), _ptr(w), _ptr(s_w), weight_bits, group_size, _ptr(y),
                                  _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+    return y
+
+
+def w8a8_gemm_splitk_noalloc(x_q, s_x, w, s_w, weight_bits=8, group_size=0, out_dtype=torch.float16, y=None,
+                             stream=None):
+    """w8a8_gemm_splitk with the partial results in the library's per-device scratch array
+    (allocates nothing; raises W8A8Error when the split plan needs more scratch than it holds).
+    Pass `y` to keep the call free of allocations on the Python side too."""
+    M, K = x_q.shape
+    N = w.shape[0]
+    y = _out(y, M, N, out_dtype, x_q.device)
+    _check(_lib.w8a8_gemm_splitk_noalloc(_ptr(x_q), _ptr(s_x), _ptr(w), _ptr(s_w), weight_bits, group_size, _ptr(y),
+                                         _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
     return y
 
 

@@ -528,6 +528,36 @@ int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const f
     return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed), st), fn);
 }
 
+int w8a8_gemm_splitk_noalloc(const int8_t *x_q, const float *s_x, const void *w, const float *s_w, int weight_bits,
+                             int group_size, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                             void *stream) {
+    const char *fn = "w8a8_gemm_splitk_noalloc";
+    int rc = check_split_kind(fn, weight_bits, group_size);
+    if (rc != W8A8_OK) return rc;
+    rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0 || weight_bits == 4);
+    if (rc != W8A8_OK) return rc;
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    const int wkind = weight_bits == 4 ? w8a8::W_INT4 : w8a8::W_INT8;
+    w8a8::GemmProblem p = make_problem(x_q, s_x, w, s_w, group_size, wkind, y, y_dtype, M, N, K, ldy);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const w8a8::SplitPlan plan = current_split_plan(p);
+    if (plan.slices > 1) {
+        const int64_t need = w8a8::splitk_workspace_bytes(p, plan);
+        if (need > w8a8::kSplitScratchBytes)
+            return fail(W8A8_ERR_UNSUPPORTED_SHAPE,
+                        "%s: the split plan (%d slices) needs %lld bytes of scratch, more than the %lld bytes this "
+                        "call holds per device; use w8a8_gemm_splitk with a workspace",
+                        fn, plan.slices, (long long)need, (long long)w8a8::kSplitScratchBytes);
+        void *ws = nullptr;
+        const hipError_t e = w8a8::splitk_scratch(&ws);
+        if (e != hipSuccess) return fail(W8A8_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(e));
+        p.ws = ws;
+        return launched(w8a8::launch_gemm_splitk(p, plan, st), fn);
+    }
+    return launched(w8a8::launch_gemm(p, g_force_cfg.load(std::memory_order_relaxed), st), fn);
+}
+
 int w8a8_debug_clock_probe(uint64_t *out, void *stream) {
     const char *fn = "w8a8_debug_clock_probe";
     if (!out || !aligned16(out)) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: out must be a 16-byte aligned pointer", fn);

@@ -2244,6 +2244,35 @@ int64_t splitk_workspace_bytes(const GemmProblem &p, const SplitPlan &plan) {
     return plan.slices > 1 ? (int64_t)plan.slices * p.M * p.N * 4 : 0;
 }
 
+// Scratch of the allocation-free split-K call (w8a8_gemm_splitk_noalloc): the slices'
+// partial results, for callers that cannot allocate device memory. Each device that runs
+// the library holds its own copy of this array, at its own address, until the process
+// ends. Host code never passes the array's name to a kernel (on the host that name is a
+// stand-in, not a device address): it takes the address per device from
+// hipGetSymbolAddress, once, with that device current.
+static __device__ __align__(256) int8_t scratch[kSplitScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t splitk_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);  // same value from any racing thread
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 hipError_t launch_gemm_splitk(GemmProblem p, const SplitPlan &plan, hipStream_t stream) {
     if (plan.slices < 2 || plan.slices > p.K / 128 || p.ws == nullptr || !split_config(p, plan.cfg))
         return hipErrorInvalidValue;

@@ -96,4 +96,10 @@ int64_t splitk_workspace_bytes(const GemmProblem &p, const SplitPlan &plan);
 // Requires plan.slices > 1, p.ws with splitk_workspace_bytes(p, plan) bytes.
 hipError_t launch_gemm_splitk(GemmProblem p, const SplitPlan &plan, hipStream_t stream);
 
+// Size of the per-device scratch array of the allocation-free split-K call.
+constexpr int64_t kSplitScratchBytes = (int64_t)32 << 20;
+// Device address of the current device's scratch array (looked up once per device with
+// hipGetSymbolAddress, then cached). Allocates nothing.
+hipError_t splitk_scratch(void **ptr);
+
 }  // namespace w8a8
