@@ -57,10 +57,13 @@ def _load():
         lib.oracle_quantize_weight_clipped.argtypes = [vp, i64, i64, i32, i32, ctypes.c_float, vp, vp]
         lib.oracle_sdpa_decode.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, ctypes.c_double, vp, vp, vp]
         lib.oracle_rmsnorm_quantize.argtypes = [vp, i32, vp, i32, ctypes.c_double, i64, i64, i64, vp, vp, vp]
+        lib.oracle_swiglu_quantize.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp]
+        lib.oracle_exp_steps.argtypes = [vp, i64, vp]
         for f in (lib.oracle_quantize_per_token, lib.oracle_quantize_weight, lib.oracle_unpack_int4,
                   lib.oracle_gemm_i32, lib.oracle_group_acc, lib.oracle_dequant_pc,
                   lib.oracle_dequant_pg, lib.oracle_dequant_pc_f32, lib.oracle_dequant_pg_f32, lib.oracle_mv, lib.oracle_quantize_weight_clipped,
-                  lib.oracle_sdpa_decode, lib.oracle_rmsnorm_quantize):
+                  lib.oracle_sdpa_decode, lib.oracle_rmsnorm_quantize, lib.oracle_swiglu_quantize,
+                  lib.oracle_exp_steps):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -124,6 +127,35 @@ def rmsnorm_quantize(x: np.ndarray, g: np.ndarray, eps: float, x_bf16: bool = Fa
     _check(_load().oracle_rmsnorm_quantize(_p(xb), int(x_bf16), _p(gb), int(g_bf16), float(eps), M, K, K,
                                            _p(xq), _p(su), _p(sx)), "rmsnorm_quantize")
     return xq, su, sx
+
+
+def swiglu_quantize(gate: np.ndarray, up: np.ndarray, bf16: bool = False):
+    """SwiGLU with the per-token quantization folded in (oracle.c cites the passages).
+
+    gate, up [M, I]: float16 arrays, or (bf16=True) uint16 arrays of bfloat16 bit patterns
+    (row strides may differ: views into one wider array work). Returns (x_q int8 [M, I],
+    s_x float32 [M], h float32 [M, I]) with h = silu(gate) * up evaluated in the specified
+    fp32 steps and x_q, s_x its per-token quantization."""
+    gb = np.asarray(gate).view(np.uint16)
+    ub = np.asarray(up).view(np.uint16)
+    if gb.strides[1] != 2 or ub.strides[1] != 2:
+        gb, ub = np.ascontiguousarray(gb), np.ascontiguousarray(ub)
+    M, I = gb.shape
+    assert ub.shape == (M, I)
+    xq = np.empty((M, I), np.int8)
+    sx = np.empty((M,), np.float32)
+    h = np.empty((M, I), np.float32)
+    _check(_load().oracle_swiglu_quantize(_p(gb), _p(ub), int(bf16), M, I, gb.strides[0] // 2, ub.strides[0] // 2,
+                                          _p(xq), _p(sx), _p(h)), "swiglu_quantize")
+    return xq, sx, h
+
+
+def exp_steps(x: np.ndarray) -> np.ndarray:
+    """The fp32 exp evaluation the SwiGLU producer specifies (oracle.c, exp_steps)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    _check(_load().oracle_exp_steps(_p(x), x.size, _p(y)), "exp_steps")
+    return y
 
 
 def quantize_weight(W: np.ndarray, bits: int = 8, group_size: int = 0):

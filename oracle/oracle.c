@@ -515,3 +515,81 @@ int oracle_rmsnorm_quantize(const uint16_t *x, int x_is_bf16, const uint16_t *g,
     }
     return ORACLE_OK;
 }
+
+/*
+ * exp in fp32 by a fixed sequence of fp32 operations, the evaluation the SwiGLU producer
+ * below specifies (and its GPU kernel follows), so that both sides take the same code
+ * decisions. Range reduction after Cody and Waite: x = k ln 2 + r with k = rint(x log2 e),
+ * r = x - k ln 2 formed with two fused multiply-adds against ln 2 split into its fp32
+ * rounding and the fp32 rounding of the remainder; |r| <= ln 2 / 2 + tiny. e^r is the Taylor
+ * polynomial of degree 7 (coefficients 1 / n!, rounded to fp32) by Horner's rule with fused
+ * multiply-adds (truncation error below |r|^8 / 8! < 5.3e-9 relative); the result is p * 2^k,
+ * 2^k built exactly. The argument is first clamped to [-87, 88], which keeps k in
+ * [-126, 127] (2^k a normal number) and the result finite.
+ */
+static float exp_steps(float x)
+{
+    const float log2e = 0x1.715476p+0f;   /* log2(e) rounded to fp32 */
+    const float ln2_hi = 0x1.62e43p-1f;   /* ln 2 rounded to fp32 */
+    const float ln2_lo = -0x1.05c61p-29f; /* ln 2 - ln2_hi rounded to fp32 */
+    if (x > 88.0f) x = 88.0f;
+    if (x < -87.0f) x = -87.0f;
+    const float k = rintf(x * log2e);
+    float r = fmaf(-k, ln2_hi, x);
+    r = fmaf(-k, ln2_lo, r);
+    float p = 1.0f / 5040.0f;
+    p = fmaf(p, r, 1.0f / 720.0f);
+    p = fmaf(p, r, 1.0f / 120.0f);
+    p = fmaf(p, r, 1.0f / 24.0f);
+    p = fmaf(p, r, 1.0f / 6.0f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    uint32_t bits = (uint32_t)((int)k + 127) << 23; /* 2^k, k in [-126, 127] */
+    float two_k;
+    memcpy(&two_k, &bits, sizeof two_k);
+    return p * two_k;
+}
+
+/*
+ * SwiGLU with the per-token quantization folded in: the producer of the down projection's
+ * input writes its int8 codes and per-token scale directly [P5 "Metal Kernel 流水线": the
+ * quantization is otherwise its own dispatch before the GEMM; P2 "W8A8 对称量化": the online
+ * quantization must not become the bottleneck; P5 "ANE+GPU 异构张量并行", 关键设计选择: the
+ * block's input preparation is shared]. The pages name no MLP; the one taken is the gated
+ * MLP of a Qwen3 block, whose down projection reads h = silu(gate) * up, gate and up being
+ * the two halves of the gate/up projection's output. In fp32:
+ *     e = exp_steps(-g);  s = g / (1 + e)  (IEEE division);  h = s * u
+ * then the per-token quantization of the run h exactly as quantize_per_token does it (h is
+ * never rounded to fp16 / bf16 first). gate / up: M rows of I half or bf16 values with row
+ * strides ldg / ldu elements. Outputs x_q [M, I], s_x [M] and, if h is not NULL, h [M, I]
+ * (fp32, for the tests).
+ */
+int oracle_swiglu_quantize(const uint16_t *gate, const uint16_t *up, int is_bf16, int64_t M, int64_t I, int64_t ldg,
+                           int64_t ldu, int8_t *x_q, float *s_x, float *h)
+{
+    if (M < 0 || I <= 0 || ldg < I || ldu < I) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float row[I];
+        for (int64_t i = 0; i < I; ++i) {
+            const uint16_t gb = gate[m * ldg + i], ub = up[m * ldu + i];
+            const float g = is_bf16 ? bf16_to_float(gb) : half_to_float(gb);
+            const float u = is_bf16 ? bf16_to_float(ub) : half_to_float(ub);
+            const float e = exp_steps(-g);
+            const float s = g / (1.0f + e);
+            row[i] = s * u;
+            if (h) h[m * I + i] = row[i];
+        }
+        s_x[m] = quantize_run(row, I, 127.0f, -128, 127, x_q + m * I);
+    }
+    return ORACLE_OK;
+}
+
+/* exp_steps over an array (for the tests' checks of the evaluation itself). */
+int oracle_exp_steps(const float *x, int64_t n, float *y)
+{
+    if (n < 0) return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) y[i] = exp_steps(x[i]);
+    return ORACLE_OK;
+}

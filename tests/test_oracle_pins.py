@@ -718,3 +718,86 @@ def test_rmsnorm_quantize_codes_equal_quantize_of_the_fp64_norm():
         assert ok.sum() >= 0.8 * M
         assert (xq[ok] == np.rint(t[ok])).all()
         np.testing.assert_allclose(sx, s, rtol=2.0 ** -20)
+
+
+# ---- SwiGLU with the per-token quantization folded in (swiglu_quantize) -----------------
+# Plausible mistakes caught: a wrong exp (range reduction, a dropped Taylor term, a wrong
+# clamp) -> fp64 exp bound and the fixed points; silu with a wrong sign or without the gate
+# factor -> fp64 silu * up bound; quantization of something other than h -> numpy's fp32
+# quantization of the returned h and the fp64 quantization away from near-ties; gate and up
+# swapped -> the asymmetric fp64 check.
+
+def test_exp_steps_against_fp64_exp():
+    x = np.concatenate([np.linspace(-87.0, 88.0, 400001), [0.0, -0.0, 1e-30, -1e-30, 0.34657359, -0.34657359]])
+    x = x.astype(np.float32)
+    y = oracle.exp_steps(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    assert (np.abs(y - ref) <= 2.0 ** -22 * ref).all()
+    assert oracle.exp_steps(np.zeros(1, np.float32))[0] == 1.0
+    # clamped arguments: finite, and equal to the value at the clamp
+    big = oracle.exp_steps(np.array([88.0, 100.0, 1e30, -87.0, -200.0, -1e30], np.float32))
+    assert big[0] == big[1] == big[2] and np.isfinite(big[0]) and big[3] == big[4] == big[5] > 0
+
+
+def _silu64(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def _swiglu_inputs(M, I, seed, bf16=False):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((M, I)) * 2.0
+    u = rng.standard_normal((M, I))
+    g[:, rng.choice(I, 3, replace=False)] *= 20  # large gate values (silu ~ g and ~ 0)
+    if bf16:
+        import torch
+        gb = torch.from_numpy(g.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        ub = torch.from_numpy(u.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return gb, ub, (gb.astype(np.uint32) << 16).view(np.float32), (ub.astype(np.uint32) << 16).view(np.float32)
+    g16, u16 = g.astype(np.float16), u.astype(np.float16)
+    return g16, u16, g16.astype(np.float32), u16.astype(np.float32)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_swiglu_quantize_h_codes_and_scale(bf16):
+    M, I = 120, 384
+    ga, ua, gf, uf = _swiglu_inputs(M, I, seed=51, bf16=bf16)
+    xq, sx, h = oracle.swiglu_quantize(ga, ua, bf16=bf16)
+    # h against fp64 silu(g) * u: exp within 2^-22, then one add, one division, one product;
+    # below g = -87 the exp argument is clamped and h is only bounded (|h| <= |g u| 2^-125,
+    # since 1 + e^87 > 2^125): those values quantize to 0 next to any normal entry of the row
+    h64 = _silu64(gf.astype(np.float64)) * uf.astype(np.float64)
+    hd = h.astype(np.float64)
+    live = gf >= -87.0
+    assert (np.abs(hd - h64) <= 2.0 ** -20 * np.abs(h64) + 1e-37)[live].all()
+    assert (np.abs(hd) <= np.abs(gf.astype(np.float64) * uf) * 2.0 ** -125)[~live].all()
+    # the quantization of the returned h, recomputed with numpy's IEEE fp32 division
+    s_np = (np.abs(h).max(axis=1) / np.float32(127.0)).astype(np.float32)
+    assert (sx.view(np.uint32) == s_np.view(np.uint32)).all()
+    q_np = np.clip(np.rint(h / s_np[:, None]), -128, 127).astype(np.int8)
+    assert (xq == q_np).all()
+    # and against the fp64 definition, away from near-ties: the fp32 evaluation moves a
+    # quotient of magnitude <= 127 by less than 127 * 2^-21 < 2^-14
+    s64 = np.abs(h64).max(axis=1) / 127.0
+    t = h64 / s64[:, None]
+    ok = ~(np.abs(np.abs(t - np.floor(t)) - 0.5) < 2.0 ** -13).any(axis=1)
+    assert ok.sum() >= 0.8 * M
+    assert (xq[ok] == np.rint(t[ok])).all()
+
+
+def test_swiglu_quantize_closed_forms_and_strided_halves():
+    M, I = 6, 64
+    ga, ua, _, _ = _swiglu_inputs(M, I, seed=52)
+    ga[0] = 0          # silu(0) = 0: a zero row
+    ua[1] = 0          # up = 0: a zero row
+    ga[2] = 60.0       # silu(g) = g / (1 + e^-60) = g in fp32: h = g * u exactly
+    ua[2] = np.float16(-1.5)
+    xq, sx, h = oracle.swiglu_quantize(ga, ua)
+    assert sx[0] == 0 and sx[1] == 0 and (xq[:2] == 0).all()
+    assert (h[2] == np.float32(60.0) * np.float32(-1.5)).all() and (xq[2] == -127).all()
+    # gate and up as the two halves of one [M, 2I] array (the gate/up projection's output)
+    both = np.concatenate([ga, ua], axis=1)
+    xq2, sx2, h2 = oracle.swiglu_quantize(both[:, :I], both[:, I:])
+    assert (xq2 == xq).all() and (sx2 == sx).all() and (h2 == h).all()
+    # swapping gate and up changes the result (silu applies to the gate only)
+    xq3, _, _ = oracle.swiglu_quantize(ua, ga)
+    assert (xq3[3:] != xq[3:]).any()
