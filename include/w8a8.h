@@ -105,12 +105,35 @@ int rmsnorm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t l
                      int gamma_dtype, float eps, int8_t *x_q, float *s_x, void *stream);
 
 /*
+ * swiglu_quantize -- the producer of a gated MLP's down-projection input writes that input's
+ * codes itself, so the per-token quantization (README "Metal Kernel 流水线" step 1; juejin
+ * post, "W8A8 对称量化": it must stay cheap) needs no pass of its own. The input is
+ * h = silu(gate) * up, gate and up being the two halves of the gate/up projection's output:
+ *   e = exp(-g) (the fixed fp32 evaluation below);  s = g / (1 + e) (IEEE);  h = s * u  (fp32)
+ *   x_q [M, I] int8, row stride I, and s_x [M] fp32: the per-token quantization of h exactly as
+ *   quantize_per_token computes it (h is not rounded to fp16 / bf16 first).
+ * exp(x) is evaluated as: x clamped to [-87, 88]; k = rint(x * RN(log2 e)); r = fma(-k, RN(ln 2),
+ * x), r = fma(-k, RN(ln 2 - RN(ln 2)), r); p = the Taylor polynomial of degree 7 in r with the
+ * coefficients RN(1 / n!), by Horner's rule with fmas; result p * 2^k (RN = fp32 rounding).
+ * With that, the codes and scales are bit-reproducible; h is within 2^-20 relative of
+ * silu(g) * u for g >= -87.
+ *   gate, up  [M, I] fp16 or bf16 (dtype), row strides ldg, ldu elements (they may be views
+ *             into one [M, 2 I] array)
+ * Constraints: M >= 0, I >= 8, I % 8 == 0, ldg, ldu >= I and multiples of 8, all pointers
+ * 16-byte aligned. Inputs finite.
+ */
+int swiglu_quantize(const void *gate, const void *up, int dtype, int64_t M, int64_t I, int64_t ldg, int64_t ldu,
+                    int8_t *x_q, float *s_x, void *stream);
+
+/*
  * quantize_weight -- offline min-max weight quantization (README "说明": min-max
  * by default; "量化": symmetric int8 per channel / per group, int4 zero point 8).
  *   W      [N, K] fp32 (row n = output channel n)
  *   bits 8, group_size 0      : w_q int8 [N, K],        s_w [N]       = max_k |W[n,:]| / 127
  *   bits 8, group_size 64|128 : w_q int8 [N, K],        s_w [N, K/gs] = max |W[n, group]| / 127
  *   bits 4, group_size 64|128 : w_q uint8 [N, K/2],     s_w [N, K/gs] = max |W[n, group]| / 7
+ *   bits 4, group_size 0      : w_q uint8 [N, K/2],     s_w [N]       = max_k |W[n,:]| / 7
+ *       (the README's per-column INT4, section "量化": one scale per output channel)
  *       int4 codes q = clamp(rne(W / s), -8, 7) stored as u = q + 8, byte j of row n
  *       = u[n, 2j] | u[n, 2j+1] << 4 (even k in the low nibble).
  * Constraints: N >= 1, K >= 64, K % 64 == 0, K % group_size == 0. Inputs finite.
@@ -175,12 +198,25 @@ int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, c
                  int64_t ldy, void *stream);
 
 /*
+ * w4a8_gemm_pc -- W4A8 GEMM with per-column int4 weights (Cider README "量化": W4A8 weights are
+ * symmetric INT4, zero point 8, per column): one scale per output channel, the int4 codes
+ * unpacked inside the GEMM's weight-tile load as for w4a8_gemm_pg, then the per-channel path:
+ *   w_packed [N, K/2] uint8 (quantize_weight with bits = 4, group_size = 0), s_w [N] fp32
+ *   acc = sum_k x_q[m,k] * q[n,k]  (q = u - 8, exact int32);  y = rne_out((fp32(acc) * s_x[m]) * s_w[n])
+ *   W8A8_I32 writes acc itself.
+ * Constraints: as w8a8_gemm_pc.
+ */
+int w4a8_gemm_pc(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, const float *s_w, void *y,
+                 int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream);
+
+/*
  * w8a8_linear -- the whole layer in one call: per-token activation quantization of x
  * followed by the int8 GEMM with fused dequant (juejin post, "INT8 TensorOps 内核设计":
  * quantize_per_token, then matmul_fused_dequant). The weight arguments select the GEMM:
  *   weight_bits 8, group_size 0      -> w8a8_gemm_pc (w = w_q [N, K] int8, s_w [N])
  *   weight_bits 8, group_size 64|128 -> w8a8_gemm_pg (s_w [N, K/group_size])
  *   weight_bits 4, group_size 64|128 -> w4a8_gemm_pg (w = w_packed [N, K/2])
+ *   weight_bits 4, group_size 0      -> w4a8_gemm_pc (w = w_packed [N, K/2], s_w [N])
  *   x [M, K] fp16 or bf16 (x_dtype), row stride ldx elements (ldx >= K, ldx % 8 == 0).
  *   x_q [M, K] int8 and s_x [M] fp32 (caller-owned) receive the codes and scales exactly as
  *   quantize_per_token writes them; y [M, N] as for the GEMM calls (not W8A8_I32).
@@ -225,12 +261,14 @@ int int8_mv(const void *x, int x_dtype, int64_t ldx, const int8_t *w_q, const fl
  *
  * w8a8_gemm_splitk_workspace: bytes of workspace the split form uses for this problem,
  *   slices * M * N * 4; 0 when the library would not split it (M <= 16, K % 128 != 0, int4
- *   weights with W8A8_I32 output, or a single pass estimated faster). The value depends only
- *   on the arguments, the device's compute-unit count and the debug knobs below.
+ *   weights with per-channel scales or with W8A8_I32 output, or a single pass estimated
+ *   faster). The value depends only on the arguments, the device's compute-unit count and
+ *   the debug knobs below.
  *   Negative: -status for invalid arguments (the checks of the GEMM calls).
  *
  * w8a8_gemm_splitk: the GEMM selected as in w8a8_linear (weight_bits 8 / group_size 0:
- *   w8a8_gemm_pc; 8 / 64|128: w8a8_gemm_pg; 4 / 64|128: w4a8_gemm_pg, w = w_packed),
+ *   w8a8_gemm_pc; 8 / 64|128: w8a8_gemm_pg; 4 / 64|128: w4a8_gemm_pg, w = w_packed;
+ *   4 / 0: w4a8_gemm_pc, which has no split form and always runs its single pass),
  *   same operands, layouts and constraints, plus
  *   workspace        device memory, 16-byte aligned, owned by the caller, not overlapping
  *                    any operand; contents on return are unspecified. It must stay

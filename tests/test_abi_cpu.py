@@ -38,7 +38,7 @@ def unavailable(monkeypatch):
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for required in ("quantize_per_token", "quantize_weight", "w8a8_gemm_pc", "w8a8_gemm_pg",
-                     "w4a8_gemm_pg", "w8a8_linear", "w8a8_is_available", "w8a8_last_error",
+                     "w4a8_gemm_pg", "w4a8_gemm_pc", "w8a8_linear", "w8a8_is_available", "w8a8_last_error",
                      "w8a8_status_string", "int8_mv", "w8a8_gemm_splitk", "w8a8_gemm_splitk_workspace",
                      "rmsnorm_quantize", "sdpa_decode", "quantize_weight_clipped"):
         assert required in names, names
@@ -115,7 +115,6 @@ def test_quantize_validation(w8a8):
     assert lib.quantize_per_token(FAKE, F16, 4, 64, 68, FAKE, FAKE, None) == INVALID
     assert lib.quantize_per_token(None, F16, 4, 64, 64, FAKE, FAKE, None) == INVALID
     assert lib.quantize_weight(FAKE, 16, 256, 3, 0, FAKE, FAKE, None) == INVALID
-    assert lib.quantize_weight(FAKE, 16, 256, 4, 0, FAKE, FAKE, None) == INVALID
     assert lib.quantize_weight(FAKE, 16, 256, 8, 32, FAKE, FAKE, None) == INVALID
     assert lib.quantize_weight(FAKE, 16, 200, 8, 0, FAKE, FAKE, None) == UNSUPPORTED_SHAPE
     assert lib.quantize_weight(FAKE, 0, 256, 8, 0, FAKE, FAKE, None) == INVALID
@@ -162,7 +161,6 @@ def _linear(lib, x=FAKE, x_dtype=F16, ldx=256, bits=8, gs=0, x_q=FAKE, y_dtype=F
     (dict(x_dtype=F32), INVALID, "x_dtype"),
     (dict(bits=2), INVALID, "weight_bits"),
     (dict(gs=32), INVALID, "group_size"),
-    (dict(bits=4, gs=0), INVALID, "int4"),
     (dict(y_dtype=I32), INVALID, "y_dtype"),
     (dict(ldx=200), INVALID, "ldx"),
     (dict(ldx=260), INVALID, "ldx"),
@@ -193,7 +191,6 @@ def _splitk(lib, x_q=FAKE, bits=8, gs=0, y_dtype=F16, M=128, N=2560, K=10240, ld
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(bits=2), INVALID, "weight_bits"),
     (dict(gs=32), INVALID, "group_size"),
-    (dict(bits=4, gs=0), INVALID, "int4"),
     (dict(y_dtype=7), INVALID, "y_dtype"),
     (dict(N=250, ldy=256), UNSUPPORTED_SHAPE, "N"),
     (dict(K=100), UNSUPPORTED_SHAPE, "K"),
@@ -253,10 +250,12 @@ def test_splitk_workspace_query(w8a8):
         assert q(4, 64, F32, 64, 512, 10240) == 4 * 64 * 512 * 4
         assert lib.w8a8_debug_force_splitk(100) == OK
         assert q(8, 0, F16, 128, 2560, 1024) == 8 * 128 * 2560 * 4
-        # never split: GEMV range, K not a whole number of 128-value tiles, int4 with I32 out
+        # never split: GEMV range, K not a whole number of 128-value tiles, int4 with I32 out,
+        # per-column int4
         assert q(8, 0, F16, 16, 2560, 10240) == 0
         assert q(8, 0, F16, 128, 2560, 10240 + 64) == 0
         assert q(4, 128, I32, 128, 2560, 10240) == 0
+        assert q(4, 0, F16, 128, 2560, 10240) == 0
         assert q(8, 0, F16, 0, 2560, 10240) == 0
         # a forced configuration without a split form runs the single pass
         lib.w8a8_debug_force_config(13)
@@ -314,7 +313,6 @@ def test_mv_forced_unavailable(w8a8, unavailable):
     (dict(pct=100.5), INVALID, "clip_percentile"),
     (dict(pct=float("nan")), INVALID, "clip_percentile"),
     (dict(bits=3), INVALID, "bits"),
-    (dict(bits=4, gs=0), INVALID, "int4"),
     (dict(gs=32), INVALID, "group_size"),
     (dict(K=200), UNSUPPORTED_SHAPE, "K"),
     (dict(N=0), INVALID, "N"),
@@ -372,3 +370,39 @@ def test_clock_probe_validation(w8a8, unavailable):
     assert lib.w8a8_debug_clock_probe(None, None) == INVALID
     assert lib.w8a8_debug_clock_probe(ctypes.c_void_p(0x100008), None) == INVALID
     assert lib.w8a8_debug_clock_probe(FAKE, None) == UNSUPPORTED_DEVICE
+
+
+def test_per_column_int4_validation(w8a8, unavailable):
+    """Per-column int4 weights (group size 0) pass argument validation (W8A8_FORCE_UNAVAILABLE
+    then stops the call before any launch); a bad shape still fails first."""
+    lib = w8a8.lib()
+    assert lib.quantize_weight(FAKE, 16, 256, 4, 0, FAKE, FAKE, None) == UNSUPPORTED_DEVICE
+    assert lib.w4a8_gemm_pc(FAKE, FAKE, FAKE, FAKE, FAKE, F16, 4, 256, 512, 256, None) == UNSUPPORTED_DEVICE
+    assert lib.w4a8_gemm_pc(FAKE, FAKE, FAKE, FAKE, FAKE, F16, 4, 250, 512, 256, None) == UNSUPPORTED_SHAPE
+    assert lib.w4a8_gemm_pc(None, FAKE, FAKE, FAKE, FAKE, F16, 4, 256, 512, 256, None) == INVALID
+    assert lib.w8a8_linear(FAKE, F16, 512, FAKE, FAKE, 4, 0, FAKE, FAKE, FAKE, F16, 4, 256, 512, 256,
+                           None) == UNSUPPORTED_DEVICE
+
+
+def _swiglu(lib, g=FAKE, dtype=F16, M=4, I=512, ldg=1024, ldu=1024, xq=FAKE):
+    return lib.swiglu_quantize(g, FAKE, dtype, M, I, ldg, ldu, xq, FAKE, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F32), INVALID, "dtype"),
+    (dict(M=-1), INVALID, "M"),
+    (dict(I=500, ldg=504, ldu=504), UNSUPPORTED_SHAPE, "I"),
+    (dict(ldg=500), INVALID, "ldg"),
+    (dict(ldu=1020), INVALID, "ldu"),
+    (dict(g=None), INVALID, "null"),
+    (dict(xq=ctypes.c_void_p(0x100008)), INVALID, "aligned"),
+])
+def test_swiglu_quantize_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _swiglu(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_swiglu_quantize_forced_unavailable(w8a8, unavailable):
+    lib = w8a8.lib()
+    assert _swiglu(lib) == UNSUPPORTED_DEVICE

@@ -36,7 +36,7 @@ def weights(N, K, seed):
     return W
 
 
-@pytest.mark.parametrize("bits,gs", [(8, 0), (8, 64), (8, 128), (4, 64), (4, 128)])
+@pytest.mark.parametrize("bits,gs", [(8, 0), (8, 64), (8, 128), (4, 64), (4, 128), (4, 0)])
 @pytest.mark.parametrize("N,K", [(272, 2560), (48, 384), (16, 10240)])
 def test_clipped_bit_exact(w8a8, bits, gs, N, K):
     W = weights(N, K, seed=N + K + gs + bits)

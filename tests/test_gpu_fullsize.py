@@ -31,8 +31,10 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(10240, 2560), (2560, 10240)]
 POINTS = ([("pc", M, N, K) for M in (1, 128, 1024, 4096, 8192) for N, K in SHAPES]
           + [(mode, M, N, K) for mode in ("pg128", "pg64") for M in (128, 1024, 4096, 8192) for N, K in SHAPES]
-          + [("w4_128", M, 10240, 2560) for M in (1, 1024, 4096)])
-KIND = {"pc": (8, 0), "pg128": (8, 128), "pg64": (8, 64), "w4_128": (4, 128)}
+          + [("w4_128", M, 10240, 2560) for M in (1, 1024, 4096)]
+          # per-column int4 weights (the README's W4A8 weight format), the W4A8 sizes
+          + [("w4_0", M, 10240, 2560) for M in (1, 1024, 4096)])
+KIND = {"pc": (8, 0), "pg128": (8, 128), "pg64": (8, 64), "w4_128": (4, 128), "w4_0": (4, 0)}
 
 
 def note(msg):
@@ -62,6 +64,8 @@ def gpu_gemm(w8a8, mode, xq, sx, wq, sw, out):
         y = w8a8.w8a8_gemm_pc(xq, sx, wq, sw, out)
     elif bits == 8:
         y = w8a8.w8a8_gemm_pg(xq, sx, wq, sw, gs, out)
+    elif gs == 0:
+        y = w8a8.w4a8_gemm_pc(xq, sx, wq, sw, out)
     else:
         y = w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, out)
     torch.cuda.synchronize()
@@ -76,6 +80,9 @@ def oracle_rows(mode, x_rows, owq, osw):
     elif bits == 8:
         r = oracle.linear_pg(x_rows, owq, osw, gs)
         r["G"] = owq.shape[1] // gs
+    elif gs == 0:
+        r = oracle.linear_w4(x_rows, owq, osw, 0)
+        r["mag"], r["G"] = np.abs(r["y"]), 1
     else:
         r = oracle.linear_w4(x_rows, owq, osw, gs)
         r["G"] = x_rows.shape[1] // gs
@@ -103,7 +110,7 @@ def test_every_row(w8a8, mode, M, N, K):
         fused = host(w8a8.w8a8_linear(torch.from_numpy(x).cuda(), wq, sw, bits, gs, torch.float16, x_q=xq2, s_x=sx2)[0])
         torch.cuda.synchronize()
         assert (host(xq2) == oxq).all() and (host(sx2).view(np.uint32) == osx.view(np.uint32)).all(), "fused codes"
-    canonical = mode == "pc" or M > 16  # the fp32 fold in K order (see the module docstring)
+    canonical = gs == 0 or M > 16  # the fp32 fold in K order (see the module docstring)
     chunk = 2048 if mode == "pc" else 512
     for r0 in range(0, M, chunk):
         r1 = min(M, r0 + chunk)
@@ -115,7 +122,7 @@ def test_every_row(w8a8, mode, M, N, K):
             check_exact(y16[r0:r1], "f16", r["y32"], what)
         if fused is not None:
             check_output(fused[r0:r1], "f16", r["y"], r["mag"], r["G"], what + " (w8a8_linear)")
-            if mode == "pc":
+            if gs == 0:
                 check_exact(fused[r0:r1], "f16", r["y32"], what + " (w8a8_linear)")
 
 

@@ -55,7 +55,9 @@ def weights(w8a8, W, mode):
 
 def two_step(w8a8, xd, wq, sw, bits, gs, out):
     xq, sx = w8a8.quantize_per_token(xd)
-    if bits == 4:
+    if bits == 4 and gs == 0:
+        y = w8a8.w4a8_gemm_pc(xq, sx, wq, sw, out)
+    elif bits == 4:
         y = w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, out)
     elif gs:
         y = w8a8.w8a8_gemm_pg(xq, sx, wq, sw, gs, out)
@@ -77,6 +79,8 @@ def oracle_y(x, W, mode):
         gs = int(mode[3:])
         wq, sw = oracle.quantize_weight(W, 4, gs)
         r = oracle.linear_w4(x, wq, sw, gs)
+        if gs == 0:
+            return r["y"], np.abs(r["y"]), 1
     return r["y"], r["mag"], W.shape[1] // gs
 
 
@@ -88,7 +92,7 @@ def with_edge_rows(x):
     return x
 
 
-@pytest.mark.parametrize("mode", ["pc", "pg64", "pg128", "w4_128", "w4_64"])
+@pytest.mark.parametrize("mode", ["pc", "pg64", "pg128", "w4_128", "w4_64", "w4_0"])
 @pytest.mark.parametrize("M,N,K", [(1, 272, 2560), (2, 48, 10240), (3, 1040, 640), (5, 16, 4096), (8, 272, 1280),
                                    (16, 528, 2560), (1, 10240, 2560), (17, 272, 640), (40, 48, 1280)])
 def test_linear_fp16(w8a8, mode, M, N, K):
@@ -105,12 +109,12 @@ def test_linear_fp16(w8a8, mode, M, N, K):
         assert (host(xq) == oq).all(), "activation codes differ from the oracle"
         assert (host(sx).view(np.uint32) == osx.view(np.uint32)).all(), "activation scales differ"
         check_output(host(y), fmt, y64, mag, G, f"linear {mode} {M}x{N}x{K} {fmt}")
-        if mode == "pc":
+        if gs == 0:
             y2, _, _ = two_step(w8a8, xd, wq, sw, bits, gs, out)
             assert (host(y) == host(y2)).all(), "per-channel output differs from the two-step path"
 
 
-@pytest.mark.parametrize("mode", ["pc", "pg128", "w4_128"])
+@pytest.mark.parametrize("mode", ["pc", "pg128", "w4_128", "w4_0"])
 @pytest.mark.parametrize("M", [1, 4, 16, 33])
 def test_linear_bf16_input_and_tiny_rows(w8a8, mode, M):
     """bf16 activations, including a row whose scale is below 2^-100 (exact-division path)."""
@@ -130,17 +134,15 @@ def test_linear_bf16_input_and_tiny_rows(w8a8, mode, M):
     assert (host(xq) == oq).all() and (host(sx).view(np.uint32) == osx.view(np.uint32)).all()
     # the oracle's dequantization of the oracle's codes (equal to the GPU's, checked above)
     K_ = x16.shape[1]
-    if mode == "pc":
-        owq, osw = oracle.quantize_weight(W, 8, 0)
-        y64 = oracle.dequant_pc(oracle.gemm_i32(oq, owq), osx, osw)
+    owq, osw = oracle.quantize_weight(W, bits, gs)
+    codes = oracle.unpack_int4(owq, K_) if bits == 4 else owq
+    if gs == 0:
+        y64 = oracle.dequant_pc(oracle.gemm_i32(oq, codes), osx, osw)
         mag, G = np.abs(y64), 1
         assert (host(y) == host(y2)).all()
     else:
-        gs_ = 128
-        owq, osw = oracle.quantize_weight(W, bits, gs_)
-        codes = oracle.unpack_int4(owq, K_) if bits == 4 else owq
-        y64, mag = oracle.dequant_pg(oracle.group_acc(oq, codes, gs_), osx, osw)
-        G = K_ // gs_
+        y64, mag = oracle.dequant_pg(oracle.group_acc(oq, codes, gs), osx, osw)
+        G = K_ // gs
     check_output(host(y), "f16", y64, mag, G, f"linear bf16 {mode} M={M}")
     check_output(host(y2), "f16", y64, mag, G, f"two-step bf16 {mode} M={M}")
 

@@ -118,7 +118,8 @@ def test_quantize_empty_batch(w8a8):
 
 @pytest.mark.parametrize("bits,gs,N,K", [(8, 0, 272, 2560), (8, 64, 272, 2560), (8, 128, 48, 384),
                                          (4, 128, 272, 2560), (4, 64, 48, 384),
-                                         (8, 0, 10240, 2560), (4, 128, 10240, 2560)])
+                                         (8, 0, 10240, 2560), (4, 128, 10240, 2560), (4, 0, 272, 2560),
+                                         (4, 0, 10240, 2560)])
 def test_quantize_weight(w8a8, bits, gs, N, K):
     note(f"quantize_weight bits={bits} gs={gs} N={N} K={K}")
     _, W = linear_inputs(0, N, K, seed=N + K + gs)
@@ -132,7 +133,7 @@ def test_quantize_weight(w8a8, bits, gs, N, K):
 
 # ---- GEMM + dequant ----------------------------------------------------------------------
 
-MODES = ["pc", "pg64", "pg128", "w4_128", "w4_64"]
+MODES = ["pc", "pg64", "pg128", "w4_128", "w4_64", "w4_0"]
 
 
 def run_mode(w8a8, mode, x, W, out_dtype, y=None):
@@ -149,7 +150,10 @@ def run_mode(w8a8, mode, x, W, out_dtype, y=None):
     else:
         gs = int(mode[3:])
         wq, sw = w8a8.quantize_weight(Wd, 4, gs)
-        yt = w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, out_dtype, y=y)
+        if gs:
+            yt = w8a8.w4a8_gemm_pg(xq, sx, wq, sw, gs, out_dtype, y=y)
+        else:
+            yt = w8a8.w4a8_gemm_pc(xq, sx, wq, sw, out_dtype, y=y)
     torch.cuda.synchronize()
     return yt
 
@@ -168,7 +172,10 @@ def oracle_mode(mode, x, W):
         gs = int(mode[3:])
         wq, sw = oracle.quantize_weight(W, 4, gs)
         r = oracle.linear_w4(x, wq, sw, gs)
-        r["G"] = W.shape[1] // gs
+        if gs:
+            r["G"] = W.shape[1] // gs
+        else:
+            r["mag"], r["G"] = np.abs(r["y"]), 1
     return r
 
 
@@ -234,7 +241,7 @@ def test_gemm_strided_output_and_empty(w8a8):
     assert y.shape == (0, 272)
 
 
-@pytest.mark.parametrize("mode", ["pc", "pg64", "w4_128"])
+@pytest.mark.parametrize("mode", ["pc", "pg64", "w4_128", "w4_0"])
 def test_every_config_identical(w8a8, mode):
     """Every tile configuration gives bit-identical results (catches edge-mask and LDS races)."""
     M, N, K = 300, 528, 1280
@@ -266,6 +273,10 @@ def test_every_config_identical(w8a8, mode):
     ("pc", 2048, 1024, 4096),     # 64 x 128 tiles, one round (Qwen3 k/v shape)
     ("pc", 1536, 2560, 10240),    # 128 x 128 tiles, one round
     ("pg128", 768, 2560, 10240),  # 64 x 64 per-group DMA tiles
+    ("w4_0", 1, 10240, 2560),     # per-column int4: GEMV
+    ("w4_0", 1024, 10240, 2560),  # 128 x 256 DMA tiles without the fold
+    ("w4_0", 4096, 10240, 2560),
+    ("w4_0", 768, 2560, 10240),   # 64 x 64 DMA tiles without the fold
 ])
 def test_full_size_config_shapes(w8a8, mode, M, N, K):
     note(f"full size {mode} M={M} N={N} K={K}")

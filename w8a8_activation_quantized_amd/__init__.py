@@ -35,9 +35,11 @@ _SIGNATURES = {
     "quantize_per_token": ([_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "quantize_weight": ([_vp, _i64, _i64, _int, _int, _vp, _vp, _vp], _int),
     "rmsnorm_quantize": ([_vp, _int, _i64, _i64, _i64, _vp, _int, ctypes.c_float, _vp, _vp, _vp], _int),
+    "swiglu_quantize": ([_vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "w8a8_gemm_pc": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w8a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w4a8_gemm_pg": ([_vp, _vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
+    "w4a8_gemm_pc": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp], _int),
     "w8a8_linear": ([_vp, _int, _i64, _vp, _vp, _int, _int, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp],
                     _int),
     "w8a8_gemm_splitk_workspace": ([_int, _int, _int, _i64, _i64, _i64], _i64),
@@ -156,6 +158,28 @@ def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float, x_q: torc
     return x_q, s_x
 
 
+def swiglu_quantize(gate: torch.Tensor, up: torch.Tensor, x_q: torch.Tensor | None = None,
+                    s_x: torch.Tensor | None = None, stream=None):
+    """Codes and per-token scale of h = silu(gate) * up: gate, up [M, I] fp16/bf16 with a
+    contiguous last dimension (they may be the two halves of one [M, 2 I] tensor).
+    Returns (x_q int8 [M, I], s_x fp32 [M])."""
+    for t in (gate, up):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("gate and up must be 2-D with a contiguous last dimension")
+    if gate.dtype != up.dtype or gate.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("gate and up must both be float16 or both bfloat16")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    M, I = gate.shape
+    if x_q is None:
+        x_q = torch.empty((M, I), dtype=torch.int8, device=gate.device)
+    if s_x is None:
+        s_x = torch.empty((M,), dtype=torch.float32, device=gate.device)
+    _check(_lib.swiglu_quantize(_ptr(gate), _ptr(up), _DTYPE_CODE[gate.dtype], M, I, gate.stride(0), up.stride(0),
+                                _ptr(x_q), _ptr(s_x), _stream(stream)))
+    return x_q, s_x
+
+
 def quantize_weight(W: torch.Tensor, bits: int = 8, group_size: int = 0, stream=None):
     """W fp32 [N, K] -> (w_q, s_w); int8 [N, K] or packed uint8 [N, K/2]."""
     if W.dtype != torch.float32 or W.dim() != 2 or not W.is_contiguous():
@@ -223,6 +247,16 @@ def w4a8_gemm_pg(x_q, s_x, w_packed, s_w, group_size, out_dtype=torch.float16, y
     y = _out(y, M, N, out_dtype, x_q.device)
     _check(_lib.w4a8_gemm_pg(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(s_w), group_size, _ptr(y),
                              _DTYPE_CODE[y.dtype], M, N, K, y.stride(0), _stream(stream)))
+    return y
+
+
+def w4a8_gemm_pc(x_q, s_x, w_packed, s_w, out_dtype=torch.float16, y=None, stream=None):
+    """W4A8 with per-column int4 weights: one scale per output channel, s_w [N]."""
+    M, K = x_q.shape
+    N = w_packed.shape[0]
+    y = _out(y, M, N, out_dtype, x_q.device)
+    _check(_lib.w4a8_gemm_pc(_ptr(x_q), _ptr(s_x), _ptr(w_packed), _ptr(s_w), _ptr(y), _DTYPE_CODE[y.dtype], M, N, K,
+                             y.stride(0), _stream(stream)))
     return y
 
 

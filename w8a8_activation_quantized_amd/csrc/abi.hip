@@ -147,7 +147,7 @@ w8a8::GemmProblem make_problem(const int8_t *x_q, const float *s_x, const void *
 int run_gemm(const char *fn, const int8_t *x_q, const float *s_x, const void *w, const float *s_w,
              int gs, int wkind, void *y, int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy,
              void *stream) {
-    int rc = check_gemm(fn, x_q, s_x, w, s_w, gs, y, y_dtype, M, N, K, ldy, gs != 0 || wkind == w8a8::W_INT4);
+    int rc = check_gemm(fn, x_q, s_x, w, s_w, gs, y, y_dtype, M, N, K, ldy, gs != 0);
     if (rc != W8A8_OK) return rc;
     if ((rc = check_device()) != W8A8_OK) return rc;
     if (M == 0) return ok();
@@ -260,14 +260,38 @@ int rmsnorm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t l
                     fn);
 }
 
+int swiglu_quantize(const void *gate, const void *up, int dtype, int64_t M, int64_t I, int64_t ldg, int64_t ldu,
+                    int8_t *x_q, float *s_x, void *stream) {
+    const char *fn = "swiglu_quantize";
+    if (dtype != W8A8_F16 && dtype != W8A8_BF16)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: dtype must be F16 or BF16", fn);
+    if (M < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: M = %lld < 0", fn, (long long)M);
+    if (I < 8 || I % 8 != 0)
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: I = %lld must be a positive multiple of 8", fn, (long long)I);
+    if (M > INT32_MAX || I > INT32_MAX || M * I > ((int64_t)1 << 40))
+        return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: sizes too large", fn);
+    if (ldg < I || ldg % 8 != 0 || ldu < I || ldu % 8 != 0)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldg = %lld, ldu = %lld must be >= I and multiples of 8", fn,
+                    (long long)ldg, (long long)ldu);
+    if (M > 0) {
+        if (!gate || !up || !x_q || !s_x) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+        if (!aligned16(gate) || !aligned16(up) || !aligned16(x_q) || !aligned16(s_x))
+            return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    }
+    int rc = check_device();
+    if (rc != W8A8_OK) return rc;
+    if (M == 0) return ok();
+    return launched(w8a8::launch_swiglu_quantize(gate, ldg, up, ldu, dtype == W8A8_BF16, (int)M, (int)I, x_q, s_x,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int quantize_weight(const float *W, int64_t N, int64_t K, int bits, int group_size, void *w_q,
                     float *s_w, void *stream) {
     const char *fn = "quantize_weight";
     if (bits != 8 && bits != 4) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: bits must be 8 or 4", fn);
     if (group_size != 0 && group_size != 64 && group_size != 128)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
-    if (bits == 4 && group_size == 0)
-        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
     if (N < 1) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: N = %lld < 1", fn, (long long)N);
     if (K < 64 || K % 64 != 0)
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 64", fn,
@@ -294,8 +318,6 @@ int quantize_weight_clipped(const float *W, int64_t N, int64_t K, int bits, int 
     if (bits != 8 && bits != 4) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: bits must be 8 or 4", fn);
     if (group_size != 0 && group_size != 64 && group_size != 128)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
-    if (bits == 4 && group_size == 0)
-        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
     if (N < 1) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: N = %lld < 1", fn, (long long)N);
     if (K < 64 || K % 64 != 0)
         return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "%s: K = %lld must be a positive multiple of 64", fn,
@@ -337,14 +359,17 @@ int w4a8_gemm_pg(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, c
                     K, ldy, stream);
 }
 
+int w4a8_gemm_pc(const int8_t *x_q, const float *s_x, const uint8_t *w_packed, const float *s_w, void *y,
+                 int y_dtype, int64_t M, int64_t N, int64_t K, int64_t ldy, void *stream) {
+    return run_gemm("w4a8_gemm_pc", x_q, s_x, w_packed, s_w, 0, w8a8::W_INT4, y, y_dtype, M, N, K, ldy, stream);
+}
+
 // Validation shared by the split-K query and call: weight_bits / group_size as for w8a8_linear.
 static int check_split_kind(const char *fn, int weight_bits, int group_size) {
     if (weight_bits != 8 && weight_bits != 4)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: weight_bits must be 8 or 4", fn);
     if (group_size != 0 && group_size != 64 && group_size != 128)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
-    if (weight_bits == 4 && group_size == 0)
-        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
     return W8A8_OK;
 }
 
@@ -363,15 +388,12 @@ int w8a8_linear(const void *x, int x_dtype, int64_t ldx, const void *w, const fl
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: weight_bits must be 8 or 4", fn);
     if (group_size != 0 && group_size != 64 && group_size != 128)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: group_size must be 0, 64 or 128", fn);
-    if (weight_bits == 4 && group_size == 0)
-        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: int4 weights need group_size 64 or 128", fn);
     if (y_dtype == W8A8_I32)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: y_dtype must be F16, BF16 or F32", fn);
     if (ldx < K || ldx % 8 != 0)
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: ldx = %lld must be >= K and a multiple of 8", fn,
                     (long long)ldx);
-    int rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy,
-                        group_size != 0 || weight_bits == 4);
+    int rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0);
     if (rc != W8A8_OK) return rc;
     if (M > 0 && (!x || !aligned16(x)))
         return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: x must be a non-null 16-byte aligned pointer", fn);
@@ -493,7 +515,7 @@ int64_t w8a8_gemm_splitk_workspace(int weight_bits, int group_size, int y_dtype,
                                    int64_t K) {
     const char *fn = "w8a8_gemm_splitk_workspace";
     int rc = check_split_kind(fn, weight_bits, group_size);
-    if (rc == W8A8_OK) rc = check_gemm_shape(fn, group_size, y_dtype, M, N, K, N, group_size != 0 || weight_bits == 4);
+    if (rc == W8A8_OK) rc = check_gemm_shape(fn, group_size, y_dtype, M, N, K, N, group_size != 0);
     if (rc != W8A8_OK) return -(int64_t)rc;
     ok();
     if (M == 0) return 0;
@@ -509,7 +531,7 @@ int w8a8_gemm_splitk(const int8_t *x_q, const float *s_x, const void *w, const f
     const char *fn = "w8a8_gemm_splitk";
     int rc = check_split_kind(fn, weight_bits, group_size);
     if (rc != W8A8_OK) return rc;
-    rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0 || weight_bits == 4);
+    rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0);
     if (rc != W8A8_OK) return rc;
     if (workspace_bytes < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace_bytes < 0", fn);
     if (workspace && !aligned16(workspace))
@@ -534,7 +556,7 @@ int w8a8_gemm_splitk_noalloc(const int8_t *x_q, const float *s_x, const void *w,
     const char *fn = "w8a8_gemm_splitk_noalloc";
     int rc = check_split_kind(fn, weight_bits, group_size);
     if (rc != W8A8_OK) return rc;
-    rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0 || weight_bits == 4);
+    rc = check_gemm(fn, x_q, s_x, w, s_w, group_size, y, y_dtype, M, N, K, ldy, group_size != 0);
     if (rc != W8A8_OK) return rc;
     if ((rc = check_device()) != W8A8_OK) return rc;
     if (M == 0) return ok();

@@ -854,6 +854,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
 // exactly while no value is subnormal (a power-of-two scaling commutes with rounding in
 // the normal range; every product of a nonzero sum and a scale >= 2^-100 is normal).
 // The epilogue multiplies by 2^-4 (exact) before s_x.
+//
+// GS = 0: per-channel weight scales (int4 weights of one scale per output channel, Cider
+// README "量化": per-column INT4; or the raw int32 sums of int4 weights): no fold, the int32
+// sums run over all of K (16 x the sums for int4, exactly: |16 acc| <= 16 K 127 8 < 2^31 for
+// K <= 131072, which the launcher checks), shifted right by 4 (exact) and dequantized as the
+// per-channel kernels do, y = (fp32(acc) * s_x[m]) * s_w[n].
 template <int BN_, int BM_, int STAGES_, int WGN_, int WGM_, int GS_, int WK_>
 struct MgShape {
     static constexpr int BN = BN_, BM = BM_, BK = 128, STAGES = STAGES_, WGN = WGN_, WGM = WGM_, GS = GS_, WK = WK_;
@@ -862,14 +868,15 @@ struct MgShape {
     static constexpr int FM = WM / 16, FN = WN / 16;
     static constexpr int WB = WK == W_INT4 ? 64 : 128;        // weight bytes per row per K-tile
     static constexpr int W_TILE = BN * WB, X_TILE = BM * BK;
-    static constexpr int GPK = BK / GS;                         // groups per K-tile (1 or 2)
+    static constexpr bool PC = GS == 0;                         // per-channel scales: no fold
+    static constexpr int GPK = PC ? 0 : BK / GS;                // groups per K-tile (1 or 2)
     static constexpr int SCALES = GPK * BN * 4;
     static constexpr int STAGE = W_TILE + X_TILE + SCALES;
     static constexpr int WG = W_TILE / 1024, XG = X_TILE / 1024;  // 1 KiB DMA pieces per stage
     static constexpr int NG = WG + XG;
-    static constexpr int NSD = GPK * BN / 64;                   // 4-byte scale DMAs per stage
+    static constexpr int NSD = GPK * BN / 64;                   // 4-byte scale DMAs per stage (none for PC)
     static constexpr int GPW = (NG + NW - 1) / NW;              // tile DMAs per wave (max)
-    static_assert(GS == 64 || GS == 128, "group size");
+    static_assert(GS == 0 || GS == 64 || GS == 128, "group size");
     static_assert(BN % 64 == 0 && BM % 8 == 0 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
     static_assert(W_TILE % 1024 == 0 && NSD <= NW, "loader shape");
     static_assert(STAGES * STAGE <= 163840, "LDS");
@@ -897,7 +904,7 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
 template <class S>
 __device__ __forceinline__ void mg_issue(const GemmProblem &p, int m0, int n0, int kt, int8_t *st, int wave,
                                          int lane) {
-    const int G = p.K / S::GS;
+    const int G = S::PC ? 1 : p.K / (S::PC ? 1 : S::GS);
 #pragma unroll
     for (int j = 0; j < S::GPW; ++j) {
         const int g = wave + j * S::NW;
@@ -919,7 +926,7 @@ __device__ __forceinline__ void mg_issue(const GemmProblem &p, int m0, int n0, i
             }
         }
     }
-    if (wave < S::NSD) {
+    if (!S::PC && wave < S::NSD) {
         // scales [gi][n] of this K-tile: gather gi = wave / (BN / 64), n block wave % (BN / 64)
         const int gi = wave / (S::BN / 64), nb = wave % (S::BN / 64);
         const int n = min(n0 + nb * 64 + lane, p.N - 1);
@@ -932,7 +939,7 @@ __device__ __forceinline__ int mg_ops_per_stage(int wave) {
     int n = 0;
 #pragma unroll
     for (int j = 0; j < S::GPW; ++j) n += (wave + j * S::NW < S::NG) ? 1 : 0;
-    return n + (wave < S::NSD ? 1 : 0);
+    return n + (!S::PC && wave < S::NSD ? 1 : 0);
 }
 
 // Weight fragments as read from LDS: int8 codes (v4i), or for int4 the lane's 16 packed
@@ -1025,6 +1032,96 @@ __device__ __forceinline__ void mg_scales(const int8_t *st, int gi, int wn, int 
     for (int fn = 0; fn < S::FN; ++fn) sw[fn] = *reinterpret_cast<const float4 *>(sc + wn * S::WN + fn * 16 + 4 * fchunk);
 }
 
+// Per-channel epilogue of the GS = 0 form: the int32 sums (16 x the sums for int4 weights,
+// shifted back exactly) dequantized as y = (fp32(acc) * s_x[m]) * s_w[n], or stored raw for
+// I32 output; SPLIT stores the slice's int32 sums to p.ws for splitk_finish_kernel.
+template <class S, bool SPLIT>
+__device__ __forceinline__ void mg_pc_epilogue(const GemmProblem &p, v4i (&acc)[S::FN][S::FM], int8_t *smem, int m0,
+                                               int n0, int wm, int wn, int frow, int fchunk, int tid, int ks) {
+    constexpr int FM = S::FM, FN = S::FN;
+    const int M = p.M, N = p.N;
+    if constexpr (S::WK == W_INT4) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = acc[fn][fm] >> 4;
+    }
+    if constexpr (SPLIT) {
+        int32_t *ws = static_cast<int32_t *>(p.ws) + (int64_t)ks * M * N;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + wm * S::WM + fm * 16 + frow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+                if (n >= N) continue;
+                const v4i v = acc[fn][fm];
+                *reinterpret_cast<int4 *>(ws + (int64_t)m * N + n) = make_int4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        return;
+    }
+    const float *__restrict__ sxp = p.sx;
+    const float *__restrict__ swp = p.sw;
+    float sxm[FM];
+    float4 s4[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sxm[fm] = sxp[min(m0 + wm * S::WM + fm * 16 + frow, M - 1)];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        s4[fn] = *reinterpret_cast<const float4 *>(swp + min(n0 + wn * S::WN + fn * 16 + 4 * fchunk, N - 4));
+    const int out = p.out;
+    if ((out == OUT_F16 || out == OUT_BF16) && p.y_rows16) {
+        constexpr int RS = S::BM * (S::BN * 2 + 16) <= S::STAGES * S::STAGE ? S::BN * 2 + 16 : S::BN * 2;
+        static_assert(S::BM * S::BN * 2 <= S::STAGES * S::STAGE, "staged output tile must fit the LDS buffers");
+        lds_barrier();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int lr = wm * S::WM + fm * 16 + frow;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const v4i v = acc[fn][fm];
+                const float y0 = ((float)v[0] * sxm[fm]) * s4[fn].x, y1 = ((float)v[1] * sxm[fm]) * s4[fn].y;
+                const float y2 = ((float)v[2] * sxm[fm]) * s4[fn].z, y3 = ((float)v[3] * sxm[fm]) * s4[fn].w;
+                const uint2 w = out == OUT_F16 ? make_uint2(f16_bits(y0) | (f16_bits(y1) << 16), f16_bits(y2) | (f16_bits(y3) << 16))
+                                               : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
+                *reinterpret_cast<uint2 *>(smem + lr * RS + 2 * (wn * S::WN + fn * 16 + 4 * fchunk)) = w;
+            }
+        }
+        lds_barrier();
+        constexpr int CPR = S::BN / 8;
+        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
+#pragma unroll 4
+        for (int c = tid; c < S::BM * CPR; c += S::NT) {
+            const int r = c / CPR, cc = c - r * CPR;
+            if (r < rows && cc * 8 < cols) {
+                const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
+                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm * S::WM + fm * 16 + frow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + wn * S::WN + fn * 16 + 4 * fchunk;
+            if (n >= N) continue;
+            const int64_t off = (int64_t)m * p.ldy + n;
+            const v4i v = acc[fn][fm];
+            if (out == OUT_I32) {
+                *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = make_int4(v[0], v[1], v[2], v[3]);
+            } else {
+                store4(p.y, off, out, ((float)v[0] * sxm[fm]) * s4[fn].x, ((float)v[1] * sxm[fm]) * s4[fn].y,
+                       ((float)v[2] * sxm[fm]) * s4[fn].z, ((float)v[3] * sxm[fm]) * s4[fn].w);
+            }
+        }
+    }
+}
+
 // SPLIT: one K-slice per workgroup; the slice's fold t (times 2^-4 for int4) goes to p.ws as
 // fp32, and the slices are added and scaled by s_x afterwards.
 template <int BN, int BM, int STAGES, int WGN, int WGM, int GS, int WK, bool SPLIT>
@@ -1085,10 +1182,14 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
         const int8_t *st = smem + cur * S::STAGE;
         // everything this wave still needs from stage kt is read before its barrier
         mg_frags<S>(st, 1, wm, wn, frow, fchunk, r1, b1);
-        // K-step 0 opens group kt (gs 128) or 2 kt (gs 64) while the previous group is folded
-        mg_fold_mma<S>(acc, S::GPK == 2 ? sw1 : sw0, t, a0, b0);
-        mg_scales<S>(st, 0, wn, fchunk, sw0);
-        if constexpr (S::GPK == 2) mg_scales<S>(st, 1, wn, fchunk, sw1);
+        if constexpr (S::PC) {
+            mg_mma<S, false>(acc, a0, b0);
+        } else {
+            // K-step 0 opens group kt (gs 128) or 2 kt (gs 64) while the previous group is folded
+            mg_fold_mma<S>(acc, S::GPK == 2 ? sw1 : sw0, t, a0, b0);
+            mg_scales<S>(st, 0, wn, fchunk, sw0);
+            if constexpr (S::GPK == 2) mg_scales<S>(st, 1, wn, fchunk, sw1);
+        }
         wait_lgkmcnt0();
         mg_unpack<S>(r1, a1);
         if (kt + 1 < KT) {
@@ -1107,6 +1208,10 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
         }
         wait_lgkmcnt0();
         mg_unpack<S>(r0, a0);
+    }
+    if constexpr (S::PC) {
+        mg_pc_epilogue<S, SPLIT>(p, acc, smem, m0, n0, wm, wn, frow, fchunk, tid, ks);
+        return;
     }
     mg_fold<S>(acc, S::GPK == 2 ? sw1 : sw0, t);  // the last group
 
@@ -1930,7 +2035,7 @@ hipError_t linear_small_fq(const GemmProblem &p, hipStream_t stream) {
     if (p.wkind == W_INT4) {
         if (gs == 64) return launch_gemv_dma_x<64, W_INT4, true, FQ>(p, stream);
         if (gs == 128) return launch_gemv_dma_x<128, W_INT4, true, FQ>(p, stream);
-        return hipErrorNotSupported;
+        return launch_gemv_dma_x<0, W_INT4, true, FQ>(p, stream);
     }
     if (gs == 64) return launch_gemv_dma_x<64, W_INT8, true, FQ>(p, stream);
     if (gs == 128) return launch_gemv_dma_x<128, W_INT8, true, FQ>(p, stream);
@@ -2093,6 +2198,13 @@ hipError_t launch_mg(const GemmProblem &p, int group_m, hipStream_t stream) {
 // Per-group / W4A8 on the DMA pipeline: 128 x 256 tiles, or 64 x 64 for small M.
 template <bool SPLIT = false>
 hipError_t dispatch_mg(const GemmProblem &p, bool small, int group_m, hipStream_t stream) {
+    if (p.gs == 0 || p.out == OUT_I32) {
+        // per-channel scales or the raw int32 sums: the GS = 0 form, int4 weights only
+        // (int8 weights take the per-channel kernels)
+        if (p.wkind != W_INT4) return hipErrorInvalidValue;
+        return small ? launch_mg<64, 64, 4, 2, 2, 0, W_INT4, SPLIT>(p, group_m, stream)
+                     : launch_mg<128, 256, 3, 2, 4, 0, W_INT4, SPLIT>(p, group_m, stream);
+    }
     if (small) {
         if (p.wkind == W_INT4)
             return p.gs == 64 ? launch_mg<64, 64, 4, 2, 2, 64, W_INT4, SPLIT>(p, group_m, stream)
@@ -2108,11 +2220,28 @@ hipError_t dispatch_mg(const GemmProblem &p, bool small, int group_m, hipStream_
     return launch_mg<128, 256, 3, 2, 4, 128, W_INT8, SPLIT>(p, group_m, stream);
 }
 
+// Largest K for the GS = 0 form of gemm_mg_kernel with int4 weights: its int32 sums are 16 x
+// the integer products, |16 sum| <= 16 K 127 8 < 2^31.
+constexpr int kMgPcMaxK = 131072;
+
+// The GS = 0 form of gemm_mg_kernel serves int4 weights with per-channel scales, and the raw
+// int32 sums of int4 weights.
+bool mg_per_channel(const GemmProblem &p) {
+    return p.wkind == W_INT4 && (p.gs == 0 || p.out == OUT_I32) && p.K % 128 == 0 && p.K <= kMgPcMaxK;
+}
+
 int choose_config(const GemmProblem &p) {
     // Measured on MI355X (fp16 out, M = 32 .. 8192, N = 2560 .. 12288, K = 2560 .. 12288).
     if (p.M <= 16) return 10;  // weight-streaming GEMV
     const bool dma = p.K % 128 == 0;
     const int64_t cus = num_cus();
+    if (mg_per_channel(p)) {
+        // int4 weights, one scale per output channel: the per-group DMA kernels without the
+        // fold, chosen as for per-group int4 weights
+        const int64_t t11 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
+        if (t11 >= cus / 2) return 11;
+        return p.M <= 1024 ? 12 : 4;
+    }
     if (p.gs > 0 && p.out != OUT_I32) {
         // per-group: the 128 x 256 DMA kernel once it has enough tiles to spread over the
         // chip, else 64 x 64 DMA tiles up to M = 768 (int8) / 1024 (int4), else the
@@ -2311,7 +2440,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         id = 4;
     }
     const bool grouped = p.gs > 0 && p.out != OUT_I32;
-    if (grouped && (id == 11 || id == 12) && p.K % 128 == 0)
+    if ((grouped || mg_per_channel(p)) && (id == 11 || id == 12) && p.K % 128 == 0)
         return dispatch_mg(p, id == 12, kConfigs[id].group_m, stream);
     if (grouped) {
         if (id != 4) id = 0;
