@@ -379,7 +379,13 @@ def qwen3_block(args, torch, w8a8):
     """One Qwen3-8B-shaped decoder block's seven linears at prefill (M=2048 tokens), W8A8
     per-channel, bf16 out: each of the four block inputs is quantized once per step; q, k,
     v share one GEMM over their concatenated weights (N = 6144) and gate, up another
-    (N = 24576): exact, since per-channel weight scales belong to output rows."""
+    (N = 24576): exact, since per-channel weight scales belong to output rows.
+
+    A second chain times the same GEMMs with the producers writing their int8 inputs: the
+    RMSNorm in front of q/k/v and of gate/up (rmsnorm_quantize, from the residual stream)
+    and the SwiGLU between gate/up and down (swiglu_quantize, from the gate/up GEMM's bf16
+    output); the attention output keeps quantize_per_token. Both chains are reported, with
+    the time of their four quantization-side kernels."""
     from synth_inputs import qwen3_8b_block_inputs, QWEN3_8B_BLOCK
 
     M = 2048
@@ -398,30 +404,63 @@ def qwen3_block(args, torch, w8a8):
                        "sx": torch.empty((M,), dtype=torch.float32, device="cuda"),
                        "y": torch.empty((M, N), dtype=torch.bfloat16, device="cuda")})
     del inputs, weights
+    qkv, o, gu, down = stages
+    I = down["K"]
+    # norm weights of the two RMSNorms (near one, as trained ones are)
+    rng = np.random.default_rng(1)
+    g_attn = torch.from_numpy((1 + 0.1 * rng.standard_normal(qkv["K"])).astype(np.float16)).cuda()
+    g_mlp = torch.from_numpy((1 + 0.1 * rng.standard_normal(gu["K"])).astype(np.float16)).cuda()
+    eps = 1e-6
 
-    def run(st, stream):
-        w8a8.quantize_per_token(st["x"], st["xq"], st["sx"], stream=stream)
+    def gemm(st, stream):
         w8a8.w8a8_gemm_pc(st["xq"], st["sx"], st["wq"], st["sw"], y=st["y"], stream=stream)
 
-    def step(i):
-        cur = torch.cuda.current_stream()
-        for st in stages:
-            run(st, cur)
+    quant = {  # the quantization-side kernel of each stage, per chain
+        "standalone": [lambda st_, cur: w8a8.quantize_per_token(st_["x"], st_["xq"], st_["sx"], stream=cur)] * 4,
+        "producers": [
+            lambda st_, cur: w8a8.rmsnorm_quantize(st_["x"], g_attn, eps, st_["xq"], st_["sx"], stream=cur),
+            lambda st_, cur: w8a8.quantize_per_token(st_["x"], st_["xq"], st_["sx"], stream=cur),
+            lambda st_, cur: w8a8.rmsnorm_quantize(st_["x"], g_mlp, eps, st_["xq"], st_["sx"], stream=cur),
+            lambda st_, cur: w8a8.swiglu_quantize(gu["y"][:, :I], gu["y"][:, I:], st_["xq"], st_["sx"], stream=cur),
+        ],
+    }
 
-    ms_per_step, event_ms = timed_steps(args, torch, step)
-    value = ops / (ms_per_step * 1e-3) / 1e12
-    # dominant kernel: the gate+up GEMM (N = 24576, 52 % of the block's operations)
-    big = max(stages, key=lambda st: st["N"] * st["K"])
+    def make_step(chain):
+        def step(i):
+            cur = torch.cuda.current_stream()
+            for st, q in zip(stages, quant[chain]):
+                q(st, cur)
+                gemm(st, cur)
+        return step
+
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        w8a8.w8a8_gemm_pc(big["xq"], big["sx"], big["wq"], big["sw"], y=big["y"], stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    gemm_ms = e0.elapsed_time(e1) / args.steps
-    big_ops = 2.0 * M * big["N"] * big["K"]
+
+    def launch_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_per_step, event_ms = timed_steps(args, torch, make_step("standalone"), w8a8)
+    sclk = dict(CLOCK) or None
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    prod_ms, prod_event_ms = timed_steps(args, torch, make_step("producers"), w8a8)
+    chains = {}
+    for chain in ("standalone", "producers"):
+        kernels = [launch_ms(lambda st=st, q=q: q(st, stream)) for st, q in zip(stages, quant[chain])]
+        chains[chain] = {"quantize_side_us": [k * 1e3 for k in kernels], "quantize_side_total_us": sum(kernels) * 1e3}
+    chains["standalone"].update({"ms_per_step": ms_per_step, "tops": value,
+                                 "kernels": "quantize_per_token x4"})
+    chains["producers"].update({"ms_per_step": prod_ms, "tops": ops / (prod_ms * 1e-3) / 1e12,
+                                "kernels": "rmsnorm_quantize (q|k|v), quantize_per_token (o), rmsnorm_quantize "
+                                           "(gate|up), swiglu_quantize (down, from the gate|up output)"})
+    # dominant kernel: the gate+up GEMM (N = 24576, 52 % of the block's operations)
+    gemm_ms = launch_ms(lambda: gemm(gu, stream))
+    big_ops = 2.0 * M * gu["N"] * gu["K"]
     achieved = big_ops / (gemm_ms * 1e-3) / 1e12
     result = {
         "metric": "INT8 TOPS of one Qwen3-8B block's seven W8A8 linears (quantize + GEMM + dequant), M=2048",
@@ -433,10 +472,11 @@ def qwen3_block(args, torch, w8a8):
                    "M": M, "shapes_NK": [[st["N"], st["K"]] for st in stages], "out": "bf16",
                    "parallelism": "single GPU"},
         "frac_of_peak_step": value / PEAK_INT8_TOPS,
-        "step_event_ms": event_ms,
+        "step_event_ms": event_ms, "sclk": sclk,
+        "chains": chains,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                      "frac": achieved / PEAK_INT8_TOPS, "traffic": None,
-                     "kernel": f"gemm ({big['name']}: M={M} N={big['N']} K={big['K']})", "launch_ms": gemm_ms},
+                     "kernel": f"gemm ({gu['name']}: M={M} N={gu['N']} K={gu['K']})", "launch_ms": gemm_ms},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = qwen3_cpu_baseline(stages, args.cpu_seconds)

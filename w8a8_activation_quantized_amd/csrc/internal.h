@@ -42,6 +42,11 @@ hipError_t launch_quantize_per_token(const void *x, bool bf16, int64_t ldx, int 
 hipError_t launch_rmsnorm_quantize(const void *x, bool x_bf16, int64_t ldx, const void *g, bool g_bf16, float eps,
                                    int M, int K, int8_t *xq, float *sx, hipStream_t stream);
 
+// SwiGLU producer: codes and per-token scale of h = silu(gate) * up (fp16 / bf16 rows of I
+// values, row strides ldg / ldu elements).
+hipError_t launch_swiglu_quantize(const void *gate, int64_t ldg, const void *up, int64_t ldu, bool bf16, int M, int I,
+                                  int8_t *xq, float *sx, hipStream_t stream);
+
 // Offline weight quantization.
 hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
                                   float *sw, hipStream_t stream);

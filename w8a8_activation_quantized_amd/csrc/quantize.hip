@@ -326,6 +326,140 @@ hipError_t launch_norm_rows(const void *x, int64_t ldx, const void *g, float eps
     return hipGetLastError();
 }
 
+// ---- SwiGLU with the per-token quantization folded in ---------------------------------
+// The producer of the down projection's input in a gated MLP writes that input's codes
+// directly (Cider README "Metal Kernel 流水线": the quantization is otherwise a dispatch of
+// its own; juejin post, "W8A8 对称量化": it must stay cheap): h = silu(gate) * up in fp32,
+// then the per-token quantization of h, with h held in registers between the pass that finds
+// max|h| and the pass that writes the codes. silu(g) = g / (1 + e^-g) uses one fixed fp32
+// evaluation of e^x, so that the codes are reproducible bit for bit by any implementation of
+// the same steps: the argument clamped to [-87, 88]; Cody-Waite reduction x = k ln 2 + r,
+// k = rint(x log2 e), r by two fmas against ln 2 split into its fp32 rounding and the
+// rounding of the remainder; e^r by the degree-7 Taylor polynomial (1 / n! in fp32), Horner
+// with fmas; times 2^k built from its exponent bits. Division g / (1 + e) is IEEE; the
+// quotient h / s of the codes is the corrected reciprocal of the quantize kernel.
+
+__device__ __forceinline__ float exp_fixed(float x) {
+    x = __builtin_amdgcn_fmed3f(x, -87.0f, 88.0f);
+    const float k = __builtin_rintf(x * 0x1.715476p+0f);   // log2 e
+    float r = __builtin_fmaf(-k, 0x1.62e43p-1f, x);         // ln 2, high part
+    r = __builtin_fmaf(-k, -0x1.05c61p-29f, r);             // ln 2, low part
+    float p = 0x1.a01a02p-13f;                              // 1/7!
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);              // 1/6!
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);               // 1/5!
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);               // 1/4!
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);               // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return p * __builtin_bit_cast(float, (uint32_t)((int)k + 127) << 23);  // k in [-126, 127]
+}
+
+// h = silu(g) * u for the eight values of one 16-byte chunk of gate and of up.
+template <bool BF16>
+__device__ __forceinline__ void swiglu_h8(uint4 gc, uint4 uc, float (&h)[8]) {
+    const uint32_t gw[4] = {gc.x, gc.y, gc.z, gc.w}, uw[4] = {uc.x, uc.y, uc.z, uc.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float g = to_float<BF16>(e ? gw[i] >> 16 : gw[i] & 0xffffu);
+            const float u = to_float<BF16>(e ? uw[i] >> 16 : uw[i] & 0xffffu);
+            const float silu = g / (1.0f + exp_fixed(-g));
+            h[2 * i + e] = silu * u;
+        }
+}
+
+template <bool BF16, bool FAST, int CPT>
+__device__ __forceinline__ void swiglu_row_store(const float (&hc)[CPT][8], const uint16_t *grow, const uint16_t *urow,
+                                                 int8_t *qrow, int tid, int nch, float s, float r) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + NORM_THREADS * j;
+        if (c < nch) *reinterpret_cast<uint2 *>(qrow + 8 * c) = norm_quant8<FAST>(hc[j], s, r);
+    }
+    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS) {
+        float h[8];
+        swiglu_h8<BF16>(*reinterpret_cast<const uint4 *>(grow + 8 * c), *reinterpret_cast<const uint4 *>(urow + 8 * c), h);
+        *reinterpret_cast<uint2 *>(qrow + 8 * c) = norm_quant8<FAST>(h, s, r);
+    }
+}
+
+// A row per 256-thread workgroup: thread t takes the 16-byte chunks t + 256 j and holds h of
+// the first CPT of them in registers (recomputing the rest); the four waves combine max|h|
+// through LDS.
+template <int CPT, bool BF16>
+__global__ __launch_bounds__(NORM_THREADS) void swiglu_quantize_kernel(const uint16_t *__restrict__ gate, int64_t ldg,
+                                                                        const uint16_t *__restrict__ up, int64_t ldu,
+                                                                        int I, int8_t *__restrict__ xq,
+                                                                        float *__restrict__ sx) {
+    __shared__ uint32_t wmax[NORM_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = blockIdx.x;
+    const uint16_t *grow = gate + (int64_t)m * ldg, *urow = up + (int64_t)m * ldu;
+    int8_t *qrow = xq + (int64_t)m * I;
+    const int nch = I >> 3;
+
+    float hc[CPT][8];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + NORM_THREADS * j;
+        if (c < nch) {
+            swiglu_h8<BF16>(*reinterpret_cast<const uint4 *>(grow + 8 * c), *reinterpret_cast<const uint4 *>(urow + 8 * c),
+                            hc[j]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t hb = __builtin_bit_cast(uint32_t, hc[j][e]) & 0x7fffffffu;
+                amax = amax > hb ? amax : hb;
+            }
+        }
+    }
+    for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS) {
+        float h[8];
+        swiglu_h8<BF16>(*reinterpret_cast<const uint4 *>(grow + 8 * c), *reinterpret_cast<const uint4 *>(urow + 8 * c), h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t hb = __builtin_bit_cast(uint32_t, h[e]) & 0x7fffffffu;
+            amax = amax > hb ? amax : hb;
+        }
+    }
+    amax = wave_max_u32(amax);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NORM_THREADS / 64; ++w) amax = amax > wmax[w] ? amax : wmax[w];
+
+    const float s = __builtin_bit_cast(float, amax) / 127.0f;
+    if (tid == 0) sx[m] = s;
+    if (s == 0.0f) {
+        for (int c = tid; c < nch; c += NORM_THREADS) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
+        return;
+    }
+    if (s >= kMinFastScale)
+        swiglu_row_store<BF16, true, CPT>(hc, grow, urow, qrow, tid, nch, s, 1.0f / s);
+    else
+        swiglu_row_store<BF16, false, CPT>(hc, grow, urow, qrow, tid, nch, s, 0.f);
+}
+
+template <bool BF16>
+hipError_t launch_swiglu_rows(const void *gate, int64_t ldg, const void *up, int64_t ldu, int M, int I, int8_t *xq,
+                              float *sx, hipStream_t stream) {
+    const int per_thread = (I / 8 + NORM_THREADS - 1) / NORM_THREADS;
+    dim3 grid(M), block(NORM_THREADS);
+    const uint16_t *gp = static_cast<const uint16_t *>(gate), *up_ = static_cast<const uint16_t *>(up);
+#define W8A8_SWIGLU_LAUNCH(C) \
+    hipLaunchKernelGGL((swiglu_quantize_kernel<C, BF16>), grid, block, 0, stream, gp, ldg, up_, ldu, I, xq, sx)
+    if (per_thread <= 1) W8A8_SWIGLU_LAUNCH(1);
+    else if (per_thread <= 2) W8A8_SWIGLU_LAUNCH(2);
+    else if (per_thread <= 4) W8A8_SWIGLU_LAUNCH(4);
+    else if (per_thread <= 6) W8A8_SWIGLU_LAUNCH(6);
+    else W8A8_SWIGLU_LAUNCH(8);
+#undef W8A8_SWIGLU_LAUNCH
+    return hipGetLastError();
+}
+
 // ---- offline weight quantization ------------------------------------------------------
 // One wavefront per run (a weight row for per-channel, one K-group for per-group).
 // Min-max symmetric (Cider README "说明"): s = max|W| / qdiv, q = clamp(rne(W / s)).
@@ -468,6 +602,12 @@ hipError_t launch_rmsnorm_quantize(const void *x, bool x_bf16, int64_t ldx, cons
                               : launch_norm_rows<true, false>(x, ldx, g, eps, M, K, xq, sx, stream);
     return g_bf16 ? launch_norm_rows<false, true>(x, ldx, g, eps, M, K, xq, sx, stream)
                   : launch_norm_rows<false, false>(x, ldx, g, eps, M, K, xq, sx, stream);
+}
+
+hipError_t launch_swiglu_quantize(const void *gate, int64_t ldg, const void *up, int64_t ldu, bool bf16, int M, int I,
+                                  int8_t *xq, float *sx, hipStream_t stream) {
+    return bf16 ? launch_swiglu_rows<true>(gate, ldg, up, ldu, M, I, xq, sx, stream)
+                : launch_swiglu_rows<false>(gate, ldg, up, ldu, M, I, xq, sx, stream);
 }
 
 hipError_t launch_quantize_weight(const float *W, int N, int K, int bits, int gs, void *wq,
