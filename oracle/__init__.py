@@ -41,8 +41,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        # W8A8_ORACLE_LIB: another build of oracle.c (the sanitizer tests load one built
+        # with AddressSanitizer and UndefinedBehaviorSanitizer)
+        path = os.environ.get("W8A8_ORACLE_LIB")
+        if not path:
+            path = build(force=False)
+        lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_quantize_per_token.argtypes = [vp, i32, i64, i64, i64, vp, vp]
         lib.oracle_quantize_weight.argtypes = [vp, i64, i64, i32, i32, vp, vp]

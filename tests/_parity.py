@@ -49,9 +49,11 @@ def check_output(y_gpu: np.ndarray, fmt: str, y64: np.ndarray, mag: np.ndarray, 
             f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance; first at {tuple(i)}: "
             f"gpu={yg[tuple(i)]!r} ref={y64[tuple(i)]!r} tol={tol[tuple(i)]!r}")
     if fmt == "f16":
-        # rounding mode: almost every output must equal the correctly rounded reference
-        exact = (y_gpu == y64.astype(np.float16)).mean()
-        assert exact >= 0.99, f"{what}: only {exact:.4f} of fp16 outputs are RNE(y64)"
+        # rounding mode: almost every output must equal the correctly rounded reference (an
+        # fp32 evaluation rounds differently from the fp64 value at a few outputs; on small
+        # outputs one or two of them are more than 1 %)
+        miss = int((y_gpu != y64.astype(np.float16)).sum())
+        assert miss <= max(2, 0.01 * y_gpu.size), f"{what}: {miss} of {y_gpu.size} fp16 outputs are not RNE(y64)"
     return float(err.max()) if err.size else 0.0
 
 

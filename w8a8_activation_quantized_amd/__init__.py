@@ -16,7 +16,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libw8a8.so")
+# W8A8_LIB names another build of the same library (the sanitizer tests load a build whose
+# host code carries AddressSanitizer and UndefinedBehaviorSanitizer)
+LIB_PATH = os.environ.get("W8A8_LIB") or os.path.join(_HERE, "libw8a8.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -625,15 +625,15 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
 // [g BM/2, (g+1) BM/2) of the tile and wave q of a group owns weight rows [q BN/4,
 // (q+1) BN/4), so each SIMD holds one wave of each group. Every K-step has two phases
 // separated by workgroup barriers; group 1 starts one phase late (one extra barrier),
-// so while one group issues its MFMAs (and, between them, its share of the DMA for a
-// later stage) the other reads its next fragments from LDS. The matrix pipe of each SIMD
-// then alternates between the two waves instead of idling while both wait on LDS at
-// once, which is what a single barrier per K-tile with all waves in step leaves it doing.
+// so while one group issues its MFMAs the other reads its next fragments from LDS and
+// issues its share of the DMA for a later stage. The matrix pipe of each SIMD then
+// alternates between the two waves instead of idling while both wait on LDS at once,
+// which is what a single barrier per K-tile with all waves in step leaves it doing.
 //
 // Stage j is read by group 0 in phase 2j and by group 1 in phase 2j+1. Each wave waits
 // for its own DMA of stage j+1 at the end of its memory phase of K-step j, so both
 // groups' parts of a stage have landed by the barrier before its first reader; the
-// buffer of stage j-1 is refilled (with stage j+STAGES-1) in the compute phase of K-step
+// buffer of stage j-1 is refilled (with stage j+STAGES-1) in the memory phase of K-step
 // j, which follows both groups' reads of it.
 template <int BN_, int BM_, int STAGES_>
 struct PpShape {
@@ -647,8 +647,6 @@ struct PpShape {
     static constexpr int FULL_WAVES = PIECES - (PPW - 1) * NW;
     static constexpr int LDS = 163840;
     static constexpr int CPR = BN / 8;                   // 16-byte output chunks per staged row
-    static constexpr int SP = FN * FM / PPW;             // MFMAs between a wave's DMA pieces
-    static_assert(SP >= 8, "DMA slots SP i + 2 Q of the four waves of a group");
     static_assert(BN % 64 == 0 && BM % 32 == 0, "tile shape");
     static_assert(STAGES >= 3 && STAGES <= 4 && STAGES * STAGE <= LDS, "stages");
     static_assert(BM * BN * 2 <= LDS, "staged output tile");
@@ -675,12 +673,13 @@ __device__ __forceinline__ void pp_wait(int after, bool full) {
     }
 }
 
-// The K loop of one wave; Q = the wave's index in its group, a template parameter so that
-// each wave's DMA slots are fixed in its own copy of the code (no branches between the
-// MFMAs). A DMA instruction holds the CU's address unit for about one MFMA's time and a
-// wave cannot issue past one that waits for it; piece i of wave Q goes after MFMA
-// SP i + 2 Q, so the four waves of a group, released by the same barrier, do not queue
-// behind each other and the MFMA stream of each is not held up.
+// The K loop of one wave; Q = the wave's index in its group. A wave issues its DMA pieces
+// for stage j + STAGES - 1 in its memory phase of K-step j, right after its fragment reads:
+// the buffer refilled (that of stage j - 1) is free by then, since each group read it in an
+// earlier phase, before a barrier, and the compute phase then holds MFMAs only. (Measured
+// against issuing the pieces at fixed slots between the MFMAs of the compute phase: 94.3
+// against 96.0 us at M = 4096, N = 10240, K = 2560; 155 against 157 us at M = 8192,
+// N = 2560, K = 10240; 184.5 against 186.5 us at M = 8192, N = 10240, K = 2560.)
 template <class S, int Q>
 __device__ __forceinline__ void pp_loop(v4i (&acc)[S::FN][S::FM], const int8_t *const (&src)[S::PPW], int8_t *smem,
                                         int KT, int grp, int wave, bool full, int frow, int fchunk) {
@@ -688,7 +687,8 @@ __device__ __forceinline__ void pp_loop(v4i (&acc)[S::FN][S::FM], const int8_t *
     v4i a[FN], b[FM];
     int cur = 0, fb = STAGES - 1;  // buffers of stage j and of stage j + STAGES - 1
     for (int j = 0; j < KT; ++j) {
-        // memory phase: this K-step's fragments; this wave's part of stage j + 1 landed
+        // memory phase: this K-step's fragments (this wave's part of stage j + 1 landed), then
+        // this wave's DMA for stage j + STAGES - 1
         const int8_t *st = smem + cur * S::STAGE;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -696,24 +696,22 @@ __device__ __forceinline__ void pp_loop(v4i (&acc)[S::FN][S::FM], const int8_t *
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<64>(grp * S::WM + fm * 16 + frow, fchunk));
+        if (j + STAGES - 1 < KT) {
+            const int koff = (j + STAGES - 1) * S::BK;
+            int8_t *fdst = smem + fb * S::STAGE + wave * 1024;
+#pragma unroll
+            for (int piece = 0; piece < PPW; ++piece)
+                if (piece < PPW - 1 || full) dma_16B(src[piece] + koff, fdst + piece * S::NW * 1024);
+        }
         wait_lgkmcnt0();
-        if (j + 1 < KT) pp_wait<S>(min(STAGES - 3, KT - 2 - j), full);
+        // stages issued after j + 1 by now: j + 2 .. j + STAGES - 1
+        if (j + 1 < KT) pp_wait<S>(min(STAGES - 2, KT - 2 - j), full);
         lds_barrier();
-        // compute phase, with this wave's DMA for stage j + STAGES - 1 in its slots
-        const bool fill = j + STAGES - 1 < KT, fill_last = fill && full;
-        const int koff = (j + STAGES - 1) * S::BK;
-        int8_t *fdst = smem + fb * S::STAGE + wave * 1024;
+        // compute phase: MFMAs only
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
-                const int t = fn * FM + fm;
-                if (t % S::SP == 2 * Q && t / S::SP < PPW) {
-                    const int piece = t / S::SP;
-                    if (piece < PPW - 1 ? fill : fill_last) dma_16B(src[piece] + koff, fdst + piece * S::NW * 1024);
-                }
-            }
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
         lds_barrier();
         cur = cur + 1 == STAGES ? 0 : cur + 1;
         fb = fb + 1 == STAGES ? 0 : fb + 1;
