@@ -22,7 +22,8 @@ same graph runs up to 20 % slower per step (clocks still ramping), so a short ru
 that transient rather than the kernels.
 
 Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 1000] [--no-cpu-baseline]
-       [--workload pc|pg64|pg128|w4|m1|m1w4|qwen3|mv|mvg128|sdpa|rmsnorm] [--copy-ref-mb MB] [--no-graph]
+       [--workload pc|pg64|pg128|w4|w4pc|m1|m1w4|m1w4pc|qwen3|mv|mvg128|sdpa|rmsnorm] [--copy-ref-mb MB]
+       [--no-graph] [--no-m1]
 
 roofline.traffic (HBM bytes per GEMM launch) comes from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed under profiles/ for this workload, scaled by the same
@@ -53,6 +54,8 @@ WORKLOADS = {
     "w4": (4096, 10240, 2560, 4, 128),
     "m1": (1, 10240, 2560, 8, 0),
     "m1w4": (1, 10240, 2560, 4, 128),
+    "w4pc": (4096, 10240, 2560, 4, 0),
+    "m1w4pc": (1, 10240, 2560, 4, 0),
 }
 
 
@@ -582,7 +585,10 @@ def linear_bench(args, torch, w8a8, workload):
     stream = torch.cuda.current_stream()
     fused = M <= 16
 
-    if bits == 4:
+    if bits == 4 and gs == 0:
+        def gemm(w, st):
+            w8a8.w4a8_gemm_pc(xq, sx, w, sw, y=y, stream=st)
+    elif bits == 4:
         def gemm(w, st):
             w8a8.w4a8_gemm_pg(xq, sx, w, sw, gs, y=y, stream=st)
     elif gs:
@@ -648,7 +654,9 @@ def linear_bench(args, torch, w8a8, workload):
         achieved = ops / (gemm_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                     "frac": achieved / PEAK_INT8_TOPS, "traffic": measured_traffic(workload),
-                    "kernel": "gemm (int8 MFMA, fused per-channel dequant)", "launch_ms": gemm_ms}
+                    "kernel": "gemm (int8 MFMA" + (", int4 weights unpacked in the operand load" if bits == 4 else "")
+                              + (f", fused per-group dequant, gs={gs})" if gs else ", fused per-channel dequant)"),
+                    "launch_ms": gemm_ms}
 
     result = {
         "metric": f"INT8 TOPS & % MFMA peak of fused quant-GEMM-dequant, M={M} N={N} K={K}",

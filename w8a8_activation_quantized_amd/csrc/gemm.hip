@@ -635,20 +635,26 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
 // groups' parts of a stage have landed by the barrier before its first reader; the
 // buffer of stage j-1 is refilled (with stage j+STAGES-1) in the memory phase of K-step
 // j, which follows both groups' reads of it.
-template <int BN_, int BM_, int STAGES_>
+// BKS: K bytes per stage row. 64: a stage holds one K-step, 16 rows of 64 bytes per DMA
+// piece. 128: a stage holds two K-steps, 8 rows of 128 bytes per piece (whole 128-byte row
+// segments per DMA, which stream at a higher rate from L2), two stages.
+template <int BN_, int BM_, int STAGES_, int BKS_ = 64>
 struct PpShape {
-    static constexpr int BN = BN_, BM = BM_, BK = 64, STAGES = STAGES_;
+    static constexpr int BN = BN_, BM = BM_, BK = 64, BKS = BKS_, STAGES = STAGES_;
+    static constexpr int KPS = BKS / BK;                 // K-steps per stage
     static constexpr int NW = 8, NT = 512;
     static constexpr int WN = BN / 4, WM = BM / 2;
     static constexpr int FN = WN / 16, FM = WM / 16;
-    static constexpr int W_TILE = BN * BK, STAGE = (BN + BM) * BK;
-    static constexpr int PIECES = (BN + BM) / 16;        // 1 KiB DMA pieces (16 rows) per stage
+    static constexpr int W_TILE = BN * BKS, STAGE = (BN + BM) * BKS;
+    static constexpr int RPP = 1024 / BKS;               // rows per 1 KiB DMA piece
+    static constexpr int PIECES = (BN + BM) / RPP;       // DMA pieces per stage
     static constexpr int PPW = (PIECES + NW - 1) / NW;   // pieces per wave (max)
     static constexpr int FULL_WAVES = PIECES - (PPW - 1) * NW;
     static constexpr int LDS = 163840;
     static constexpr int CPR = BN / 8;                   // 16-byte output chunks per staged row
     static_assert(BN % 64 == 0 && BM % 32 == 0, "tile shape");
-    static_assert(STAGES >= 3 && STAGES <= 4 && STAGES * STAGE <= LDS, "stages");
+    static_assert(BKS == 64 ? STAGES >= 3 && STAGES <= 4 : BKS == 128 && STAGES == 2, "stages");
+    static_assert(STAGES * STAGE <= LDS, "LDS");
     static_assert(BM * BN * 2 <= LDS, "staged output tile");
     static_assert(2 * PPW < 64, "vmcnt range");
 };
@@ -718,9 +724,47 @@ __device__ __forceinline__ void pp_loop(v4i (&acc)[S::FN][S::FM], const int8_t *
     }
 }
 
-template <int BN, int BM, int STAGES>
+// The K loop with two stages of 128-value K-tiles (BKS = 128): stage s (K-steps 2 s and
+// 2 s + 1) sits in buffer s & 1. In its memory phase of K-step 2 s a wave reads its
+// fragments of the first half of stage s and issues its DMA pieces for stage s + 1 into the
+// other buffer, whose stage s - 1 both groups finished reading in earlier phases; at the end
+// of its memory phase of K-step 2 s + 1 it waits for those pieces, so every part of stage
+// s + 1 has landed by the barrier before its first reader.
+template <class S, int Q>
+__device__ __forceinline__ void pp_loop2(v4i (&acc)[S::FN][S::FM], const int8_t *const (&src)[S::PPW], int8_t *smem,
+                                         int KT, int grp, int wave, bool full, int frow, int fchunk) {
+    constexpr int FN = S::FN, FM = S::FM, PPW = S::PPW;
+    v4i a[FN], b[FM];
+    for (int j = 0; j < KT; ++j) {
+        const int stg = j >> 1, h = j & 1;
+        const int8_t *st = smem + (stg & 1) * S::STAGE;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(Q * S::WN + fn * 16 + frow, 4 * h + fchunk));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<128>(grp * S::WM + fm * 16 + frow, 4 * h + fchunk));
+        if (h == 0 && 2 * (stg + 1) < KT) {
+            const int koff = (stg + 1) * S::BKS;
+            int8_t *fdst = smem + ((stg + 1) & 1) * S::STAGE + wave * 1024;
+#pragma unroll
+            for (int piece = 0; piece < PPW; ++piece)
+                if (piece < PPW - 1 || full) dma_16B(src[piece] + koff, fdst + piece * S::NW * 1024);
+        }
+        wait_lgkmcnt0();
+        if (h == 1 && j + 1 < KT) wait_vmcnt<0>();  // stage s + 1: this wave's pieces landed
+        lds_barrier();
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+        lds_barrier();
+    }
+}
+
+template <int BN, int BM, int STAGES, int BKS = 64>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tmap) {
-    using S = PpShape<BN, BM, STAGES>;
+    using S = PpShape<BN, BM, STAGES, BKS>;
     constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW;
     __shared__ __attribute__((aligned(1024))) int8_t smem[S::LDS];
 
@@ -733,17 +777,18 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 
-    // Loader: wave w issues pieces g = w + j * NW of each stage (pieces below BN / 16 are
-    // weight rows, the rest token rows); lane i covers row 16 g + i / 4 of the stage and
-    // loads its 16-byte chunk (i & 3) ^ ((row >> 1) & 3), which is where the fragment
-    // reads look for it.
+    // Loader: wave w issues pieces g = w + j * NW of each stage (pieces below BN / RPP are
+    // weight rows, the rest token rows); lane i covers row RPP g + i / LPR of the stage (LPR =
+    // 64 / RPP lanes per row) and loads its 16-byte chunk (i % LPR) ^ ((row >> 1) & (LPR - 1)),
+    // which is where the fragment reads look for it.
+    constexpr int RPP = S::RPP, LPR = 64 / S::RPP;
     const int8_t *src[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
         const int g = min(wave + j * S::NW, S::PIECES - 1);
-        const bool is_w = g < BN / 16;
-        const int lrow = (is_w ? g : g - BN / 16) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((lrow >> 1) & 3);
+        const bool is_w = g < BN / RPP;
+        const int lrow = (is_w ? g : g - BN / RPP) * RPP + lane / LPR;
+        const int c = (lane % LPR) ^ ((lrow >> 1) & (LPR - 1));
         const int grow = is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
         src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + 16 * c);
     }
@@ -756,18 +801,32 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
 
     const int frow = lane & 15, fchunk = lane >> 4;
     const int KT = K / S::BK;
+    if constexpr (S::BKS == 64) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < KT) pp_issue<S>(src, s * S::BK, smem + s * S::STAGE, wave);
-    pp_wait<S>(min(STAGES - 2, KT - 1), full);
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < KT) pp_issue<S>(src, s * S::BK, smem + s * S::STAGE, wave);
+        pp_wait<S>(min(STAGES - 2, KT - 1), full);
+    } else {
+        pp_issue<S>(src, 0, smem, wave);  // stage 0; stage 1 goes out in the first K-step
+        wait_vmcnt<0>();
+    }
     lds_barrier();
     if (grp == 1) lds_barrier();  // group 1 runs one phase behind group 0
 
-    switch (wq) {
-        case 0: pp_loop<S, 0>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
-        case 1: pp_loop<S, 1>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
-        case 2: pp_loop<S, 2>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
-        default: pp_loop<S, 3>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+    if constexpr (S::BKS == 64) {
+        switch (wq) {
+            case 0: pp_loop<S, 0>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 1: pp_loop<S, 1>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 2: pp_loop<S, 2>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            default: pp_loop<S, 3>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+        }
+    } else {
+        switch (wq) {
+            case 0: pp_loop2<S, 0>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 1: pp_loop2<S, 1>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 2: pp_loop2<S, 2>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            default: pp_loop2<S, 3>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+        }
     }
     if (grp == 0) lds_barrier();  // pairs with group 1's last compute barrier: LDS is free
 
@@ -2126,6 +2185,7 @@ constexpr Config kConfigs[] = {
     {256, 320, 8},  // 13: direct-to-LDS, BN=320 BM=256, 4 stages of 64, two wave groups in alternation
     {128, 128, 4},  // 14: direct-to-LDS, BN=128 BM=128, 4 stages, 4 waves (64 n x 64 m each)
     {128, 64, 4},   // 15: direct-to-LDS, BN=64 BM=128, 6 stages, 8 waves (32 n x 32 m each); mid M
+    {256, 320, 8},  // 16: as 13 with two stages of 128-value K-tiles (128-byte DMA row segments)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2171,14 +2231,14 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 
-template <int BN, int BM, int STAGES>
+template <int BN, int BM, int STAGES, int BKS = 64>
 hipError_t launch_pp(const GemmProblem &p, int group_m, hipStream_t stream) {
     TileMap t;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.group_m = group_m;
     dim3 grid(t.tiles_m * t.tiles_n), block(512);
-    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES>), grid, block, 0, stream, p, t);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS>), grid, block, 0, stream, p, t);
     return hipGetLastError();
 }
 
@@ -2278,8 +2338,13 @@ int choose_config(const GemmProblem &p) {
     const double c6 = (double)((t6 + cus - 1) / cus) * 160 * 256 / 1.0;
     const double c7 = (double)((t7 + cus - 1) / cus) * 128 * 256 / 0.9;
     const double c12 = (double)((t12 + cus - 1) / cus) * 64 * 64 / 0.4;
+    // (the 320 x 256 ping-pong form with two stages of 128-value K-tiles, 16, against the same
+    // tile with four 64-value stages, 13, which K % 128 == 0 always allows here: 91.4 against
+    // 94.0 us at M = 4096, N = 10240, K = 2560; 148 against 150.5 us at M = 8192, N = 2560,
+    // K = 10240; 177 against 183 us at M = 8192, N = 10240, K = 2560; whole 128-byte row
+    // segments per DMA halve the L2 requests, and the chip holds a 6 % higher clock)
     if (c12 < c6 && c12 < c7 && c12 < c13) return 12;
-    if (c13 < c6 && c13 < c7) return 13;
+    if (c13 < c6 && c13 < c7) return 16;
     return c6 <= c7 ? 6 : 7;
 }
 
@@ -2453,6 +2518,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 11: return launch_ms<128, 256, 3, 2, 4>(p, gm, stream);
         case 12: return launch_ms<64, 64, 4, 2, 2>(p, gm, stream);
         case 13: return launch_pp<320, 256, 4>(p, gm, stream);
+        case 16: return launch_pp<320, 256, 2, 128>(p, gm, stream);
         case 14: return launch_ms<128, 128, 4, 2, 2>(p, gm, stream);
         case 15: return launch_ms<64, 128, 6, 2, 4>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
