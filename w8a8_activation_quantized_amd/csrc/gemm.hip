@@ -1082,11 +1082,32 @@ __device__ __forceinline__ void mg_fold_mma(v4i (&acc)[S::FN][S::FM], const floa
         }
 }
 
+// The group scales of a stage, FN float4 64 bytes apart, read in one asm block that also
+// retires them. The stage landed before the barrier that opened it; read as ordinary loads,
+// the compiler cannot tell them from the LDS targets of the DMA still in flight and waits
+// for all of that DMA first (vmcnt(0) every K-tile, which empties the stage ring).
 template <class S>
 __device__ __forceinline__ void mg_scales(const int8_t *st, int gi, int wn, int fchunk, float4 (&sw)[S::FN]) {
-    const float *sc = reinterpret_cast<const float *>(st + S::W_TILE + S::X_TILE) + gi * S::BN;
+    typedef float v4f_t __attribute__((ext_vector_type(4)));
+    const float *sc = reinterpret_cast<const float *>(st + S::W_TILE + S::X_TILE) + gi * S::BN + wn * S::WN + 4 * fchunk;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float *)sc;
+    static_assert(S::FN == 2 || S::FN == 4, "scale reads per wave");
+    v4f_t v[4];
+    if constexpr (S::FN == 4) {
+        asm volatile(
+            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:64\n\t"
+            "ds_read_b128 %2, %4 offset:128\n\tds_read_b128 %3, %4 offset:192\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+            : "v"(a)
+            : "memory");
+    } else {
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:64\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1])
+                     : "v"(a)
+                     : "memory");
+    }
 #pragma unroll
-    for (int fn = 0; fn < S::FN; ++fn) sw[fn] = *reinterpret_cast<const float4 *>(sc + wn * S::WN + fn * 16 + 4 * fchunk);
+    for (int fn = 0; fn < S::FN; ++fn) sw[fn] = make_float4(v[fn][0], v[fn][1], v[fn][2], v[fn][3]);
 }
 
 // Per-channel epilogue of the GS = 0 form: the int32 sums (16 x the sums for int4 weights,
@@ -1225,10 +1246,40 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
     float4 sw0[FN], sw1[FN];
 #pragma unroll
     for (int i = 0; i < FN; ++i) sw0[i] = sw1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int cur = 0;
+    // One group per K-tile with eight waves: the waves of the second half (one on each SIMD)
+    // run each K-tile as [fold the closed group and open the next with K-step 0][K-step 1],
+    // the first half as [K-step 1 of the previous K-tile][fold and open]. Between two
+    // barriers each SIMD then has one wave folding while the other runs MFMAs only, where
+    // with all waves in step both fold at once (VALU-bound) and then both wait on MFMAs.
+    // Both halves read all of a stage before the barrier that ends it.
+    constexpr bool LAG = !S::PC && S::GPK == 1 && S::NW == 8;
+    if (LAG && wave >= S::NW / 2) {
+        for (int kt = 0; kt < KT; ++kt) {
+            const int fill = kt + STAGES - 1;
+            if (fill < KT) {
+                int fb = cur + STAGES - 1;
+                fb -= fb >= STAGES ? STAGES : 0;
+                mg_issue<S>(p, m0, n0, kt0 + fill, smem + fb * S::STAGE, wave, lane);
+            }
+            const int8_t *st = smem + cur * S::STAGE;
+            mg_frags<S>(st, 0, wm, wn, frow, fchunk, r0, b0);
+            mg_unpack<S>(r0, a0);
+            mg_fold_mma<S>(acc, sw0, t, a0, b0);  // group kt-1 folds, group kt opens
+            mg_frags<S>(st, 1, wm, wn, frow, fchunk, r1, b1);
+            mg_scales<S>(st, 0, wn, fchunk, sw0);
+            mg_unpack<S>(r1, a1);
+            mg_mma<S, false>(acc, a1, b1);  // K-step 1 closes group kt
+            if (kt + 1 < KT) {
+                wait_vmcnt_rt(OPS * min(STAGES - 2, KT - 2 - kt));
+                lds_barrier();
+                cur = cur + 1 == STAGES ? 0 : cur + 1;
+            }
+        }
+    } else {
     mg_frags<S>(smem, 0, wm, wn, frow, fchunk, r0, b0);
     wait_lgkmcnt0();
     mg_unpack<S>(r0, a0);
-    int cur = 0;
     for (int kt = 0; kt < KT; ++kt) {
         const int fill = kt + STAGES - 1;
         if (fill < KT) {
@@ -1265,6 +1316,7 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
         }
         wait_lgkmcnt0();
         mg_unpack<S>(r0, a0);
+    }
     }
     if constexpr (S::PC) {
         mg_pc_epilogue<S, SPLIT>(p, acc, smem, m0, n0, wm, wn, frow, fchunk, tid, ks);
