@@ -2380,13 +2380,16 @@ int choose_config(const GemmProblem &p) {
     }
     // per-channel: among the DMA kernels, the fewest chip-wide rounds of tiles times tile
     // area over the kernel's work rate per unit area (320 x 256 in alternating wave
-    // groups: 1.05, 160 x 256: 1.0, 128 x 256: 0.9, 64 x 64: 0.4); partial tiles and a
-    // partly filled last round cost whole ones
+    // groups with 128-value stages: 1.2, 160 x 256: 1.0, 128 x 256: 0.9, 64 x 64: 0.4);
+    // partial tiles and a partly filled last round cost whole ones. (With 1.2 the 320 x 256
+    // form takes M = 2048, N = 6144, K = 4096: 54.6 against 56.8 us for 128 x 256; M = 1536,
+    // N = 10240, K = 2560: 40.0 against 44.2; M = 2048, N = 10240: 45.3 against 47.6; and
+    // ties 160 x 256 at M = 2048, N = 24576, K = 4096, 173.9 against 172.5 us.)
     const int64_t t13 = (int64_t)((p.M + 255) / 256) * ((p.N + 319) / 320);
     const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
     const int64_t t7 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
     const int64_t t12 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
-    const double c13 = (double)((t13 + cus - 1) / cus) * 320 * 256 / 1.05;
+    const double c13 = (double)((t13 + cus - 1) / cus) * 320 * 256 / 1.2;
     const double c6 = (double)((t6 + cus - 1) / cus) * 160 * 256 / 1.0;
     const double c7 = (double)((t7 + cus - 1) / cus) * 128 * 256 / 0.9;
     const double c12 = (double)((t12 + cus - 1) / cus) * 64 * 64 / 0.4;
