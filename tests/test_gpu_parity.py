@@ -289,6 +289,24 @@ def test_full_size_config_shapes(w8a8, mode, M, N, K):
         compare(run_mode(w8a8, mode, x, W, out), r, f"{mode} {M}x{N}x{K} {out}")
 
 
+@pytest.mark.parametrize("mode", ["pg128", "w4_128", "pg64"])
+@pytest.mark.parametrize("M,N,K", [(300, 528, 128), (300, 528, 256), (513, 272, 384)])
+def test_grouped_few_k_tiles(w8a8, mode, M, N, K):
+    """The per-group DMA kernels (128 x 256 and 64 x 64 forms) with one, two and three
+    128-value K-tiles: the first group's fold of zeros, the loop with no barrier inside, and
+    (gs = 128) the two halves of the workgroup that fold half a K-tile apart; ragged M and N."""
+    x, W = linear_inputs(M, N, K, seed=M + K)
+    r = oracle_mode(mode, x, W)
+    try:
+        for cfg in (11, 12):
+            w8a8.w8a8_debug_force_config(cfg)
+            for out in (torch.float16, torch.int32):
+                note(f"few K-tiles {mode} {M}x{N}x{K} config {cfg} {out}")
+                compare(run_mode(w8a8, mode, x, W, out), r, f"cfg {cfg} {mode} {M}x{N}x{K} {out}")
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
+
+
 def _bf16_rne_bits(f32: np.ndarray) -> np.ndarray:
     u = f32.view(np.uint32).astype(np.uint64)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

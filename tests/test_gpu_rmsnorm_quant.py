@@ -99,6 +99,34 @@ def test_rmsnorm_quantize_special_rows_and_stride(w8a8):
         assert q[1, 333] == -127 and (np.delete(q[1], 333) == 0).all()
 
 
+def test_rmsnorm_quantize_bf16_extreme_rows(w8a8):
+    """bf16 rows whose squares leave the fp32 range (|x| ~ 1e30: x^2 ~ 1e60; |x| ~ 2^-100 and
+    the subnormal 2^-130: x^2 ~ 2^-200 .. 2^-260) and rows near the fp32 overflow of x^2
+    (|x| ~ 1e19). The kernel sums the squares of bf16 rows in fp64, as the oracle does, so the
+    scale stays finite and nonzero at eps = 0 and equals the oracle's to the sum's bound."""
+    K = 512
+    rng = np.random.default_rng(9)
+    x32 = np.stack([rng.standard_normal(K) * 1e30,
+                    rng.standard_normal(K) * 2.0 ** -100,
+                    np.where(np.arange(K) % 5 == 0, 2.0 ** -130, 0.0) * np.where(np.arange(K) % 2 == 0, 1, -1),
+                    rng.standard_normal(K) * 1e19]).astype(np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    xb = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # RNE to bf16 bit patterns
+    g = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+    xd = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    gd = torch.from_numpy(g).cuda()
+    for eps in (0.0, 1e-6):
+        note(f"rmsnorm_quantize bf16 extreme rows eps={eps}")
+        xq, sx = w8a8.rmsnorm_quantize(xd, gd, eps)
+        torch.cuda.synchronize()
+        rq, _, rs = oracle.rmsnorm_quantize(xb, g, eps, x_bf16=True, g_bf16=False)
+        got_q, got_s = xq.cpu().numpy(), sx.cpu().numpy().astype(np.float64)
+        assert (got_q == rq).all(), f"eps={eps}: codes differ"
+        assert np.isfinite(got_s).all() and (got_s > 0).all(), f"eps={eps}: scales {got_s}"
+        bound = 1.01 * ((K + 1) / 2 + 8) * 2.0 ** -24 * rs
+        assert (np.abs(got_s - rs) <= bound).all(), f"eps={eps}: scales {got_s} against {rs}"
+
+
 def test_rmsnorm_quantize_feeds_the_gemm(w8a8):
     """The codes and scale go into w8a8_gemm_pc unchanged; the GEMM output matches the oracle's
     linear layer applied to the same codes (fp32 bound of the per-channel epilogue)."""

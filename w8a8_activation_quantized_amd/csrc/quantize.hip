@@ -16,6 +16,7 @@
 // The absmax works on the magnitude bit patterns (bits & 0x7fff), which order
 // like the magnitudes for finite fp16/bf16 values.
 #include <cmath>
+#include <type_traits>
 
 #include "act_quant.h"
 #include "internal.h"
@@ -213,12 +214,19 @@ __device__ __forceinline__ void norm_u8(uint4 xc, uint4 gc, float (&u)[8], float
         }
 }
 
-__device__ __forceinline__ void norm_stats8(const float (&u)[8], const float (&xv)[8], uint32_t &amax, float &ss) {
+// Sum of squares: fp32 for fp16 rows (x^2 of any half stays within the fp32 normal range,
+// 2^-48 .. 2^32); fp64 for bf16 rows, whose squares leave the fp32 range for |x| > 2^64 or
+// |x| < 2^-75 (inf or 0 sums, so an infinite or zero scale beside nonzero codes).
+template <typename SS>
+__device__ __forceinline__ void norm_stats8(const float (&u)[8], const float (&xv)[8], uint32_t &amax, SS &ss) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint32_t ub = __builtin_bit_cast(uint32_t, u[e]) & 0x7fffffffu;
         amax = amax > ub ? amax : ub;
-        ss = __builtin_fmaf(xv[e], xv[e], ss);
+        if constexpr (std::is_same<SS, double>::value)
+            ss = __builtin_fma((double)xv[e], (double)xv[e], ss);
+        else
+            ss = __builtin_fmaf(xv[e], xv[e], ss);
     }
 }
 
@@ -255,8 +263,9 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
                                                                          const uint16_t *__restrict__ g, float eps,
                                                                          int K, int8_t *__restrict__ xq,
                                                                          float *__restrict__ sx) {
+    using SS = typename std::conditional<XBF, double, float>::type;
     __shared__ uint32_t wmax[NORM_THREADS / 64];
-    __shared__ float wsum[NORM_THREADS / 64];
+    __shared__ SS wsum[NORM_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = blockIdx.x;
     const uint16_t *row = x + (int64_t)m * ldx;
@@ -265,7 +274,7 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
 
     float uc[CPT][8];
     uint32_t amax = 0;
-    float ss = 0.0f;
+    SS ss = 0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + NORM_THREADS * j;
@@ -298,7 +307,12 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
     }
 
     const float s = __builtin_bit_cast(float, amax) / 127.0f;
-    if (tid == 0) sx[m] = s == 0.0f ? 0.0f : s * (1.0f / __builtin_sqrtf(ss / (float)K + eps));
+    if (tid == 0) {
+        if constexpr (XBF)
+            sx[m] = s == 0.0f ? 0.0f : (float)((double)s * (1.0 / __builtin_sqrt(ss / (double)K + (double)eps)));
+        else
+            sx[m] = s == 0.0f ? 0.0f : s * (1.0f / __builtin_sqrtf(ss / (float)K + eps));
+    }
     if (s == 0.0f) {
         for (int c = tid; c < nch; c += NORM_THREADS) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
         return;
