@@ -220,7 +220,7 @@ def test_gemm_strided_output_and_empty(w8a8):
     # row strides of 304 (16-byte rows: staged stores) and 276 (8-byte rows: direct
     # stores), both 16-bit types, in the automatic choice and the DMA-pipeline kernels
     try:
-        for cfg in (-1, 6, 7, 13, 16):
+        for cfg in (-1, 6, 7, 13, 16, 17):
             w8a8.w8a8_debug_force_config(cfg)
             for ldy in (304, 276):
                 for out, fmt in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
@@ -274,8 +274,9 @@ def test_every_config_identical(w8a8, mode):
     ("pc", 1536, 2560, 10240),    # 128 x 128 tiles, one round
     ("pg128", 768, 2560, 10240),  # 64 x 64 per-group DMA tiles
     ("w4_0", 1, 10240, 2560),     # per-column int4: GEMV
-    ("w4_0", 1024, 10240, 2560),  # 128 x 256 DMA tiles without the fold
+    ("w4_0", 1024, 10240, 2560),  # 320 x 256 ping-pong tiles, int4 unpacked in the memory phase
     ("w4_0", 4096, 10240, 2560),
+    ("w4_0", 2048, 2560, 10240),  # 128 x 256 DMA tiles without the fold
     ("w4_0", 768, 2560, 10240),   # 64 x 64 DMA tiles without the fold
 ])
 def test_full_size_config_shapes(w8a8, mode, M, N, K):
@@ -303,6 +304,32 @@ def test_grouped_few_k_tiles(w8a8, mode, M, N, K):
             for out in (torch.float16, torch.int32):
                 note(f"few K-tiles {mode} {M}x{N}x{K} config {cfg} {out}")
                 compare(run_mode(w8a8, mode, x, W, out), r, f"cfg {cfg} {mode} {M}x{N}x{K} {out}")
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
+
+
+@pytest.mark.parametrize("K", [130816, 130944, 131072])
+@pytest.mark.parametrize("M", [2, 300])
+def test_int4_per_channel_extreme_sums(w8a8, M, K):
+    """int4 weights with per-channel scales, raw int32 sums at their largest: every activation
+    code -128 and every weight -8 (stored nibble 0), so each sum is K * 1024 (closed form).
+    The paths that sum 16 q in int32 (16 K 1024 < 2^31) take K up to 130944 in whole
+    128-value K-tiles (M > 16; 130816 is the last that the DMA GEMV, K % 256 == 0, takes at
+    M <= 16); K = 131072 must take the kernels that sum q."""
+    N = 64
+    xq = torch.full((M, K), -128, dtype=torch.int8, device="cuda")
+    sx = torch.ones((M,), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+    sw = torch.ones((N,), dtype=torch.float32, device="cuda")
+    cfgs = (-1, 17) if M > 16 else (-1,)
+    try:
+        for cfg in cfgs:
+            w8a8.w8a8_debug_force_config(cfg)
+            note(f"int4 extreme sums M={M} K={K} config {cfg}")
+            y = w8a8.w4a8_gemm_pc(xq, sx, wq, sw, torch.int32)
+            torch.cuda.synchronize()
+            got = host(y)
+            assert (got == K * 1024).all(), f"M={M} K={K} cfg {cfg}: {np.unique(got)[:4]} against {K * 1024}"
     finally:
         w8a8.w8a8_debug_force_config(-1)
 

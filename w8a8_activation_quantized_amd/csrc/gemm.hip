@@ -62,6 +62,11 @@ __device__ __forceinline__ int swz(int row, int chunk) {
         return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
+// Largest K for int32 sums of 16 q (int4 weights unpacked as 16 q, see unpack_nibbles_x16)
+// over all of K: |16 sum| <= 16 K 128 8 < 2^31 needs K < 131072 (codes -128 are accepted),
+// and the kernels that use it take K in whole 128-value K-tiles.
+constexpr int kInt4X16MaxK = 131072 - 128;
+
 // Eight packed bytes (two dwords; 16 nibbles, even k in the low nibble) -> sixteen int8
 // codes q = u - 8 in k order.
 __device__ __forceinline__ uint32_t interleave_lo(uint32_t lo, uint32_t hi) {
@@ -638,22 +643,29 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
 // BKS: K bytes per stage row. 64: a stage holds one K-step, 16 rows of 64 bytes per DMA
 // piece. 128: a stage holds two K-steps, 8 rows of 128 bytes per piece (whole 128-byte row
 // segments per DMA, which stream at a higher rate from L2), two stages.
-template <int BN_, int BM_, int STAGES_, int BKS_ = 64>
+// WK = W_INT4: int4 weights (per-channel scales or the raw int32 sums), 64 bytes per weight
+// row per 128-value stage, 16 rows per DMA piece; the fragments are unpacked to 16 q in the
+// memory phase and the sums shifted right by 4 (exact) before the epilogue.
+template <int BN_, int BM_, int STAGES_, int BKS_ = 64, int WK_ = W_INT8>
 struct PpShape {
-    static constexpr int BN = BN_, BM = BM_, BK = 64, BKS = BKS_, STAGES = STAGES_;
+    static constexpr int BN = BN_, BM = BM_, BK = 64, BKS = BKS_, STAGES = STAGES_, WK = WK_;
     static constexpr int KPS = BKS / BK;                 // K-steps per stage
     static constexpr int NW = 8, NT = 512;
     static constexpr int WN = BN / 4, WM = BM / 2;
     static constexpr int FN = WN / 16, FM = WM / 16;
-    static constexpr int W_TILE = BN * BKS, STAGE = (BN + BM) * BKS;
-    static constexpr int RPP = 1024 / BKS;               // rows per 1 KiB DMA piece
-    static constexpr int PIECES = (BN + BM) / RPP;       // DMA pieces per stage
+    static constexpr int WB = WK == W_INT4 ? BKS / 2 : BKS;  // weight bytes per row per stage
+    static constexpr int W_TILE = BN * WB, STAGE = BN * WB + BM * BKS;
+    static constexpr int RPP = 1024 / BKS;               // token rows per 1 KiB DMA piece
+    static constexpr int RPPW = 1024 / WB;               // weight rows per piece
+    static constexpr int W_PIECES = BN / RPPW;
+    static constexpr int PIECES = W_PIECES + BM / RPP;   // DMA pieces per stage
     static constexpr int PPW = (PIECES + NW - 1) / NW;   // pieces per wave (max)
     static constexpr int FULL_WAVES = PIECES - (PPW - 1) * NW;
     static constexpr int LDS = 163840;
     static constexpr int CPR = BN / 8;                   // 16-byte output chunks per staged row
     static_assert(BN % 64 == 0 && BM % 32 == 0, "tile shape");
     static_assert(BKS == 64 ? STAGES >= 3 && STAGES <= 4 : BKS == 128 && STAGES == 2, "stages");
+    static_assert(WK == W_INT8 || BKS == 128, "int4 weights take 128-value stages");
     static_assert(STAGES * STAGE <= LDS, "LDS");
     static_assert(BM * BN * 2 <= LDS, "staged output tile");
     static_assert(2 * PPW < 64, "vmcnt range");
@@ -731,27 +743,39 @@ __device__ __forceinline__ void pp_loop(v4i (&acc)[S::FN][S::FM], const int8_t *
 // of its memory phase of K-step 2 s + 1 it waits for those pieces, so every part of stage
 // s + 1 has landed by the barrier before its first reader.
 template <class S, int Q>
-__device__ __forceinline__ void pp_loop2(v4i (&acc)[S::FN][S::FM], const int8_t *const (&src)[S::PPW], int8_t *smem,
-                                         int KT, int grp, int wave, bool full, int frow, int fchunk) {
+__device__ __forceinline__ void pp_loop2(v4i (&acc)[S::FN][S::FM], const int8_t *const (&src)[S::PPW],
+                                         const int (&kadv)[S::PPW], int8_t *smem, int KT, int grp, int wave, bool full,
+                                         int frow, int fchunk) {
     constexpr int FN = S::FN, FM = S::FM, PPW = S::PPW;
     v4i a[FN], b[FM];
     for (int j = 0; j < KT; ++j) {
         const int stg = j >> 1, h = j & 1;
         const int8_t *st = smem + (stg & 1) * S::STAGE;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(Q * S::WN + fn * 16 + frow, 4 * h + fchunk));
+        for (int fn = 0; fn < FN; ++fn) {
+            const int r = Q * S::WN + fn * 16 + frow;
+            if constexpr (S::WK == W_INT4)  // the 16-byte piece with this lane's 16 values
+                a[fn] = *reinterpret_cast<const v4i *>(st + r * 64 + (((2 * h + (fchunk >> 1)) ^ ((r >> 2) & 3)) << 4));
+            else
+                a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(r, 4 * h + fchunk));
+        }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<128>(grp * S::WM + fm * 16 + frow, 4 * h + fchunk));
         if (h == 0 && 2 * (stg + 1) < KT) {
-            const int koff = (stg + 1) * S::BKS;
             int8_t *fdst = smem + ((stg + 1) & 1) * S::STAGE + wave * 1024;
 #pragma unroll
             for (int piece = 0; piece < PPW; ++piece)
-                if (piece < PPW - 1 || full) dma_16B(src[piece] + koff, fdst + piece * S::NW * 1024);
+                if (piece < PPW - 1 || full) dma_16B(src[piece] + (stg + 1) * kadv[piece], fdst + piece * S::NW * 1024);
         }
         wait_lgkmcnt0();
+        if constexpr (S::WK == W_INT4) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const uint2 w = (fchunk & 1) ? make_uint2(a[fn][2], a[fn][3]) : make_uint2(a[fn][0], a[fn][1]);
+                a[fn] = __builtin_bit_cast(v4i, unpack_nibbles_x16(w.x, w.y));
+            }
+        }
         if (h == 1 && j + 1 < KT) wait_vmcnt<0>();  // stage s + 1: this wave's pieces landed
         lds_barrier();
 #pragma unroll
@@ -762,9 +786,9 @@ __device__ __forceinline__ void pp_loop2(v4i (&acc)[S::FN][S::FM], const int8_t 
     }
 }
 
-template <int BN, int BM, int STAGES, int BKS = 64>
+template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tmap) {
-    using S = PpShape<BN, BM, STAGES, BKS>;
+    using S = PpShape<BN, BM, STAGES, BKS, WK>;
     constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW;
     __shared__ __attribute__((aligned(1024))) int8_t smem[S::LDS];
 
@@ -777,20 +801,30 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 
-    // Loader: wave w issues pieces g = w + j * NW of each stage (pieces below BN / RPP are
+    // Loader: wave w issues pieces g = w + j * NW of each stage (pieces below W_PIECES are
     // weight rows, the rest token rows); lane i covers row RPP g + i / LPR of the stage (LPR =
     // 64 / RPP lanes per row) and loads its 16-byte chunk (i % LPR) ^ ((row >> 1) & (LPR - 1)),
-    // which is where the fragment reads look for it.
-    constexpr int RPP = S::RPP, LPR = 64 / S::RPP;
+    // which is where the fragment reads look for it (64-byte int4 weight rows: chunk
+    // (i % 4) ^ ((row >> 2) & 3)). kadv: bytes a piece's source advances per stage.
+    constexpr int RPP = S::RPP, LPR = 64 / S::RPP, LPRW = 64 / S::RPPW;
     const int8_t *src[PPW];
+    int kadv[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
         const int g = min(wave + j * S::NW, S::PIECES - 1);
-        const bool is_w = g < BN / RPP;
-        const int lrow = (is_w ? g : g - BN / RPP) * RPP + lane / LPR;
-        const int c = (lane % LPR) ^ ((lrow >> 1) & (LPR - 1));
-        const int grow = is_w ? min(n0 + lrow, N - 1) : min(m0 + lrow, M - 1);
-        src[j] = (is_w ? static_cast<const int8_t *>(p.wq) : p.xq) + ((int64_t)grow * K + 16 * c);
+        const bool is_w = g < S::W_PIECES;
+        if (is_w) {
+            const int lrow = g * S::RPPW + lane / LPRW;
+            const int c = WK == W_INT4 ? (lane % LPRW) ^ ((lrow >> 2) & 3) : (lane % LPRW) ^ ((lrow >> 1) & (LPRW - 1));
+            const int64_t rb = WK == W_INT4 ? K / 2 : K;  // bytes per weight row
+            src[j] = static_cast<const int8_t *>(p.wq) + ((int64_t)min(n0 + lrow, N - 1) * rb + 16 * c);
+            kadv[j] = S::WB;
+        } else {
+            const int lrow = (g - S::W_PIECES) * RPP + lane / LPR;
+            const int c = (lane % LPR) ^ ((lrow >> 1) & (LPR - 1));
+            src[j] = p.xq + ((int64_t)min(m0 + lrow, M - 1) * K + 16 * c);
+            kadv[j] = S::BKS;
+        }
     }
 
     v4i acc[FN][FM];
@@ -822,13 +856,20 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
         }
     } else {
         switch (wq) {
-            case 0: pp_loop2<S, 0>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
-            case 1: pp_loop2<S, 1>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
-            case 2: pp_loop2<S, 2>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
-            default: pp_loop2<S, 3>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 0: pp_loop2<S, 0>(acc, src, kadv, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 1: pp_loop2<S, 1>(acc, src, kadv, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 2: pp_loop2<S, 2>(acc, src, kadv, smem, KT, grp, wave, full, frow, fchunk); break;
+            default: pp_loop2<S, 3>(acc, src, kadv, smem, KT, grp, wave, full, frow, fchunk); break;
         }
     }
     if (grp == 0) lds_barrier();  // pairs with group 1's last compute barrier: LDS is free
+    if constexpr (WK == W_INT4) {
+        // int4: the sums of 16 q, shifted back exactly (K <= kInt4X16MaxK)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = acc[i][j] >> 4;
+    }
 
     // ---- epilogue (per-channel dequant or raw int32) ----
     const float *__restrict__ sxp = p.sx;
@@ -914,9 +955,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
 //
 // GS = 0: per-channel weight scales (int4 weights of one scale per output channel, Cider
 // README "量化": per-column INT4; or the raw int32 sums of int4 weights): no fold, the int32
-// sums run over all of K (16 x the sums for int4, exactly: |16 acc| <= 16 K 127 8 < 2^31 for
-// K <= 131072, which the launcher checks), shifted right by 4 (exact) and dequantized as the
-// per-channel kernels do, y = (fp32(acc) * s_x[m]) * s_w[n].
+// sums run over all of K (16 x the sums for int4, exactly while K <= kInt4X16MaxK, which the
+// launcher checks), shifted right by 4 (exact) and dequantized as the per-channel kernels do,
+// y = (fp32(acc) * s_x[m]) * s_w[n].
 template <int BN_, int BM_, int STAGES_, int WGN_, int WGM_, int GS_, int WK_>
 struct MgShape {
     static constexpr int BN = BN_, BM = BM_, BK = 128, STAGES = STAGES_, WGN = WGN_, WGM = WGM_, GS = GS_, WK = WK_;
@@ -1893,11 +1934,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
                 const int byte = t * 32 + fchunk * 8;
                 const v4i q = *reinterpret_cast<const v4i *>(slot + frow * 128 + (((byte >> 4) ^ ((frow >> 1) & 7)) << 4));
                 const uint2 w = (byte & 8) ? make_uint2(q[2], q[3]) : make_uint2(q[0], q[1]);
-                // grouped: 16 q, and facc holds 16 t; the raw int32 sums keep q
-                if constexpr (S::GROUPED)
-                    a = __builtin_bit_cast(v4i, unpack_nibbles_x16(w.x, w.y));
-                else
-                    a = __builtin_bit_cast(v4i, unpack_nibbles(w.x, w.y));
+                // 16 q: grouped, facc holds 16 t; per channel and the raw int32 sums, the
+                // sums of 16 q are shifted back at the end (K <= kInt4X16MaxK)
+                a = __builtin_bit_cast(v4i, unpack_nibbles_x16(w.x, w.y));
             } else {
                 a = *reinterpret_cast<const v4i *>(slot + frow * 128 + (((t * 4 + fchunk) ^ ((frow >> 1) & 7)) << 4));
             }
@@ -2062,6 +2101,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_dma_kernel(GemmProbl
             t.z += u.z;
             t.w += u.w;
         }
+        if constexpr (WK == W_INT4) t = make_int4(t.x >> 4, t.y >> 4, t.z >> 4, t.w >> 4);  // exact
         if (p.out == OUT_I32) {
             *reinterpret_cast<int4 *>(static_cast<int32_t *>(p.y) + off) = t;
             return;
@@ -2078,6 +2118,9 @@ hipError_t launch_gemv_dma_x(const GemmProblem &p, hipStream_t stream) {
     using S = GvShape<GS, WK, XL>;
     const int RB = WK == W_INT4 ? p.K / 2 : p.K;
     if (RB % 128 != 0 || p.M > 16) return hipErrorNotSupported;
+    // int4 per channel / raw sums: int32 sums of 16 q (longer K: the register-staged GEMV,
+    // or quantize + GEMM for the fused call)
+    if (WK == W_INT4 && GS == 0 && p.K > kInt4X16MaxK) return hipErrorNotSupported;
     // in-kernel quantization copies x rows with 16-byte DMA: rows must start 16-byte aligned
     if (FQ && ((reinterpret_cast<uintptr_t>(p.x) & 15) != 0 || (p.ldx * 2) % 16 != 0)) return hipErrorNotSupported;
     const int NCH = p.K / S::KPC;
@@ -2238,6 +2281,7 @@ constexpr Config kConfigs[] = {
     {128, 128, 4},  // 14: direct-to-LDS, BN=128 BM=128, 4 stages, 4 waves (64 n x 64 m each)
     {128, 64, 4},   // 15: direct-to-LDS, BN=64 BM=128, 6 stages, 8 waves (32 n x 32 m each); mid M
     {256, 320, 8},  // 16: as 13 with two stages of 128-value K-tiles (128-byte DMA row segments)
+    {256, 320, 8},  // 17: as 16 with int4 weights (per-channel scales or raw int32 sums); int8: 16
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2283,14 +2327,14 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 
-template <int BN, int BM, int STAGES, int BKS = 64>
+template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8>
 hipError_t launch_pp(const GemmProblem &p, int group_m, hipStream_t stream) {
     TileMap t;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.group_m = group_m;
     dim3 grid(t.tiles_m * t.tiles_n), block(512);
-    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS>), grid, block, 0, stream, p, t);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS, WK>), grid, block, 0, stream, p, t);
     return hipGetLastError();
 }
 
@@ -2330,14 +2374,10 @@ hipError_t dispatch_mg(const GemmProblem &p, bool small, int group_m, hipStream_
     return launch_mg<128, 256, 3, 2, 4, 128, W_INT8, SPLIT>(p, group_m, stream);
 }
 
-// Largest K for the GS = 0 form of gemm_mg_kernel with int4 weights: its int32 sums are 16 x
-// the integer products, |16 sum| <= 16 K 127 8 < 2^31.
-constexpr int kMgPcMaxK = 131072;
-
-// The GS = 0 form of gemm_mg_kernel serves int4 weights with per-channel scales, and the raw
-// int32 sums of int4 weights.
+// The GS = 0 form of gemm_mg_kernel and the int4 form of gemm_pp_kernel serve int4 weights
+// with per-channel scales, and the raw int32 sums of int4 weights (sums of 16 q).
 bool mg_per_channel(const GemmProblem &p) {
-    return p.wkind == W_INT4 && (p.gs == 0 || p.out == OUT_I32) && p.K % 128 == 0 && p.K <= kMgPcMaxK;
+    return p.wkind == W_INT4 && (p.gs == 0 || p.out == OUT_I32) && p.K % 128 == 0 && p.K <= kInt4X16MaxK;
 }
 
 int choose_config(const GemmProblem &p) {
@@ -2346,10 +2386,19 @@ int choose_config(const GemmProblem &p) {
     const bool dma = p.K % 128 == 0;
     const int64_t cus = num_cus();
     if (mg_per_channel(p)) {
-        // int4 weights, one scale per output channel: the per-group DMA kernels without the
-        // fold, chosen as for per-group int4 weights
+        // int4 weights, one scale per output channel (or the raw int32 sums): with enough tiles
+        // the 320 x 256 ping-pong form with the unpack in its memory phase, or the per-group DMA
+        // kernels without the fold, by rounds of tiles x tile area over the work rate per unit
+        // area (1.44 : 1, measured: M = 4096, N = 10240, K = 2560 96.6 against 138.7 us; M =
+        // 1024 45.1 against 55.6; M = 8192, N = 2560, K = 10240 153.1 against 282.7); few tiles:
+        // as for per-group int4 weights
         const int64_t t11 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
-        if (t11 >= cus / 2) return 11;
+        const int64_t t17 = (int64_t)((p.M + 255) / 256) * ((p.N + 319) / 320);
+        if (t11 >= cus / 2) {
+            const double c11 = (double)((t11 + cus - 1) / cus) * 128 * 256;
+            const double c17 = (double)((t17 + cus - 1) / cus) * 320 * 256 / 1.44;
+            return c17 < c11 ? 17 : 11;
+        }
         return p.M <= 1024 ? 12 : 4;
     }
     if (p.gs > 0 && p.out != OUT_I32) {
@@ -2560,6 +2609,8 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
     const bool grouped = p.gs > 0 && p.out != OUT_I32;
     if ((grouped || mg_per_channel(p)) && (id == 11 || id == 12) && p.K % 128 == 0)
         return dispatch_mg(p, id == 12, kConfigs[id].group_m, stream);
+    if (mg_per_channel(p) && id == 17) return launch_pp<320, 256, 2, 128, W_INT4>(p, kConfigs[17].group_m, stream);
+    if (id == 17) id = 16;
     if (grouped) {
         if (id != 4) id = 0;
         const int gm = kConfigs[id].group_m;
