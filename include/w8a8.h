@@ -319,9 +319,12 @@ int w8a8_gemm_splitk_noalloc(const int8_t *x_q, const float *s_x, const void *w,
  *   evaluated in fp32 (exact products on the matrix cores, fp32 sums, exp2 on pre-scaled
  *   scores) and rounded once to o_dtype.
  *   workspace / workspace_bytes: device memory for the per-slice partial results, at least
- *   sdpa_decode_workspace(B, Hq, Hkv, N, D) bytes (0 means one pass suffices); NULL or less
+ *   sdpa_decode_workspace(B, Hq, Hkv, N, D) bytes (0 means one pass suffices; the size holds
+ *   every slice count sdpa_decode_autotune may pick); NULL or less than the chosen count needs
  *   runs a single slice per KV head (correct, slower for long caches). Caller-owned, 16-byte
- *   aligned, contents unspecified on return; one per call in flight.
+ *   aligned, contents unspecified on return; one per call in flight. The slice count is the
+ *   autotuned one for this size class if sdpa_decode_autotune has run, else a fixed rule
+ *   (about one workgroup per compute unit, at least 128 keys per slice).
  * Constraints: B >= 0 (0: no-op), Hq % Hkv == 0, Hq / Hkv <= 16, D in {64, 128},
  * 1 <= N <= Ncap, 0 < scale < inf (usually 1 / sqrt(D)); inputs finite.
  * sdpa_decode_workspace returns -status for invalid arguments.
@@ -330,6 +333,26 @@ int64_t sdpa_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int
 int sdpa_decode(const void *q, const void *k, const void *v, int dtype, void *o, int o_dtype, int64_t B,
                 int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap, int64_t D, float scale, void *workspace,
                 int64_t workspace_bytes, void *stream);
+
+/*
+ * sdpa_decode_autotune -- the split's autotuning (Cider README "优化 SDPA（解码注意力）",
+ * AutoTune: block sizes swept per GQA ratio, head count and sequence length, the fastest
+ * cached). Runs sdpa_decode on the given tensors with each candidate number of key slices per
+ * KV head -- one slice, and the fixed rule's count r times 1/4, 1/2, 1, 2 and 4, each slice at
+ * least 128 keys, the partials within the workspace -- times each over 10 launches on the
+ * stream with HIP events, and records the fastest for (current device, dtype, B, Hq, Hkv, D,
+ * N rounded up to a power of two) in a process-wide table; later sdpa_decode calls of that
+ * size class use it (at most N / 128 slices at their N) instead of the rule. *slices_out (may
+ * be NULL) receives the count chosen. Arguments as sdpa_decode (B >= 1); o holds the last
+ * launch's result; a workspace of sdpa_decode_workspace(...) bytes fits every candidate.
+ * Waits for the stream: not for use under graph capture. The table is guarded by a mutex.
+ * sdpa_decode_tuned_slices returns the recorded count for the size class of these arguments on
+ * the current device, 0 if none, or -status for invalid arguments.
+ */
+int sdpa_decode_autotune(const void *q, const void *k, const void *v, int dtype, void *o, int o_dtype, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap, int64_t D, float scale, void *workspace,
+                         int64_t workspace_bytes, void *stream, int *slices_out);
+int sdpa_decode_tuned_slices(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D);
 
 /*
  * Debug knob: force the number of K-slices of w8a8_gemm_splitk (-1 = automatic, 1 = never

@@ -40,7 +40,8 @@ def test_header_declares_the_hot_path():
     for required in ("quantize_per_token", "quantize_weight", "w8a8_gemm_pc", "w8a8_gemm_pg",
                      "w4a8_gemm_pg", "w4a8_gemm_pc", "w8a8_linear", "w8a8_is_available", "w8a8_last_error",
                      "w8a8_status_string", "int8_mv", "w8a8_gemm_splitk", "w8a8_gemm_splitk_workspace",
-                     "rmsnorm_quantize", "sdpa_decode", "quantize_weight_clipped"):
+                     "rmsnorm_quantize", "sdpa_decode", "sdpa_decode_autotune", "sdpa_decode_tuned_slices",
+                     "quantize_weight_clipped"):
         assert required in names, names
 
 
@@ -358,11 +359,43 @@ def test_sdpa_validation(w8a8, kw, status, needle):
 def test_sdpa_forced_unavailable_and_workspace_query(w8a8, unavailable):
     lib = w8a8.lib()
     assert _sdpa(lib) == UNSUPPORTED_DEVICE
-    # the size query is host arithmetic: slices * B * Hq * (D + 4) * 4 bytes, 0 for one slice
+    # the size query is host arithmetic: slices * B * Hq * (D + 4) * 4 bytes for the most
+    # slices the autotuner may pick (4 x the rule's count, at least 128 keys each), 0 for one
+    # slice; with no GPU the rule takes 256 compute units: 64 slices for 4 KV heads
     assert lib.sdpa_decode_workspace(1, 32, 8, 64, 128) == 0
-    n = lib.sdpa_decode_workspace(1, 32, 4, 32768, 128)
-    assert n > 0 and n % (32 * 132 * 4) == 0
+    assert lib.sdpa_decode_workspace(1, 32, 4, 32768, 128) == 32 * 132 * 4 * 256
+    assert lib.sdpa_decode_workspace(1, 32, 4, 4096, 128) == 32 * 132 * 4 * 32  # N / 128 caps it
     assert lib.sdpa_decode_workspace(1, 32, 3, 1024, 128) < 0
+
+
+def _tune(lib, q=FAKE, dtype=F16, o_dtype=F16, B=1, Hq=8, Hkv=2, N=64, Ncap=64, D=128, scale=0.088, ws=None,
+          ws_bytes=0, out=None):
+    return lib.sdpa_decode_autotune(q, FAKE, FAKE, dtype, FAKE, o_dtype, B, Hq, Hkv, N, Ncap, D, scale, ws, ws_bytes,
+                                    None, out)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=F32), INVALID, "dtype"),
+    (dict(B=0), INVALID, "B"),
+    (dict(Hq=6, Hkv=4), INVALID, "Hkv"),
+    (dict(D=96), UNSUPPORTED_SHAPE, "D"),
+    (dict(N=65, Ncap=64), INVALID, "N"),
+    (dict(q=None), INVALID, "null"),
+    (dict(ws_bytes=-1), INVALID, "workspace_bytes"),
+])
+def test_sdpa_autotune_validation(w8a8, kw, status, needle):
+    lib = w8a8.lib()
+    assert _tune(lib, **kw) == status
+    assert needle in lib.w8a8_last_error().decode()
+
+
+def test_sdpa_autotune_unavailable_and_empty_table(w8a8, unavailable):
+    lib = w8a8.lib()
+    best = ctypes.c_int(-7)
+    assert _tune(lib, out=ctypes.byref(best)) == UNSUPPORTED_DEVICE
+    assert best.value == -7  # nothing written
+    assert lib.sdpa_decode_tuned_slices(F16, 1, 32, 8, 4096, 128) == 0
+    assert lib.sdpa_decode_tuned_slices(F16, 1, 32, 3, 4096, 128) == -INVALID
 
 
 def test_clock_probe_validation(w8a8, unavailable):

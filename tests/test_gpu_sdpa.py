@@ -93,6 +93,29 @@ def test_sdpa_parity(w8a8, B, Hq, Hkv, N, Ncap, D):
                 check(o, r, N, D, what)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,D", [(1, 32, 8, 4096, 128), (1, 32, 4, 32768, 128), (2, 8, 8, 3000, 64)])
+def test_sdpa_autotune(w8a8, B, Hq, Hkv, N, D):
+    """The autotuner picks one of its candidate slice counts, records it for the size class
+    (N rounded up to a power of two), and later calls in that class (here N and a shorter
+    cache) use it and still match the oracle; without a workspace only one slice is tried."""
+    q, k, v = inputs(B, Hq, Hkv, N, N, D, seed=B + Hq + Hkv + N)
+    qd, kd, vd = dev(q, False), dev(k, False), dev(v, False)
+    ws = torch.zeros(max(w8a8.sdpa_decode_workspace(B, Hq, Hkv, N, D), 16) // 4, dtype=torch.int32, device="cuda")
+    note(f"sdpa autotune B={B} Hq={Hq} Hkv={Hkv} N={N} D={D}")
+    best = w8a8.sdpa_decode_autotune(qd, kd, vd, workspace=ws)
+    assert 1 <= best <= max(1, N // 128), best
+    N2 = (1 << (N - 1).bit_length()) // 2 + 1  # the shortest cache of the same power-of-two class
+    assert w8a8.sdpa_decode_tuned_slices(torch.float16, B, Hq, Hkv, N, D) == best
+    assert w8a8.sdpa_decode_tuned_slices(torch.float16, B, Hq, Hkv, N2, D) == best
+    for n in (N, N2):
+        r = oracle.sdpa_decode(q, k, v, N=n, bf16=False)
+        o = w8a8.sdpa_decode(qd, kd, vd, N=n, workspace=ws)
+        torch.cuda.synchronize()
+        check(o, r, n, D, f"after autotune (best {best}) N={n}")
+    assert w8a8.sdpa_decode_autotune(qd, kd, vd, workspace=None) == 1
+    w8a8.sdpa_decode_autotune(qd, kd, vd, workspace=ws)  # leave the class tuned with a workspace
+
+
 def test_sdpa_graph_replay(w8a8):
     B, Hq, Hkv, N, D = 1, 32, 8, 8192, 128
     q, k, v = inputs(B, Hq, Hkv, N, N, D, seed=3)

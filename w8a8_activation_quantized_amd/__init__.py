@@ -55,6 +55,9 @@ _SIGNATURES = {
     "sdpa_decode_workspace": ([_i64, _i64, _i64, _i64, _i64], _i64),
     "sdpa_decode": ([_vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _i64,
                      _vp], _int),
+    "sdpa_decode_autotune": ([_vp, _vp, _vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
+                              _i64, _vp, ctypes.POINTER(ctypes.c_int)], _int),
+    "sdpa_decode_tuned_slices": ([_int, _i64, _i64, _i64, _i64, _i64], _int),
 }
 for _name, (_args, _res) in _SIGNATURES.items():
     _f = getattr(_lib, _name)
@@ -364,3 +367,32 @@ def sdpa_decode(q, k, v, N=None, scale=None, out_dtype=None, o=None, workspace=N
     _check(_lib.sdpa_decode(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], _ptr(o), _DTYPE_CODE[o.dtype], B, Hq, Hkv,
                             N, Ncap, D, scale, _ptr(workspace), ws_bytes, _stream(stream)))
     return o
+
+
+def sdpa_decode_autotune(q, k, v, N=None, scale=None, out_dtype=None, o=None, workspace=None, stream=None) -> int:
+    """Time sdpa_decode on these tensors for each candidate slice count and record the fastest
+    for their size class (later sdpa_decode calls use it). Returns the count chosen. Waits for
+    the stream; arguments as sdpa_decode."""
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("q, k, v must be contiguous fp16 / bf16 tensors")
+    B, Hq, D = q.shape
+    _, Hkv, Ncap, _ = k.shape
+    N = Ncap if N is None else N
+    scale = 1.0 / (D ** 0.5) if scale is None else scale
+    if o is None:
+        o = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    best = ctypes.c_int(0)
+    _check(_lib.sdpa_decode_autotune(_ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype], _ptr(o), _DTYPE_CODE[o.dtype], B, Hq,
+                                     Hkv, N, Ncap, D, scale, _ptr(workspace), ws_bytes, _stream(stream),
+                                     ctypes.byref(best)))
+    return best.value
+
+
+def sdpa_decode_tuned_slices(dtype, B, Hq, Hkv, N, D) -> int:
+    """The autotuned slice count for this size class on the current device (0: none)."""
+    n = _lib.sdpa_decode_tuned_slices(_DTYPE_CODE[dtype], B, Hq, Hkv, N, D)
+    if n < 0:
+        raise W8A8Error(-n, _lib.w8a8_last_error().decode())
+    return n

@@ -511,6 +511,34 @@ int sdpa_decode(const void *q, const void *k, const void *v, int dtype, void *o,
                     fn);
 }
 
+int sdpa_decode_autotune(const void *q, const void *k, const void *v, int dtype, void *o, int o_dtype, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t N, int64_t Ncap, int64_t D, float scale, void *workspace,
+                         int64_t workspace_bytes, void *stream, int *slices_out) {
+    const char *fn = "sdpa_decode_autotune";
+    int rc = check_sdpa(fn, dtype, o_dtype, B, Hq, Hkv, N, Ncap, D, scale);
+    if (rc != W8A8_OK) return rc;
+    if (B < 1) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: B must be at least 1", fn);
+    if (workspace_bytes < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace_bytes < 0", fn);
+    if (workspace && !aligned16(workspace))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+    if (!q || !k || !v || !o) return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", fn);
+    if ((rc = check_device()) != W8A8_OK) return rc;
+    return launched(w8a8::sdpa_autotune(q, k, v, dtype == W8A8_BF16, o, o_dtype, (int)B, (int)Hq, (int)Hkv, (int)N,
+                                        (int)Ncap, (int)D, scale, workspace, workspace_bytes,
+                                        static_cast<hipStream_t>(stream), slices_out),
+                    fn);
+}
+
+int sdpa_decode_tuned_slices(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D) {
+    const char *fn = "sdpa_decode_tuned_slices";
+    const int rc = check_sdpa(fn, dtype, W8A8_F16, B, Hq, Hkv, N, N, D, 1.0f);
+    if (rc != W8A8_OK) return -rc;
+    ok();
+    return w8a8::sdpa_tuned_slices(dtype == W8A8_BF16, (int)B, (int)Hq, (int)Hkv, (int)N, (int)D);
+}
+
 int64_t w8a8_gemm_splitk_workspace(int weight_bits, int group_size, int y_dtype, int64_t M, int64_t N,
                                    int64_t K) {
     const char *fn = "w8a8_gemm_splitk_workspace";

@@ -70,11 +70,18 @@ hipError_t launch_mv(const GemmProblem &p, hipStream_t stream);
 // [B, Hkv, Ncap, D] (first N rows used); fp16 or bf16; o [B, Hq, D] of out. Splits the keys
 // over sdpa_slices(...) workgroups per KV head when ws holds sdpa_workspace_bytes(...), else
 // runs one slice.
+// The slice count is the autotuner's for this size class when it has run on this device
+// (sdpa_autotune), else a fixed rule (sdpa_slices); the workspace size covers every count
+// the autotuner may choose.
 int sdpa_slices(int B, int Hkv, int N);
 int64_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int N, int D);
 hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool bf16, void *o, int out, int B, int Hq,
                               int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes,
                               hipStream_t stream);
+int sdpa_tuned_slices(bool bf16, int B, int Hq, int Hkv, int N, int D);
+hipError_t sdpa_autotune(const void *q, const void *k, const void *v, bool bf16, void *o, int out, int B, int Hq,
+                         int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes, hipStream_t stream,
+                         int *best_out);
 
 // Measurement aid: `blocks` workgroups each store, at out[4 b .. 4 b + 2], where they ran
 // (XCC_ID << 32 | HW_ID), the shader-clock counter and the 100 MHz counter.

@@ -20,6 +20,9 @@
 //    p = exp2(s - m), and the running sums are rescaled by exp2(m_old - m_new) per block.
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "device_common.h"
 #include "internal.h"
@@ -398,14 +401,42 @@ int sdpa_slices(int B, int Hkv, int N) {
     return std::max(1, std::min(s, 1024));
 }
 
-int64_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int N, int D) {
-    const int s = sdpa_slices(B, Hkv, N);
-    return s > 1 ? (int64_t)B * Hq * s * (D + 4) * 4 : 0;
+// Most slices any call may use: four times the rule's count (the autotuner's largest
+// candidate), at least 128 keys per slice. The workspace query sizes for it, so a tuned
+// count always fits a workspace of the queried size.
+int sdpa_max_slices(int B, int Hkv, int N) {
+    return std::max(1, std::min(std::min(4 * sdpa_slices(B, Hkv, N), std::max(1, N / 128)), 1024));
 }
 
-hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool bf16, void *o, int out, int B, int Hq,
-                              int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes,
-                              hipStream_t stream) {
+static int64_t part_bytes(int B, int Hq, int slices, int D) {
+    return slices > 1 ? (int64_t)B * Hq * slices * (D + 4) * 4 : 0;
+}
+
+int64_t sdpa_workspace_bytes(int B, int Hq, int Hkv, int N, int D) {
+    return part_bytes(B, Hq, sdpa_max_slices(B, Hkv, N), D);
+}
+
+// Tuned slice counts (the pages' AutoTune table): per device, input format, B, Hq, Hkv, D
+// and the cache length rounded up to a power of two.
+namespace {
+using TuneKey = std::tuple<int, bool, int, int, int, int, int>;
+std::mutex g_tune_mutex;
+std::map<TuneKey, int> g_tuned;
+
+int n_bucket(int N) {
+    int b = 0;
+    while ((1 << b) < N && b < 30) ++b;
+    return b;
+}
+
+TuneKey tune_key(bool bf16, int B, int Hq, int Hkv, int N, int D) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    return TuneKey(dev, bf16, B, Hq, Hkv, D, n_bucket(N));
+}
+
+SdpaArgs make_args(const void *q, const void *k, const void *v, void *o, int out, int B, int Hq, int Hkv, int N,
+                   int Ncap, float scale, void *ws, int slices) {
     SdpaArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
@@ -419,11 +450,74 @@ hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool 
     a.Ncap = Ncap;
     a.out = out;
     a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e), rounded once
-    a.slices = sdpa_slices(B, Hkv, N);
-    if (a.slices > 1 && (ws == nullptr || ws_bytes < sdpa_workspace_bytes(B, Hq, Hkv, N, D))) a.slices = 1;
+    a.slices = slices;
     a.part = static_cast<float *>(ws);
+    return a;
+}
+
+hipError_t launch_args(const SdpaArgs &a, bool bf16, int D, hipStream_t stream) {
     if (D == 64) return bf16 ? launch_sdpa_t<64, true>(a, stream) : launch_sdpa_t<64, false>(a, stream);
     return bf16 ? launch_sdpa_t<128, true>(a, stream) : launch_sdpa_t<128, false>(a, stream);
+}
+}  // namespace
+
+int sdpa_tuned_slices(bool bf16, int B, int Hq, int Hkv, int N, int D) {
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    const auto it = g_tuned.find(tune_key(bf16, B, Hq, Hkv, N, D));
+    return it == g_tuned.end() ? 0 : it->second;
+}
+
+hipError_t launch_sdpa_decode(const void *q, const void *k, const void *v, bool bf16, void *o, int out, int B, int Hq,
+                              int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes,
+                              hipStream_t stream) {
+    // the tuned count for this size class if there is one (at most N / 128 slices at this N),
+    // else the rule; one slice when the workspace cannot hold the partials
+    int slices = sdpa_tuned_slices(bf16, B, Hq, Hkv, N, D);
+    slices = slices > 0 ? std::max(1, std::min(slices, std::max(1, N / 128))) : sdpa_slices(B, Hkv, N);
+    if (slices > 1 && (ws == nullptr || ws_bytes < part_bytes(B, Hq, slices, D))) slices = 1;
+    return launch_args(make_args(q, k, v, o, out, B, Hq, Hkv, N, Ncap, scale, ws, slices), bf16, D, stream);
+}
+
+hipError_t sdpa_autotune(const void *q, const void *k, const void *v, bool bf16, void *o, int out, int B, int Hq,
+                         int Hkv, int N, int Ncap, int D, float scale, void *ws, int64_t ws_bytes, hipStream_t stream,
+                         int *best_out) {
+    // candidates: one slice, and the rule's count times 1/4, 1/2, 1, 2, 4 (at least 128 keys
+    // each, partials within the workspace); each timed over 10 launches after one untimed
+    const int r = sdpa_slices(B, Hkv, N), smax = sdpa_max_slices(B, Hkv, N);
+    int cand[6] = {1, std::max(1, r / 4), std::max(1, r / 2), r, 2 * r, 4 * r};
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    int best = 0;
+    float best_ms = 0.f;
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) {
+        const int s = cand[i];
+        if (s > smax || (s > 1 && (ws == nullptr || ws_bytes < part_bytes(B, Hq, s, D)))) continue;
+        bool seen = false;
+        for (int j = 0; j < i; ++j) seen = seen || cand[j] == s;
+        if (seen) continue;
+        const SdpaArgs a = make_args(q, k, v, o, out, B, Hq, Hkv, N, Ncap, scale, ws, s);
+        if ((e = launch_args(a, bf16, D, stream)) != hipSuccess) break;
+        if ((e = hipEventRecord(e0, stream)) != hipSuccess) break;
+        for (int rep = 0; rep < 10 && e == hipSuccess; ++rep) e = launch_args(a, bf16, D, stream);
+        if (e != hipSuccess || (e = hipEventRecord(e1, stream)) != hipSuccess) break;
+        if ((e = hipEventSynchronize(e1)) != hipSuccess) break;
+        float ms = 0.f;
+        if ((e = hipEventElapsedTime(&ms, e0, e1)) != hipSuccess) break;
+        if (best == 0 || ms < best_ms) {
+            best = s;
+            best_ms = ms;
+        }
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mutex);
+        g_tuned[tune_key(bf16, B, Hq, Hkv, N, D)] = best;
+    }
+    if (best_out) *best_out = best;
+    return hipSuccess;
 }
 
 }  // namespace w8a8
