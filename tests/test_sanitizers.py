@@ -51,21 +51,25 @@ def test_oracle_pins_under_asan_and_ubsan(tmp_path):
 
 
 def test_abi_host_code_under_asan_and_ubsan(tmp_path):
-    objs = [os.path.join(ROOT, "w8a8_activation_quantized_amd", "_build", f + ".o")
-            for f in ("quantize", "gemm", "mv", "sdpa", "diag")]
-    if not all(os.path.exists(o) for o in objs):
-        pytest.skip("the library objects are not built (run the build first)")
     rt = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
     if not rt or not os.path.exists(HIPCC):
         pytest.skip("hipcc or clang's AddressSanitizer runtime is not installed")
-    abi_o = str(tmp_path / "abi_san.o")
     lib = str(tmp_path / "libw8a8_san.so")
-    # host-side sanitizers only: each -fsanitize applies to the host compilation (-Xarch_host)
+    # host-side sanitizers only: each -fsanitize applies to the host compilation (-Xarch_host);
+    # every source's host code (argument checks, dispatch, plans, the autotuning table)
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-ffp-contract=off",
-                           *san, "-c", os.path.join(ROOT, "w8a8_activation_quantized_amd", "csrc", "abi.hip"),
-                           "-o", abi_o])
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, "-o", lib, abi_o, *objs])
+    csrc = os.path.join(ROOT, "w8a8_activation_quantized_amd", "csrc")
+    objs, procs = [], []
+    for f in ("abi", "quantize", "gemm", "mv", "sdpa", "diag"):
+        o = str(tmp_path / (f + "_san.o"))
+        objs.append(o)
+        procs.append(subprocess.Popen([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
+                                       "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-Xclang",
+                                       "-target-feature", "-Xclang", "-packed-fp32-ops", *san, "-c",
+                                       os.path.join(csrc, f + ".hip"), "-o", o],
+                                      stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL))
+    assert all(pr.wait() == 0 for pr in procs), "sanitizer build failed"
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, "-o", lib, *objs])
     out = _child({"W8A8_LIB": lib, "LD_PRELOAD": rt[-1]}, ["tests/test_abi_cpu.py"], timeout=900, log_dir=tmp_path)
     assert " passed" in out
