@@ -2367,8 +2367,11 @@ hipError_t dispatch_mg(const GemmProblem &p, bool small, int group_m, hipStream_
                           : launch_mg<64, 64, 4, 2, 2, 128, W_INT8, SPLIT>(p, group_m, stream);
     }
     if (p.wkind == W_INT4) {
-        if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT4, SPLIT>(p, group_m, stream);
-        return launch_mg<128, 256, 3, 2, 4, 128, W_INT4, SPLIT>(p, group_m, stream);
+        // waves of 32 weight rows x 128 tokens: each packed weight fragment is unpacked by
+        // two waves instead of four (gs=128 M=4096 N=10240 K=2560: 161 against 173 us with
+        // 64 x 64 per wave; gs=64 197 against 214), for 25 % more fragment reads
+        if (p.gs == 64) return launch_mg<128, 256, 3, 4, 2, 64, W_INT4, SPLIT>(p, group_m, stream);
+        return launch_mg<128, 256, 3, 4, 2, 128, W_INT4, SPLIT>(p, group_m, stream);
     }
     if (p.gs == 64) return launch_mg<128, 256, 3, 2, 4, 64, W_INT8, SPLIT>(p, group_m, stream);
     return launch_mg<128, 256, 3, 2, 4, 128, W_INT8, SPLIT>(p, group_m, stream);
