@@ -2282,6 +2282,7 @@ constexpr Config kConfigs[] = {
     {128, 64, 4},   // 15: direct-to-LDS, BN=64 BM=128, 6 stages, 8 waves (32 n x 32 m each); mid M
     {256, 320, 8},  // 16: as 13 with two stages of 128-value K-tiles (128-byte DMA row segments)
     {256, 320, 8},  // 17: as 16 with int4 weights (per-channel scales or raw int32 sums); int8: 16
+    {256, 256, 8},  // 18: as 16 with 256 x 256 tiles (64 x 128 per wave)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2437,11 +2438,17 @@ int choose_config(const GemmProblem &p) {
     // form takes M = 2048, N = 6144, K = 4096: 54.6 against 56.8 us for 128 x 256; M = 1536,
     // N = 10240, K = 2560: 40.0 against 44.2; M = 2048, N = 10240: 45.3 against 47.6; and
     // ties 160 x 256 at M = 2048, N = 24576, K = 4096, 173.9 against 172.5 us.)
+    // The 256 x 256 ping-pong form (18): 1.1, where its rounds fit better than the 320-wide
+    // one's (M = 2048, N = 24576, K = 4096: 163.5 against 185.7 us for 160 x 256; M = 2048,
+    // N = 6144, K = 4096: 52.7 against 58.4; M = 3072, N = 10240, K = 2560: 76.1 against 81.4;
+    // every other shape of that sweep keeps its choice).
     const int64_t t13 = (int64_t)((p.M + 255) / 256) * ((p.N + 319) / 320);
+    const int64_t t18 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
     const int64_t t6 = (int64_t)((p.M + 255) / 256) * ((p.N + 159) / 160);
     const int64_t t7 = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
     const int64_t t12 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
     const double c13 = (double)((t13 + cus - 1) / cus) * 320 * 256 / 1.2;
+    const double c18 = (double)((t18 + cus - 1) / cus) * 256 * 256 / 1.1;
     const double c6 = (double)((t6 + cus - 1) / cus) * 160 * 256 / 1.0;
     const double c7 = (double)((t7 + cus - 1) / cus) * 128 * 256 / 0.9;
     const double c12 = (double)((t12 + cus - 1) / cus) * 64 * 64 / 0.4;
@@ -2450,8 +2457,9 @@ int choose_config(const GemmProblem &p) {
     // 94.0 us at M = 4096, N = 10240, K = 2560; 148 against 150.5 us at M = 8192, N = 2560,
     // K = 10240; 177 against 183 us at M = 8192, N = 10240, K = 2560; whole 128-byte row
     // segments per DMA halve the L2 requests, and the chip holds a 6 % higher clock)
-    if (c12 < c6 && c12 < c7 && c12 < c13) return 12;
-    if (c13 < c6 && c13 < c7) return 16;
+    if (c12 < c6 && c12 < c7 && c12 < c13 && c12 < c18) return 12;
+    if (c13 < c6 && c13 < c7 && c13 <= c18) return 16;
+    if (c18 < c6 && c18 < c7) return 18;
     return c6 <= c7 ? 6 : 7;
 }
 
@@ -2628,6 +2636,7 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 12: return launch_ms<64, 64, 4, 2, 2>(p, gm, stream);
         case 13: return launch_pp<320, 256, 4>(p, gm, stream);
         case 16: return launch_pp<320, 256, 2, 128>(p, gm, stream);
+        case 18: return launch_pp<256, 256, 2, 128>(p, gm, stream);
         case 14: return launch_ms<128, 128, 4, 2, 2>(p, gm, stream);
         case 15: return launch_ms<64, 128, 6, 2, 4>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
