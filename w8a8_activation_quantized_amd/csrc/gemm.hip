@@ -663,7 +663,15 @@ struct PpShape {
     static constexpr int FULL_WAVES = PIECES - (PPW - 1) * NW;
     static constexpr int LDS = 163840;
     static constexpr int CPR = BN / 8;                   // 16-byte output chunks per staged row
+    // The tile's scales (s_x of its BM tokens, then s_w of its BN channels), copied to LDS with
+    // the first stage: past the stage buffers, and in the rows of the staged output that are
+    // written last (rows 3/4 BM and up belong to the second half) or past the staged tile.
+    static constexpr int SCO = STAGES * STAGE > BM * BN * 3 / 2 ? STAGES * STAGE : BM * BN * 3 / 2;
+    static constexpr int SC_PIECES = (BM + BN) / 64;     // 4-byte DMA pieces of 64 scales
+    static constexpr int HALF_ITS = BM / 2 * CPR / NT;   // store iterations per staged half
     static_assert(BN % 64 == 0 && BM % 32 == 0, "tile shape");
+    static_assert(SCO + (BM + BN) * 4 <= LDS && SCO % 16 == 0, "scale region");
+    static_assert(BM / 2 * CPR % NT == 0 && (BM / 16) % 2 == 0, "staged halves");
     static_assert(BKS == 64 ? STAGES >= 3 && STAGES <= 4 : BKS == 128 && STAGES == 2, "stages");
     static_assert(WK == W_INT8 || BKS == 128, "int4 weights take 128-value stages");
     static_assert(STAGES * STAGE <= LDS, "LDS");
@@ -786,6 +794,86 @@ __device__ __forceinline__ void pp_loop2(v4i (&acc)[S::FN][S::FM], const int8_t 
     }
 }
 
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// f(integral_constant<int, i>) for i = I .. E-1, unrolled at compile time
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < E) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, E>(f);
+    }
+}
+
+// Two outputs rounded to fp16 (or bf16) in one conversion, RNE, packed low-first. The fp32
+// inputs are pinned in registers so that the compiler cannot merge the preceding multiply
+// into a mixed-precision fma (one rounding of the exact product).
+template <bool BF>
+__device__ __forceinline__ uint32_t pack_2x16(float a, float b) {
+    asm volatile("" : "+v"(a), "+v"(b));
+    const float2_t v = {a, b};
+    if constexpr (BF) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    } else {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    }
+}
+
+// Epilogue of the 16-bit outputs: the tile is staged through LDS as [BM][BN] rows (16-byte
+// chunk index XOR-ed with (row & 7): the MFMA layout's 8-byte writes, 16 rows per
+// instruction, and the row-contiguous 16-byte reads both stay free of bank conflicts) and
+// written as 16-byte pieces of output rows, in two halves: rows [64 h, 64 h + 64) of each
+// group's 128 (fragment rows fm in [FM/2 h, FM/2 h + FM/2)). The second half is converted
+// and staged while the first half's stores go out, between them, so the conversion work
+// and the store traffic overlap.
+template <class S, bool BF>
+__device__ __forceinline__ void pp_store_staged(const v4i (&acc)[S::FN][S::FM], const float (&sxm)[S::FM],
+                                                const float4 (&s4)[S::FN], int8_t *smem, const GemmProblem &p, int m0,
+                                                int n0, int grp, int wq, int frow, int fchunk, int tid) {
+    constexpr int FN = S::FN, FM = S::FM, HF = FM / 2, RS = S::BN * 2, CPR = S::CPR, HR = S::WM / 2;
+    constexpr int ITS = S::HALF_ITS;
+    int coff[FN];  // byte offset in a staged row of this lane's 8-byte piece (row & 7 == frow & 7)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int nl = wq * S::WN + fn * 16 + 4 * fchunk;
+        coff[fn] = (((nl >> 3) ^ (frow & 7)) << 4) + ((nl & 4) << 1);
+    }
+    int8_t *rbase = smem + (grp * S::WM + frow) * RS;
+    auto stage = [&](auto fmc) __attribute__((always_inline)) {
+        constexpr int fm = decltype(fmc)::value;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const v4i v = acc[fn][fm];
+            const float y0 = ((float)v[0] * sxm[fm]) * s4[fn].x, y1 = ((float)v[1] * sxm[fm]) * s4[fn].y;
+            const float y2 = ((float)v[2] * sxm[fm]) * s4[fn].z, y3 = ((float)v[3] * sxm[fm]) * s4[fn].w;
+            *reinterpret_cast<uint2 *>(rbase + fm * 16 * RS + coff[fn]) = make_uint2(pack_2x16<BF>(y0, y1), pack_2x16<BF>(y2, y3));
+        }
+    };
+    const int rows = min(S::BM, p.M - m0), cols = min(S::BN, p.N - n0);
+    uint16_t *y = static_cast<uint16_t *>(p.y);
+    // store iteration `it` of half h: chunk c = tid + NT it of the half's BM/2 rows
+    auto store = [&](int h, int it) __attribute__((always_inline)) {
+        const int c = tid + it * S::NT;
+        const int rr = c / CPR, cc = c - rr * CPR;
+        const int r = (rr % HR) + (rr / HR) * S::WM + h * HR;
+        if (r < rows && cc * 8 < cols) {
+            const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + ((cc ^ (r & 7)) << 4));
+            *reinterpret_cast<v4u *>(y + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+        }
+    };
+    static_for<0, HF>([&](auto q) { stage(q); });
+    lds_barrier();
+    static_for<0, HF>([&](auto q) {
+        constexpr int qi = decltype(q)::value;
+        static_for<qi * ITS / HF, (qi + 1) * ITS / HF>([&](auto it) { store(0, decltype(it)::value); });
+        stage(std::integral_constant<int, HF + qi>{});
+    });
+    lds_barrier();
+    static_for<0, ITS>([&](auto it) { store(1, decltype(it)::value); });
+}
+
 template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tmap) {
     using S = PpShape<BN, BM, STAGES, BKS, WK>;
@@ -835,6 +923,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
 
     const int frow = lane & 15, fchunk = lane >> 4;
     const int KT = K / S::BK;
+    // the tile's scales go out first, so every wait for the first stage retires them
+    for (int i = wave; i < S::SC_PIECES; i += S::NW) {
+        const float *ssrc = i < BM / 64 ? p.sx + min(m0 + 64 * i + lane, M - 1)
+                                        : p.sw + min(n0 + 64 * (i - BM / 64) + lane, N - 1);
+        dma_4B(ssrc, smem + S::SCO + 256 * i);
+    }
     if constexpr (S::BKS == 64) {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
@@ -872,45 +966,21 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
     }
 
     // ---- epilogue (per-channel dequant or raw int32) ----
-    const float *__restrict__ sxp = p.sx;
-    const float *__restrict__ swp = p.sw;
+    // scales from the tile's LDS copy: entry j of s_w is s_w[min(n0 + j, N - 1)], so the
+    // channels of a partial tile that are stored read their own scales
+    const float *scl = reinterpret_cast<const float *>(smem + S::SCO);
     float sxm[FM];
     float4 s4[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) sxm[fm] = sxp[min(m0 + grp * S::WM + fm * 16 + frow, M - 1)];
+    for (int fm = 0; fm < FM; ++fm) sxm[fm] = scl[grp * S::WM + fm * 16 + frow];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-        s4[fn] = *reinterpret_cast<const float4 *>(swp + min(n0 + wq * S::WN + fn * 16 + 4 * fchunk, N - 4));
+    for (int fn = 0; fn < FN; ++fn) s4[fn] = *reinterpret_cast<const float4 *>(scl + BM + wq * S::WN + fn * 16 + 4 * fchunk);
     const int out = p.out;
     if ((out == OUT_F16 || out == OUT_BF16) && p.y_rows16) {
-        // staged through LDS as [BM][BN] 16-bit rows with the 16-byte chunk index XOR-ed
-        // with (row & 7): the MFMA layout's 8-byte writes (16 rows per instruction) and
-        // the row-contiguous 16-byte reads both stay free of bank conflicts
-        constexpr int RS = S::BN * 2;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int lr = grp * S::WM + fm * 16 + frow;
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const v4i v = acc[fn][fm];
-                const float y0 = ((float)v[0] * sxm[fm]) * s4[fn].x, y1 = ((float)v[1] * sxm[fm]) * s4[fn].y;
-                const float y2 = ((float)v[2] * sxm[fm]) * s4[fn].z, y3 = ((float)v[3] * sxm[fm]) * s4[fn].w;
-                const uint2 w = out == OUT_F16 ? make_uint2(f16_bits(y0) | (f16_bits(y1) << 16), f16_bits(y2) | (f16_bits(y3) << 16))
-                                               : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
-                const int nl = wq * S::WN + fn * 16 + 4 * fchunk;
-                *reinterpret_cast<uint2 *>(smem + lr * RS + (((nl >> 3) ^ (lr & 7)) << 4) + ((nl & 4) << 1)) = w;
-            }
-        }
-        lds_barrier();
-        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
-#pragma unroll 4
-        for (int c = tid; c < S::BM * S::CPR; c += S::NT) {
-            const int r = c / S::CPR, cc = c - r * S::CPR;
-            if (r < rows && cc * 8 < cols) {
-                const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + ((cc ^ (r & 7)) << 4));
-                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
-            }
-        }
+        if (out == OUT_F16)
+            pp_store_staged<S, false>(acc, sxm, s4, smem, p, m0, n0, grp, wq, frow, fchunk, tid);
+        else
+            pp_store_staged<S, true>(acc, sxm, s4, smem, p, m0, n0, grp, wq, frow, fchunk, tid);
         return;
     }
 #pragma unroll
