@@ -124,10 +124,61 @@ def cpu_baseline(x, W, bits, gs, budget_s):
             break
     dt = time.perf_counter() - t0
     ops = 2.0 * rows_done * N * K
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": _omp_threads(), "kind": "oracle",
+            "host": _cpu_model(),
             "sample": f"first {rows_done} of {x.shape[0]} token rows (full N={N}, K={K}); "
                       f"per-token quantize + int GEMM + fp64 dequant; {dt:.2f} s"}
+
+
+def _gomp():
+    """The OpenMP runtime the oracle library links (gcc's libgomp), or None."""
+    import ctypes
+    try:
+        return ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+
+
+def _omp_threads():
+    g = _gomp()
+    if g is not None:
+        return int(g.omp_get_max_threads())
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_single_thread():
+    """The oracle on one thread, on the small per-channel workload (M=128, N=10240, K=2560)."""
+    import oracle
+    from synth_inputs import linear_inputs
+
+    g = _gomp()
+    if g is None:
+        return None
+    M, N, K = 128, 10240, 2560
+    x, W = linear_inputs(M, N, K, seed=0)
+    oracle.build(force=False)
+    wq, sw = oracle.quantize_weight(W, 8, 0)
+    before = int(g.omp_get_max_threads())
+    g.omp_set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.linear_pc(x, wq, sw)
+        dt = time.perf_counter() - t0
+    finally:
+        g.omp_set_num_threads(before)
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TOPS", "cores": 1,
+            "sample": f"M={M} N={N} K={K} per channel, whole; {dt:.2f} s"}
 
 
 def mv_decode(args, torch, w8a8, gs):
@@ -564,6 +615,8 @@ def main():
         M, N, K, bits, gs = WORKLOADS[args.workload]
         x_np, W_np = linear_inputs(M, N, K, seed=0)
         result["cpu_baseline"] = cpu_baseline(x_np, W_np, bits, gs, args.cpu_seconds)
+        if args.workload == "pc":
+            result["cpu_baseline"]["single_thread"] = cpu_single_thread()
     print(json.dumps(result), flush=True)
     return 0
 
