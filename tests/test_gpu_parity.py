@@ -241,6 +241,28 @@ def test_gemm_strided_output_and_empty(w8a8):
     assert y.shape == (0, 272)
 
 
+@pytest.mark.parametrize("M,N,K,pad", [(4000, 10000, 512, 0), (2100, 12000, 256, 8)])
+def test_pc_several_rounds_of_tiles(w8a8, M, N, K, pad):
+    """More output tiles than compute units (several rounds of workgroups) in the ping-pong
+    configurations 16 and 18 with 16-bit outputs staged in LDS: partial tiles in M and N,
+    contiguous and strided output rows; bit-exact against the oracle's fp32 evaluation, and
+    the padding columns untouched."""
+    x, W = linear_inputs(M, N, K, seed=M + N)
+    r = oracle_mode("pc", x, W)
+    try:
+        for cfg in (-1, 16, 18):
+            w8a8.w8a8_debug_force_config(cfg)
+            for out, fmt in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
+                note(f"several rounds: config {cfg} M={M} N={N} K={K} ldy={N + pad} {fmt}")
+                ybig = torch.zeros((M, N + pad), dtype=out, device="cuda")
+                run_mode(w8a8, "pc", x, W, out, y=ybig[:, :N])
+                got = host(ybig)
+                check_exact(got[:, :N], fmt, r["y32"], f"cfg {cfg} {M}x{N}x{K} {fmt}")
+                assert (got[:, N:] == 0).all()
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
+
+
 @pytest.mark.parametrize("mode", ["pc", "pg64", "w4_128", "w4_0"])
 def test_every_config_identical(w8a8, mode):
     """Every tile configuration gives bit-identical results (catches edge-mask and LDS races)."""
