@@ -339,13 +339,15 @@ int sdpa_decode(const void *q, const void *k, const void *v, int dtype, void *o,
  * AutoTune: block sizes swept per GQA ratio, head count and sequence length, the fastest
  * cached). Runs sdpa_decode on the given tensors with each candidate number of key slices per
  * KV head -- one slice, and the fixed rule's count r times 1/4, 1/2, 1, 2 and 4, each slice at
- * least 128 keys, the partials within the workspace -- times each over 10 launches on the
- * stream with HIP events, and records the fastest for (current device, dtype, B, Hq, Hkv, D,
- * N rounded up to a power of two) in a process-wide table; later sdpa_decode calls of that
- * size class use it (at most N / 128 slices at their N) instead of the rule. *slices_out (may
- * be NULL) receives the count chosen. Arguments as sdpa_decode (B >= 1); o holds the last
- * launch's result; a workspace of sdpa_decode_workspace(...) bytes fits every candidate.
- * Waits for the stream: not for use under graph capture. The table is guarded by a mutex.
+ * least 128 keys, the partials within the workspace -- times each as a captured HIP graph of
+ * 20 calls, replayed on a private stream (created and destroyed here, ordered after the work
+ * already on `stream`), and records the fastest for (current device, dtype, B, Hq, Hkv, D,
+ * N rounded up to a power of two) in a process-wide table, keeping the rule's count unless
+ * another is at least 3 % faster; later sdpa_decode calls of that size class use it (at most
+ * N / 128 slices at their N) instead of the rule. *slices_out (may be NULL) receives the count
+ * chosen. Arguments as sdpa_decode (B >= 1); o holds the last launch's result; a workspace of
+ * sdpa_decode_workspace(...) bytes fits every candidate. Returns after the timed launches have
+ * finished: not for use under graph capture. The table is guarded by a mutex.
  * sdpa_decode_tuned_slices returns the recorded count for the size class of these arguments on
  * the current device, 0 if none, or -status for invalid arguments.
  */
