@@ -77,21 +77,28 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha(rel_path):
-    with open(os.path.join(ROOT, rel_path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(rel_paths):
+    """sha256 of the named source files' bytes, concatenated in order ('a+b+c': a kernel's
+    translation unit and the local headers it includes)."""
+    h = hashlib.sha256()
+    for rel in rel_paths.split("+"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed counter summary, if the
-    kernel's source file still has the hash recorded there."""
+    kernel's source files still have the hash recorded there."""
     path = os.path.join(ROOT, "profiles", f"traffic_gemm_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     fields = dict(re.findall(r"^\s*-?\s*(\w+)\s*=\s*(\S+)\s*$", text, flags=re.M))
     src = fields.get("kernel_source")
-    if not src or not os.path.exists(os.path.join(ROOT, src)) or fields.get("kernel_source_sha256") != source_sha(src):
+    if not src or not all(os.path.exists(os.path.join(ROOT, p)) for p in src.split("+")):
+        return None
+    if fields.get("kernel_source_sha256") != source_sha(src):
         return None
     try:
         return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])

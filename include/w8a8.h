@@ -99,7 +99,7 @@ int quantize_per_token(const void *x, int x_dtype, int64_t M, int64_t K, int64_t
  *   gamma  [K] fp16 or bf16 (gamma_dtype)
  *   eps    finite, >= 0
  * Constraints: M >= 0, K >= 8, K % 8 == 0, ldx >= K, ldx % 8 == 0, all pointers 16-byte
- * aligned. Inputs finite, sum of x^2 finite in fp32.
+ * aligned. Inputs finite; the sum of x^2 and every product x * gamma finite in fp32.
  */
 int rmsnorm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx, const void *gamma,
                      int gamma_dtype, float eps, int8_t *x_q, float *s_x, void *stream);
@@ -120,7 +120,7 @@ int rmsnorm_quantize(const void *x, int x_dtype, int64_t M, int64_t K, int64_t l
  *   gate, up  [M, I] fp16 or bf16 (dtype), row strides ldg, ldu elements (they may be views
  *             into one [M, 2 I] array)
  * Constraints: M >= 0, I >= 8, I % 8 == 0, ldg, ldu >= I and multiples of 8, all pointers
- * 16-byte aligned. Inputs finite.
+ * 16-byte aligned. Inputs finite, and every h finite in fp32 (bf16 gate and up can overflow it).
  */
 int swiglu_quantize(const void *gate, const void *up, int dtype, int64_t M, int64_t I, int64_t ldg, int64_t ldu,
                     int8_t *x_q, float *s_x, void *stream);

@@ -108,6 +108,55 @@ def test_quantize_strided_and_bf16(w8a8):
     assert (host(xq) == rq).all() and (host(sx).view(np.uint32) == rs.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("K", [256, 2560, 4096])
+def test_quantize_ties_and_magnitudes_each_row_kernel(w8a8, K):
+    """Exact ties (row maximum 127 * 2^j, so s = 2^j and half-integer multiples of s are
+    ties) and a spread of every magnitude below sampled maxima, for fp16 and bf16, at row
+    lengths taken by the wave-per-row (K=256), wave-pair (K=2560) and workgroup-per-row
+    (K=4096) kernels: codes and scales bit-exact against the oracle."""
+    note(f"quantize ties + magnitudes K={K}")
+    rng = np.random.default_rng(K)
+    rows = []
+    for j in (-20, -3, 0, 5, 9):
+        r = rng.integers(-254, 255, K) / 2.0  # half-integers: ties at s = 1
+        r[0] = 127.0
+        rows.append(np.ldexp(r, j))
+    x16 = np.stack(rows).astype(np.float16)
+    assert (np.abs(x16.astype(np.float64)).max(axis=1) == np.ldexp(127.0, np.array([-20, -3, 0, 5, 9]))).all()
+    # fp16: sampled maxima, each row a spread of the magnitudes up to the maximum, both signs
+    maxima = np.concatenate([[0x7BFF, 0x3C00, 0x0400, 0x03FF], rng.integers(1, 0x7C00, 12)]).astype(np.uint16)
+    spread = np.zeros((len(maxima), K), np.uint16)
+    for i, mb in enumerate(maxima):
+        mags = np.sort(rng.integers(0, int(mb) + 1, K // 2).astype(np.uint16))
+        mags[-1] = mb
+        v = np.concatenate([mags, mags | 0x8000])
+        spread[i] = rng.permutation(v)
+    x = np.concatenate([x16, spread.view(np.float16)])
+    xq, sx = gpu_quantize(w8a8, x)
+    rq, rs = oracle.quantize_per_token(x)
+    assert (sx.view(np.uint32) == rs.view(np.uint32)).all()
+    assert (xq == rq).all()
+    # bf16: the same tie rows (exact in bf16) and spreads of bf16 magnitudes down to 2^-100
+    # (the fast path's lower limit) and below it
+    b16 = x16.astype(np.float32).view(np.uint32) >> 16
+    assert ((b16.astype(np.uint32) << 16).view(np.float32) == x16.astype(np.float32)).all()
+    # 0x10FE = 127 * 2^-100 (s = 2^-100, the fast path's smallest scale), 0x10FD just below
+    bmax = np.concatenate([[0x7F7F, 0x3F80, 0x10FF, 0x10FE, 0x10FD, 0x0D80, 0x0080],
+                           rng.integers(0x0100, 0x7F80, 9)]).astype(np.uint16)
+    bspread = np.zeros((len(bmax), K), np.uint16)
+    for i, mb in enumerate(bmax):
+        mags = np.sort(rng.integers(0, int(mb) + 1, K // 2).astype(np.uint16))
+        mags[-1] = mb
+        bspread[i] = rng.permutation(np.concatenate([mags, mags | 0x8000]))
+    bits = np.concatenate([b16.astype(np.uint16), bspread])
+    xb = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    xq, sx = w8a8.quantize_per_token(xb.cuda())
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_per_token_bf16(bits)
+    assert (host(sx).view(np.uint32) == rs.view(np.uint32)).all()
+    assert (host(xq) == rq).all()
+
+
 def test_quantize_empty_batch(w8a8):
     xq, sx = w8a8.quantize_per_token(torch.zeros((0, 256), dtype=torch.float16, device="cuda"))
     torch.cuda.synchronize()

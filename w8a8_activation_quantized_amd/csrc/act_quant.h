@@ -54,6 +54,11 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // rounded half-to-even by adding 1.5 * 2^23: in that binade the fp32 spacing is 1, so the
 // addition itself rounds to the nearest integer (ties to even) and the code is the low
 // byte of the sum's bit pattern.
+//
+// On the fast path (finite input, s >= 2^-100) the clamp is never active and is left out:
+// s = RN(max|x| / 127) is a normal number within 2^-24 relative of max|x| / 127, so
+// |x / s| <= 127 (1 + 2^-24) / (1 - 2^-24) < 127.5 and every code already lies in
+// [-127, 127].
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 constexpr float kMinFastScale = 0x1p-100f;
@@ -79,18 +84,69 @@ __device__ __forceinline__ float quotient(float x, float s, float r) {
     return x / s;
 }
 
+// A value the compiler cannot see through (so fma(x, r, -0) is not folded into a multiply).
+__device__ __forceinline__ float opaque_f32(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// acc byte B = low byte of the bits of q + magic (the rounded code), the other bytes kept
+// (B = 0: cleared). One SDWA add per code: the rounding add also places the byte.
+template <int B>
+__device__ __forceinline__ void put_code(uint32_t &acc, float q, float magic) {
+    static_assert(B >= 0 && B < 4, "byte index");
+    if constexpr (B == 0)
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+            : "=v"(acc) : "v"(q), "v"(magic));
+    else if constexpr (B == 1)
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+            : "+v"(acc) : "v"(q), "v"(magic));
+    else if constexpr (B == 2)
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+            : "+v"(acc) : "v"(q), "v"(magic));
+    else
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+            : "+v"(acc) : "v"(q), "v"(magic));
+}
+
 // Eight elements (one 16-byte chunk) -> eight codes (8 bytes).
+// FAST (s >= 2^-100, finite input): the corrected quotient with no clamp (see above); for
+// fp16 the product x r is written fma(x, r, -0) (the same value, -0 being the additive
+// identity) so that both products read the half directly (v_fma_mix, no conversion).
+// Otherwise: IEEE division and the clamp.
 template <bool BF16, bool FAST>
 __device__ __forceinline__ uint2 quant8(uint4 c, float s, float r) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     uint32_t out[2];
+    if constexpr (FAST) {
+        const float nz = opaque_f32(-0.0f), magic = opaque_f32(kMagic);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t b0 = code_byte(quotient<FAST>(to_float<BF16>(w[2 * i] & 0xffffu), s, r));
-        const uint32_t b1 = code_byte(quotient<FAST>(to_float<BF16>(w[2 * i] >> 16), s, r));
-        const uint32_t b2 = code_byte(quotient<FAST>(to_float<BF16>(w[2 * i + 1] & 0xffffu), s, r));
-        const uint32_t b3 = code_byte(quotient<FAST>(to_float<BF16>(w[2 * i + 1] >> 16), s, r));
-        out[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        for (int i = 0; i < 2; ++i) {
+            float q[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t word = w[2 * i + (h >> 1)];
+                const float x = to_float<BF16>((h & 1) ? word >> 16 : word & 0xffffu);
+                const float q0 = BF16 ? x * r : __builtin_fmaf(x, r, nz);
+                const float e = __builtin_fmaf(-q0, s, x);
+                q[h] = __builtin_fmaf(e, r, q0);
+            }
+            uint32_t acc;
+            put_code<0>(acc, q[0], magic);
+            put_code<1>(acc, q[1], magic);
+            put_code<2>(acc, q[2], magic);
+            put_code<3>(acc, q[3], magic);
+            out[i] = acc;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t b0 = code_byte(quotient<false>(to_float<BF16>(w[2 * i] & 0xffffu), s, r));
+            const uint32_t b1 = code_byte(quotient<false>(to_float<BF16>(w[2 * i] >> 16), s, r));
+            const uint32_t b2 = code_byte(quotient<false>(to_float<BF16>(w[2 * i + 1] & 0xffffu), s, r));
+            const uint32_t b3 = code_byte(quotient<false>(to_float<BF16>(w[2 * i + 1] >> 16), s, r));
+            out[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
     }
     return make_uint2(out[0], out[1]);
 }

@@ -99,6 +99,19 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *__re
     }
 }
 
+// Codes of one row from the workgroup's threads (thread t: chunks t + NT j).
+template <bool BF16, bool FAST, int CPT, int NT>
+__device__ __forceinline__ void wg_row_store(const uint4 (&cache)[CPT], const uint16_t *row, int8_t *qrow, int tid,
+                                             int nch, float s, float r) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + NT * j;
+        if (c < nch) *reinterpret_cast<uint2 *>(qrow + 8 * c) = quant8<BF16, FAST>(cache[j], s, r);
+    }
+    for (int c = tid + NT * CPT; c < nch; c += NT)
+        *reinterpret_cast<uint2 *>(qrow + 8 * c) = quant8<BF16, FAST>(*reinterpret_cast<const uint4 *>(row + 8 * c), s, r);
+}
+
 // Long rows: a row per 256-thread workgroup (thread t takes the chunks t + 256 j, up to CPT
 // of them held in registers), the four waves' maxima combined through LDS; the same codes.
 template <int CPT, bool BF16, int NT>
@@ -132,18 +145,10 @@ __global__ __launch_bounds__(NT) void quantize_rows_wg_kernel(const uint16_t *__
         for (int c = tid; c < nch; c += NT) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
         return;
     }
-    const bool fast = s >= kMinFastScale;
-    const float r = fast ? 1.0f / s : 0.f;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = tid + NT * j;
-        if (c < nch)
-            *reinterpret_cast<uint2 *>(qrow + 8 * c) = fast ? quant8<BF16, true>(cache[j], s, r) : quant8<BF16, false>(cache[j], s, r);
-    }
-    for (int c = tid + NT * CPT; c < nch; c += NT) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(row + 8 * c);
-        *reinterpret_cast<uint2 *>(qrow + 8 * c) = fast ? quant8<BF16, true>(v, s, r) : quant8<BF16, false>(v, s, r);
-    }
+    if (s >= kMinFastScale)
+        wg_row_store<BF16, true, CPT, NT>(cache, row, qrow, tid, nch, s, 1.0f / s);
+    else
+        wg_row_store<BF16, false, CPT, NT>(cache, row, qrow, tid, nch, s, 0.f);
 }
 
 template <bool BF16>
@@ -230,13 +235,33 @@ __device__ __forceinline__ void norm_stats8(const float (&u)[8], const float (&x
     }
 }
 
+// FAST: finite s >= 2^-100 (|u| <= max|u| then keeps every quotient inside (-127.5, 127.5),
+// so no clamp), codes placed by the rounding adds; otherwise IEEE division and the clamp.
 template <bool FAST>
 __device__ __forceinline__ uint2 norm_quant8(const float (&u)[8], float s, float r) {
     uint32_t out[2] = {0, 0};
+    if constexpr (FAST) {
+        const float magic = opaque_f32(kMagic);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e >> 2] |= code_byte(quotient<FAST>(u[e], s, r)) << (8 * (e & 3));
+        for (int i = 0; i < 2; ++i) {
+            float q[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) q[h] = quotient<true>(u[4 * i + h], s, r);
+            put_code<0>(out[i], q[0], magic);
+            put_code<1>(out[i], q[1], magic);
+            put_code<2>(out[i], q[2], magic);
+            put_code<3>(out[i], q[3], magic);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e >> 2] |= code_byte(quotient<false>(u[e], s, r)) << (8 * (e & 3));
+    }
     return make_uint2(out[0], out[1]);
 }
+
+// The fast path needs a finite scale: u = x g (or silu(gate) up) of finite bf16 inputs can
+// overflow fp32, and an infinite row maximum gives s = inf.
+__device__ __forceinline__ bool fast_scale(float s) { return s >= kMinFastScale && s <= 0x1.fffffep127f; }
 
 // A row per 256-thread workgroup: thread t takes the 16-byte chunks t + 256 j, holds u = x g
 // of the first CPT of them in registers between the two passes and recomputes the rest;
@@ -317,7 +342,7 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
         for (int c = tid; c < nch; c += NORM_THREADS) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
         return;
     }
-    if (s >= kMinFastScale)
+    if (fast_scale(s))
         norm_row_store<XBF, GBF, true, CPT>(uc, row, g, qrow, tid, nch, s, 1.0f / s);
     else
         norm_row_store<XBF, GBF, false, CPT>(uc, row, g, qrow, tid, nch, s, 0.f);
@@ -451,7 +476,7 @@ __global__ __launch_bounds__(NORM_THREADS) void swiglu_quantize_kernel(const uin
         for (int c = tid; c < nch; c += NORM_THREADS) *reinterpret_cast<uint2 *>(qrow + 8 * c) = make_uint2(0, 0);
         return;
     }
-    if (s >= kMinFastScale)
+    if (fast_scale(s))
         swiglu_row_store<BF16, true, CPT>(hc, grow, urow, qrow, tid, nch, s, 1.0f / s);
     else
         swiglu_row_store<BF16, false, CPT>(hc, grow, urow, qrow, tid, nch, s, 0.f);
