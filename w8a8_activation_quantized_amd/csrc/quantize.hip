@@ -206,16 +206,19 @@ hipError_t launch_rows(const void *x, int64_t ldx, int M, int K, int8_t *xq, flo
 // the sign of a zero quotient, which makes no difference to the code).
 
 // u = x g for the eight values of one 16-byte chunk of x and of g (element e = 2 i + h of
-// dword i), one fp32 multiply each.
+// dword i), one fp32 product each, written fma(x, g, -0) (the same value: the product of two
+// halves or two bf16 values is exact in fp32, and -0 is the additive identity, also for the
+// sign of a zero) so that halves are read directly by v_fma_mix, with no conversion.
 template <bool XBF, bool GBF>
 __device__ __forceinline__ void norm_u8(uint4 xc, uint4 gc, float (&u)[8], float (&xv)[8]) {
     const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w}, gw[4] = {gc.x, gc.y, gc.z, gc.w};
+    const float nz = opaque_f32(-0.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             xv[2 * i + h] = to_float<XBF>(h ? xw[i] >> 16 : xw[i] & 0xffffu);
-            u[2 * i + h] = xv[2 * i + h] * to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu);
+            u[2 * i + h] = __builtin_fmaf(xv[2 * i + h], to_float<GBF>(h ? gw[i] >> 16 : gw[i] & 0xffffu), nz);
         }
 }
 
@@ -223,11 +226,10 @@ __device__ __forceinline__ void norm_u8(uint4 xc, uint4 gc, float (&u)[8], float
 // 2^-48 .. 2^32); fp64 for bf16 rows, whose squares leave the fp32 range for |x| > 2^64 or
 // |x| < 2^-75 (inf or 0 sums, so an infinite or zero scale beside nonzero codes).
 template <typename SS>
-__device__ __forceinline__ void norm_stats8(const float (&u)[8], const float (&xv)[8], uint32_t &amax, SS &ss) {
+__device__ __forceinline__ void norm_stats8(const float (&u)[8], const float (&xv)[8], float &amax, SS &ss) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t ub = __builtin_bit_cast(uint32_t, u[e]) & 0x7fffffffu;
-        amax = amax > ub ? amax : ub;
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(u[e]));  // |u| as a source modifier
         if constexpr (std::is_same<SS, double>::value)
             ss = __builtin_fma((double)xv[e], (double)xv[e], ss);
         else
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
     const int nch = K >> 3;
 
     float uc[CPT][8];
-    uint32_t amax = 0;
+    float amaxf = 0.0f;  // max |u| (u finite: the same value as a max over magnitude bit patterns)
     SS ss = 0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
@@ -307,15 +309,15 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(const ui
         if (c < nch) {
             norm_u8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c),
                               uc[j], xv);
-            norm_stats8(uc[j], xv, amax, ss);
+            norm_stats8(uc[j], xv, amaxf, ss);
         }
     }
     for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS) {
         float u[8], xv[8];
         norm_u8<XBF, GBF>(*reinterpret_cast<const uint4 *>(row + 8 * c), *reinterpret_cast<const uint4 *>(g + 8 * c), u, xv);
-        norm_stats8(u, xv, amax, ss);
+        norm_stats8(u, xv, amaxf, ss);
     }
-    amax = wave_max_u32(amax);
+    uint32_t amax = wave_max_u32(__builtin_bit_cast(uint32_t, amaxf));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     if (lane == 0) {
@@ -375,7 +377,7 @@ hipError_t launch_norm_rows(const void *x, int64_t ldx, const void *g, float eps
 // the same steps: the argument clamped to [-87, 88]; Cody-Waite reduction x = k ln 2 + r,
 // k = rint(x log2 e), r by two fmas against ln 2 split into its fp32 rounding and the
 // rounding of the remainder; e^r by the degree-7 Taylor polynomial (1 / n! in fp32), Horner
-// with fmas; times 2^k built from its exponent bits. Division g / (1 + e) is IEEE; the
+// with fmas; times 2^k (one rounding). Division g / (1 + e) is IEEE; the
 // quotient h / s of the codes is the corrected reciprocal of the quantize kernel.
 
 __device__ __forceinline__ float exp_fixed(float x) {
@@ -391,13 +393,16 @@ __device__ __forceinline__ float exp_fixed(float x) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    return p * __builtin_bit_cast(float, (uint32_t)((int)k + 127) << 23);  // k in [-126, 127]
+    // p 2^k (k in [-126, 127]) by v_ldexp: the same value as p times the fp32 power 2^k (one
+    // rounding either way, subnormal results included; equal for every fp16 and bf16 gate value)
+    return __builtin_amdgcn_ldexpf(p, (int)k);
 }
 
 // h = silu(g) * u for the eight values of one 16-byte chunk of gate and of up.
 template <bool BF16>
 __device__ __forceinline__ void swiglu_h8(uint4 gc, uint4 uc, float (&h)[8]) {
     const uint32_t gw[4] = {gc.x, gc.y, gc.z, gc.w}, uw[4] = {uc.x, uc.y, uc.z, uc.w};
+    const float nz = opaque_f32(-0.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -405,7 +410,7 @@ __device__ __forceinline__ void swiglu_h8(uint4 gc, uint4 uc, float (&h)[8]) {
             const float g = to_float<BF16>(e ? gw[i] >> 16 : gw[i] & 0xffffu);
             const float u = to_float<BF16>(e ? uw[i] >> 16 : uw[i] & 0xffffu);
             const float silu = g / (1.0f + exp_fixed(-g));
-            h[2 * i + e] = silu * u;
+            h[2 * i + e] = __builtin_fmaf(silu, u, nz);  // silu * u; -0 keeps an fp16 u unconverted (v_fma_mix)
         }
 }
 
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(NORM_THREADS) void swiglu_quantize_kernel(const uin
     const int nch = I >> 3;
 
     float hc[CPT][8];
-    uint32_t amax = 0;
+    float amaxf = 0.0f;  // max |h| (h is never NaN: the same value as a max over magnitude bit patterns)
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + NORM_THREADS * j;
@@ -448,22 +453,16 @@ __global__ __launch_bounds__(NORM_THREADS) void swiglu_quantize_kernel(const uin
             swiglu_h8<BF16>(*reinterpret_cast<const uint4 *>(grow + 8 * c), *reinterpret_cast<const uint4 *>(urow + 8 * c),
                             hc[j]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t hb = __builtin_bit_cast(uint32_t, hc[j][e]) & 0x7fffffffu;
-                amax = amax > hb ? amax : hb;
-            }
+            for (int e = 0; e < 8; ++e) amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(hc[j][e]));
         }
     }
     for (int c = tid + NORM_THREADS * CPT; c < nch; c += NORM_THREADS) {
         float h[8];
         swiglu_h8<BF16>(*reinterpret_cast<const uint4 *>(grow + 8 * c), *reinterpret_cast<const uint4 *>(urow + 8 * c), h);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t hb = __builtin_bit_cast(uint32_t, h[e]) & 0x7fffffffu;
-            amax = amax > hb ? amax : hb;
-        }
+        for (int e = 0; e < 8; ++e) amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(h[e]));
     }
-    amax = wave_max_u32(amax);
+    uint32_t amax = wave_max_u32(__builtin_bit_cast(uint32_t, amaxf));
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
     amax = wmax[0];
