@@ -27,13 +27,25 @@ __device__ __forceinline__ float to_float(uint32_t bits) {
     return BF16 ? bf16_bits_to_float(bits) : half_bits_to_float(bits);
 }
 
+// max(v, v of the lane that the DPP pattern CTRL selects), in the rows that ROWS enables
+// (other rows keep v).
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xf, false);
+    return v > o ? v : o;
+}
+
+// Maximum over the 64 lanes of a wave (all lanes active), returned to every lane. DPP moves
+// within and across 16-lane rows and one lane read, instead of six LDS-crossbar permutes
+// (__shfl_xor): a few cycles per step on the critical path of a row's quantization.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-        v = v > o ? v : o;
-    }
-    return v;
+    v = max_dpp<0xb1>(v);        // quad_perm [1, 0, 3, 2]
+    v = max_dpp<0x4e>(v);        // quad_perm [2, 3, 0, 1]: max of each quad
+    v = max_dpp<0x141>(v);       // row_half_mirror: max of each half-row
+    v = max_dpp<0x140>(v);       // row_mirror: max of each row
+    v = max_dpp<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3: rows (0, 1) and (2, 3)
+    v = max_dpp<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3: row 3 holds all four
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
