@@ -37,6 +37,24 @@ typedef float sd_v4f __attribute__((ext_vector_type(4)));
 constexpr int SD_WAVES = 4;  // waves per workgroup
 constexpr int SD_BK = 32;    // keys per block (two MFMA row tiles)
 
+// v combined with the value of lane l ^ 16 (xor16) or l ^ 32 (xor32) by a commutative op:
+// v_permlane16_swap / v_permlane32_swap on two copies of v leave each lane holding its own
+// value and its partner's (swap16: rows (0, 1) and (2, 3) exchanged; swap32: the halves), a
+// VALU lane exchange instead of an LDS-crossbar shuffle. Commutativity makes the result
+// the same bits as op(v, partner) in every lane.
+template <typename Op>
+__device__ __forceinline__ float xor16_combine(float v, Op op) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto sw = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return op(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32_combine(float v, Op op) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto sw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return op(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+
 // v_mfma_f32_16x16x32 on 8 values of the input format per lane (both products use it)
 template <bool BF16>
 __device__ __forceinline__ sd_v4f mma16x16x32(v4u a, v4u b, sd_v4f c) {
@@ -158,8 +176,8 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
                 s[4 * tile + e] = x;
                 bm = fmaxf(bm, x);
             }
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = xor16_combine(bm, [](float u, float v) { return fmaxf(u, v); });
+        bm = xor32_combine(bm, [](float u, float v) { return fmaxf(u, v); });
         const float mn = fmaxf(m, bm);  // finite: every block has a key below w1
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         float ps = 0.f;
@@ -168,8 +186,8 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
             s[i] = __builtin_amdgcn_exp2f(s[i] - mn + 12.0f);  // 2^12 p
             ps += s[i];
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = xor16_combine(ps, [](float u, float v) { return u + v; });
+        ps = xor32_combine(ps, [](float u, float v) { return u + v; });
         l = l * alpha + ps;
         m = mn;
         // P parts to LDS, [part][head][key]: this lane's 4 consecutive keys of each tile
