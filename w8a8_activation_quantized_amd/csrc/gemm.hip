@@ -805,6 +805,87 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Source of DMA piece `piece` of stage `stage` (int8 weights and tokens, 128-byte stage
+// rows): a 32-bit offset from the weight or token base, whichever the piece covers (both
+// uniform), so no 64-bit address per piece stays live through the MFMAs.
+template <class S>
+__device__ __forceinline__ const int8_t *pp_piece_src(const int8_t *wb, const int8_t *xb, const uint32_t (&off)[S::PPW],
+                                                      int piece, int stage, int wave) {
+    const bool is_w = min(wave + piece * S::NW, S::PIECES - 1) < S::W_PIECES;
+    return (is_w ? wb : xb) + (off[piece] + (uint32_t)stage * S::BKS);
+}
+
+// DMA pieces [LO, HI) of this wave for stage `stage` (buffer stage & 1).
+template <class S, int LO, int HI>
+__device__ __forceinline__ void pp_issue_range(const int8_t *wb, const int8_t *xb, const uint32_t (&off)[S::PPW],
+                                               int8_t *smem, int stage, int wave, bool full) {
+    int8_t *dst = smem + (stage & 1) * S::STAGE + wave * 1024;
+#pragma unroll
+    for (int piece = LO; piece < HI; ++piece)
+        if (piece < S::PPW - 1 || full) dma_16B(pp_piece_src<S>(wb, xb, off, piece, stage, wave), dst + piece * S::NW * 1024);
+}
+
+// The K loop with two stages of 128-value K-tiles and each stage's DMA split between two
+// memory phases of each group (pp_loop2 issues a wave's nine pieces of stage s + 1 in one
+// memory phase, K-step 2 s, which then runs well past the other group's MFMAs while the
+// memory phases of K-steps 2 s + 1 issue none). Stage s + 1 goes to the buffer of stage
+// s - 1:
+//   group 0: pieces [0, A) in its memory phase of K-step 2 s, [A, PPW) in that of 2 s + 1,
+//            and it waits for them after its MFMAs of K-step 2 s + 1;
+//   group 1 (one phase behind): pieces [0, B) in its memory phase of K-step 2 s - 1, right
+//            after its own fragment reads of stage s - 1 have retired (group 0 read that
+//            stage last in the phase before, so the buffer is free), [B, PPW) in its
+//            memory phase of 2 s; it waits for them in its memory phase of 2 s + 1.
+// Both waits precede the barrier in front of group 0's first read of stage s + 1 (its
+// memory phase of K-step 2 s + 2). Group 1's pieces [0, B) of stage 1 go out in the phase
+// by which it starts behind group 0.
+template <class S, int Q, int A, int B>
+__device__ __forceinline__ void pp_loop3(v4i (&acc)[S::FN][S::FM], const int8_t *wb, const int8_t *xb,
+                                         const uint32_t (&off)[S::PPW], int8_t *smem, int KT, int grp, int wave,
+                                         bool full, int frow, int fchunk) {
+    static_assert(S::WK == W_INT8 && S::BKS == 128, "int8 weights, 128-value stages");
+    constexpr int FN = S::FN, FM = S::FM, PPW = S::PPW;
+    static_assert(0 < A && A <= PPW && 0 < B && B < PPW, "piece split");
+    const int NS = KT >> 1;
+    v4i a[FN], b[FM];
+    for (int j = 0; j < KT; ++j) {
+        const int stg = j >> 1, h = j & 1;
+        const int8_t *st = smem + (stg & 1) * S::STAGE;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            a[fn] = *reinterpret_cast<const v4i *>(st + swz<128>(Q * S::WN + fn * 16 + frow, 4 * h + fchunk));
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            b[fm] = *reinterpret_cast<const v4i *>(st + S::W_TILE + swz<128>(grp * S::WM + fm * 16 + frow, 4 * h + fchunk));
+        const bool next = stg + 1 < NS;
+        if (grp == 0) {
+            if (next) {
+                if (h == 0) pp_issue_range<S, 0, A>(wb, xb, off, smem, stg + 1, wave, full);
+                else if constexpr (A < PPW) pp_issue_range<S, A, PPW>(wb, xb, off, smem, stg + 1, wave, full);
+            }
+            wait_lgkmcnt0();
+        } else if (h == 0) {
+            if (next) pp_issue_range<S, B, PPW>(wb, xb, off, smem, stg + 1, wave, full);
+            wait_lgkmcnt0();
+        } else {
+            wait_lgkmcnt0();  // this wave's reads of stage s retired: the buffer is free
+            if (stg + 2 < NS) {
+                pp_issue_range<S, 0, B>(wb, xb, off, smem, stg + 2, wave, full);
+                if (next) wait_vmcnt<B>();  // its pieces of stage s + 1 landed (the B just issued may fly)
+            } else if (next) {
+                wait_vmcnt<0>();
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+        if (grp == 0 && h == 1 && next) wait_vmcnt<0>();  // group 0's pieces of stage s + 1 landed
+        lds_barrier();
+    }
+}
+
 // Two outputs rounded to fp16 (or bf16) in one conversion, RNE, packed low-first. The fp32
 // inputs are pinned in registers so that the compiler cannot merge the preceding multiply
 // into a mixed-precision fma (one rounding of the exact product).
@@ -874,7 +955,9 @@ __device__ __forceinline__ void pp_store_staged(const v4i (&acc)[S::FN][S::FM], 
     static_for<0, ITS>([&](auto it) { store(1, decltype(it)::value); });
 }
 
-template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8>
+// SPREAD = 16 A + B selects pp_loop3 with that split of each stage's DMA pieces (int8
+// weights, 128-value stages); 0 selects pp_loop2 (or pp_loop for 64-value stages).
+template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8, int SPREAD = 0>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tmap) {
     using S = PpShape<BN, BM, STAGES, BKS, WK>;
     constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW;
@@ -915,6 +998,18 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
         }
     }
 
+    // the spread-DMA loop takes the same sources as 32-bit offsets from the two bases (the
+    // launcher checks that both operands span less than 4 GiB)
+    const int8_t *const wb = static_cast<const int8_t *>(p.wq), *const xb = p.xq;
+    uint32_t off[PPW];
+    if constexpr (SPREAD > 0) {
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+            const bool is_w = min(wave + j * S::NW, S::PIECES - 1) < S::W_PIECES;
+            off[j] = (uint32_t)(src[j] - (is_w ? wb : xb));
+        }
+    }
+
     v4i acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -939,7 +1034,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
         wait_vmcnt<0>();
     }
     lds_barrier();
-    if (grp == 1) lds_barrier();  // group 1 runs one phase behind group 0
+    if (grp == 1) {
+        // group 1 runs one phase behind group 0; with the spread DMA it issues its first
+        // third of stage 1 in that phase
+        if constexpr (SPREAD > 0)
+            if (KT >= 4) pp_issue_range<S, 0, SPREAD % 16>(wb, xb, off, smem, 1, wave, full);
+        lds_barrier();
+    }
 
     if constexpr (S::BKS == 64) {
         switch (wq) {
@@ -947,6 +1048,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
             case 1: pp_loop<S, 1>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
             case 2: pp_loop<S, 2>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
             default: pp_loop<S, 3>(acc, src, smem, KT, grp, wave, full, frow, fchunk); break;
+        }
+    } else if constexpr (SPREAD > 0) {
+        switch (wq) {
+            case 0: pp_loop3<S, 0, SPREAD / 16, SPREAD % 16>(acc, wb, xb, off, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 1: pp_loop3<S, 1, SPREAD / 16, SPREAD % 16>(acc, wb, xb, off, smem, KT, grp, wave, full, frow, fchunk); break;
+            case 2: pp_loop3<S, 2, SPREAD / 16, SPREAD % 16>(acc, wb, xb, off, smem, KT, grp, wave, full, frow, fchunk); break;
+            default: pp_loop3<S, 3, SPREAD / 16, SPREAD % 16>(acc, wb, xb, off, smem, KT, grp, wave, full, frow, fchunk); break;
         }
     } else {
         switch (wq) {
@@ -2203,6 +2311,21 @@ hipError_t launch_gemv_dma_x(const GemmProblem &p, hipStream_t stream) {
     int seg = (NCH + NW - 1) / NW;
     seg = (seg + unit - 1) / unit * unit;
     NW = (NCH + seg - 1) / seg;
+    // With x_q given, segments of equal length where a few more waves allow it: the int4
+    // rows of K = 2560 (10 chunks) as 5 x 2 instead of 3 + 3 + 3 + 1 chunks (M=1, N=10240:
+    // 6.51 -> 6.13 us per group, 5.71 -> 5.52 us per column). The fused layer keeps the
+    // split above: every extra wave also copies and reduces its part of x (7.77 against
+    // 7.95 us with five waves).
+    if (FQ == 0 && NCH % seg != 0) {
+        for (int nw = NW + 1; nw <= GEMV_MAX_WAVES; ++nw) {
+            const int s = ((NCH + nw - 1) / nw + unit - 1) / unit * unit;
+            if (s >= 2 && NCH % s == 0) {
+                seg = s;
+                NW = NCH / s;
+                break;
+            }
+        }
+    }
     const int table_groups = S::GROUPED ? ((seg * S::SPC + S::SPG - 1) / S::SPG + 1 + 3) & ~3 : 0;
     const size_t xl = XL ? (size_t)((p.M * seg * S::KPC + 1023) & ~1023) : 0;
     const size_t xh = FQ ? (size_t)((2 * p.M * seg * S::KPC + 1023) & ~1023) : 0;
@@ -2353,6 +2476,7 @@ constexpr Config kConfigs[] = {
     {256, 320, 8},  // 16: as 13 with two stages of 128-value K-tiles (128-byte DMA row segments)
     {256, 320, 8},  // 17: as 16 with int4 weights (per-channel scales or raw int32 sums); int8: 16
     {256, 256, 8},  // 18: as 16 with 256 x 256 tiles (64 x 128 per wave)
+    {256, 320, 8},  // 19: as 16 with each wave's DMA of a stage split over two memory phases
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2398,14 +2522,14 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 
-template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8>
+template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8, int SPREAD = 0>
 hipError_t launch_pp(const GemmProblem &p, int group_m, hipStream_t stream) {
     TileMap t;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.group_m = group_m;
     dim3 grid(t.tiles_m * t.tiles_n), block(512);
-    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS, WK>), grid, block, 0, stream, p, t);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS, WK, SPREAD>), grid, block, 0, stream, p, t);
     return hipGetLastError();
 }
 
@@ -2528,7 +2652,10 @@ int choose_config(const GemmProblem &p) {
     // K = 10240; 177 against 183 us at M = 8192, N = 10240, K = 2560; whole 128-byte row
     // segments per DMA halve the L2 requests, and the chip holds a 6 % higher clock)
     if (c12 < c6 && c12 < c7 && c12 < c13 && c12 < c18) return 12;
-    if (c13 < c6 && c13 < c7 && c13 <= c18) return 16;
+    // (19 is 16 with each stage's DMA split over two memory phases of each group, outputs
+    // identical: M = 4096, N = 10240, K = 2560 82.4 against 83.0 us, M = 8192, N = 2560,
+    // K = 10240 139.6 against 141.2, M = 4096, N = 2560, K = 10240 111.8 against 116.3)
+    if (c13 < c6 && c13 < c7 && c13 <= c18) return 19;
     if (c18 < c6 && c18 < c7) return 18;
     return c6 <= c7 ? 6 : 7;
 }
@@ -2707,6 +2834,11 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 13: return launch_pp<320, 256, 4>(p, gm, stream);
         case 16: return launch_pp<320, 256, 2, 128>(p, gm, stream);
         case 18: return launch_pp<256, 256, 2, 128>(p, gm, stream);
+        case 19:
+            // 32-bit DMA offsets within each operand, else the same tile as 16
+            if ((int64_t)p.N * p.K < ((int64_t)1 << 32) && (int64_t)p.M * p.K < ((int64_t)1 << 32))
+                return launch_pp<320, 256, 2, 128, W_INT8, 5 * 16 + 5>(p, gm, stream);
+            return launch_pp<320, 256, 2, 128>(p, gm, stream);
         case 14: return launch_ms<128, 128, 4, 2, 2>(p, gm, stream);
         case 15: return launch_ms<64, 128, 6, 2, 4>(p, gm, stream);
         case 5: return launch_ms<256, 256, 2, 4, 2>(p, gm, stream);
