@@ -269,7 +269,7 @@ def test_gemm_strided_output_and_empty(w8a8):
     # row strides of 304 (16-byte rows: staged stores) and 276 (8-byte rows: direct
     # stores), both 16-bit types, in the automatic choice and the DMA-pipeline kernels
     try:
-        for cfg in (-1, 6, 7, 13, 16, 17, 18, 19):
+        for cfg in (-1, 6, 7, 13, 16, 17, 18, 19, 20):
             w8a8.w8a8_debug_force_config(cfg)
             for ldy in (304, 276):
                 for out, fmt in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
@@ -293,13 +293,13 @@ def test_gemm_strided_output_and_empty(w8a8):
 @pytest.mark.parametrize("M,N,K,pad", [(4000, 10000, 512, 0), (2100, 12000, 256, 8)])
 def test_pc_several_rounds_of_tiles(w8a8, M, N, K, pad):
     """More output tiles than compute units (several rounds of workgroups) in the ping-pong
-    configurations 16, 18 and 19 with 16-bit outputs staged in LDS: partial tiles in M and N,
+    configurations 16, 18, 19 and 20 with 16-bit outputs staged in LDS: partial tiles in M and N,
     contiguous and strided output rows; bit-exact against the oracle's fp32 evaluation, and
     the padding columns untouched."""
     x, W = linear_inputs(M, N, K, seed=M + N)
     r = oracle_mode("pc", x, W)
     try:
-        for cfg in (-1, 16, 18, 19):
+        for cfg in (-1, 16, 18, 19, 20):
             w8a8.w8a8_debug_force_config(cfg)
             for out, fmt in ((torch.float16, "f16"), (torch.bfloat16, "bf16")):
                 note(f"several rounds: config {cfg} M={M} N={N} K={K} ldy={N + pad} {fmt}")

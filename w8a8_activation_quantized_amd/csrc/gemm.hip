@@ -598,7 +598,8 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
             const int r = c / CPR, cc = c - r * CPR;
             if (r < rows && cc * 8 < cols) {
                 const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
-                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+                // streaming store (see pp_store_staged)
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)));
             }
         }
         return;
@@ -1398,7 +1399,8 @@ __device__ __forceinline__ void mg_pc_epilogue(const GemmProblem &p, v4i (&acc)[
             const int r = c / CPR, cc = c - r * CPR;
             if (r < rows && cc * 8 < cols) {
                 const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
-                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+                // streaming store (see pp_store_staged)
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)));
             }
         }
         return;
@@ -1596,7 +1598,8 @@ __global__ __launch_bounds__(512) void gemm_mg_kernel(GemmProblem p, TileMap tma
             const int r = c / CPR, cc = c - r * CPR;
             if (r < rows && cc * 8 < cols) {
                 const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
-                *reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)) = v;
+                // streaming store (see pp_store_staged)
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)));
             }
         }
         return;
@@ -2481,6 +2484,7 @@ constexpr Config kConfigs[] = {
     {256, 320, 8},  // 17: as 16 with int4 weights (per-channel scales or raw int32 sums); int8: 16
     {256, 256, 8},  // 18: as 16 with 256 x 256 tiles (64 x 128 per wave)
     {256, 320, 8},  // 19: as 16 with each wave's DMA of a stage split over two memory phases
+    {256, 256, 8},  // 20: as 18 with the split DMA of 19
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2660,7 +2664,10 @@ int choose_config(const GemmProblem &p) {
     // identical: M = 4096, N = 10240, K = 2560 82.4 against 83.0 us, M = 8192, N = 2560,
     // K = 10240 139.6 against 141.2, M = 4096, N = 2560, K = 10240 111.8 against 116.3)
     if (c13 < c6 && c13 < c7 && c13 <= c18) return 19;
-    if (c18 < c6 && c18 < c7) return 18;
+    // (20 is 18 with the split DMA of 19, outputs identical: M = 2048, N = 24576, K = 4096
+    // 152.0 against 153.9 us, M = 2048, N = 6144, K = 4096 45.1 against 46.0, M = 1536,
+    // N = 10240, K = 2560 36.6 against 37.4)
+    if (c18 < c6 && c18 < c7) return 20;
     return c6 <= c7 ? 6 : 7;
 }
 
@@ -2838,6 +2845,10 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 13: return launch_pp<320, 256, 4>(p, gm, stream);
         case 16: return launch_pp<320, 256, 2, 128>(p, gm, stream);
         case 18: return launch_pp<256, 256, 2, 128>(p, gm, stream);
+        case 20:
+            if ((int64_t)p.N * p.K < ((int64_t)1 << 32) && (int64_t)p.M * p.K < ((int64_t)1 << 32))
+                return launch_pp<256, 256, 2, 128, W_INT8, 4 * 16 + 4>(p, gm, stream);
+            return launch_pp<256, 256, 2, 128>(p, gm, stream);
         case 19:
             // 32-bit DMA offsets within each operand, else the same tile as 16
             if ((int64_t)p.N * p.K < ((int64_t)1 << 32) && (int64_t)p.M * p.K < ((int64_t)1 << 32))
