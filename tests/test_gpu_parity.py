@@ -312,6 +312,36 @@ def test_pc_several_rounds_of_tiles(w8a8, M, N, K, pad):
         w8a8.w8a8_debug_force_config(-1)
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_pp_split_dma_stage_counts(w8a8, K):
+    """The ping-pong configurations with each stage's DMA split over two memory phases (19,
+    20) and their one-phase forms (16, 18) at one, two, three and five 128-value stages: the
+    first stage issued in the prologue only, group 1's share of stage 1 issued before its
+    late start, the last stage with no DMA after it, an odd stage count; partial tiles in M
+    and N. Bit-exact against the oracle's fp32 evaluation (fp16) and its int32 sums, and
+    identical across the four configurations."""
+    M, N = 300, 704
+    x, W = linear_inputs(M, N, K, seed=K)
+    r = oracle_mode("pc", x, W)
+    outs = {}
+    try:
+        for cfg in (16, 18, 19, 20):
+            w8a8.w8a8_debug_force_config(cfg)
+            for out, fmt in ((torch.float16, "f16"), (torch.int32, "i32")):
+                note(f"split DMA: config {cfg} K={K} {fmt}")
+                y = host(run_mode(w8a8, "pc", x, W, out))
+                if fmt == "f16":
+                    check_exact(y, fmt, r["y32"], f"cfg {cfg} K={K}")
+                else:
+                    assert (y.astype(np.int64) == r["acc"]).all(), f"cfg {cfg} K={K}: int32 sums differ"
+                outs.setdefault(fmt, []).append(y)
+    finally:
+        w8a8.w8a8_debug_force_config(-1)
+    for fmt, ys in outs.items():
+        for y in ys[1:]:
+            assert (y.view(np.uint8) == ys[0].view(np.uint8)).all(), f"configurations differ ({fmt}, K={K})"
+
+
 @pytest.mark.parametrize("mode", ["pc", "pg64", "w4_128", "w4_0"])
 def test_every_config_identical(w8a8, mode):
     """Every tile configuration gives bit-identical results (catches edge-mask and LDS races)."""
