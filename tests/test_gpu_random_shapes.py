@@ -1,4 +1,6 @@
-"""Parity at seeded random shapes: every weight format and output type against the oracle,
+"""Parity at seeded random shapes: every weight format and output type against the oracle
+(160 cases), the split-K call at random forced configurations and slice counts (40), and
+decode attention at random head counts, cache lengths and formats (40),
 on shapes that no fixed test picks (ragged M, N and K, small M that runs the GEMV, the tile
 configurations the automatic choice reaches at those shapes).
 
@@ -72,3 +74,90 @@ def test_random_shape(w8a8, i):
     oq, osx = oracle.quantize_per_token(x)
     assert (tp.host(xq) == oq).all() and (tp.host(sx).view(np.uint32) == osx.view(np.uint32)).all(), what
     check_output(tp.host(y), tp.OUT_FMT[out], r["y"], r["mag"], r["G"], "linear " + what)
+
+
+# ---- split-K at random shapes, configurations and slice counts ------------------------
+
+def draw_split_cases(n, seed=2027):
+    import test_gpu_splitk as tk
+    rng = np.random.default_rng(seed)
+    modes = list(tk.KIND)
+    cases = []
+    for _ in range(n):
+        mode = modes[rng.integers(len(modes))]
+        cfgs = tk.SPLIT_CFGS[mode]
+        cfg = int(cfgs[rng.integers(len(cfgs))])
+        M = int(rng.integers(17, 401))
+        N = 16 * int(rng.integers(1, 101))
+        K = 128 * int(rng.integers(2, 81))
+        slices = int(rng.integers(2, min(32, K // 128) + 1))
+        out = OUTS[rng.integers(len(OUTS))]
+        cases.append((mode, cfg, M, N, K, slices, out))
+    return cases
+
+
+SPLIT_CASES = draw_split_cases(40)
+
+
+@pytest.mark.parametrize("i", range(len(SPLIT_CASES)))
+def test_random_splitk(w8a8, i):
+    """The split-K call with a forced tile configuration and slice count: within the fp32
+    bound of the oracle; per-channel (and int32) results identical to the single pass."""
+    import test_gpu_splitk as tk
+    mode, cfg, M, N, K, slices, out = SPLIT_CASES[i]
+    what = f"split case {i}: {mode} cfg {cfg} M={M} N={N} K={K} slices {slices} {out}"
+    tp.note(what)
+    prob = tk.Problem(w8a8, mode, M, N, K, seed=3000 + i)
+    ref = tk.host(prob.single(w8a8, out))
+    try:
+        tk.forced(w8a8, cfg, slices)
+        if not tk.has_split(mode, cfg, out):
+            assert prob.workspace_bytes(w8a8, out) == 0
+            return
+        assert prob.workspace_bytes(w8a8, out) == slices * M * N * 4
+        yt = prob.split(w8a8, out)
+    finally:
+        tk.reset(w8a8)
+    prob.check(yt, what)
+    if mode == "pc" or out == torch.int32:
+        assert (tk.host(yt).view(np.uint8) == ref.view(np.uint8)).all(), f"{what}: differs from the single pass"
+
+
+# ---- decode attention at random head counts, cache lengths and formats -----------------
+
+def draw_sdpa_cases(n, seed=2028):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        N = int(rng.integers(1, 9001))
+        Ncap = N + int(rng.integers(0, 64))
+        D = int(rng.choice([64, 128]))
+        bf16 = bool(rng.integers(2))
+        out = [torch.float16, torch.bfloat16, torch.float32][rng.integers(3)]
+        cases.append((B, Hkv * G, Hkv, N, Ncap, D, bf16, out))
+    return cases
+
+
+SDPA_CASES = draw_sdpa_cases(40)
+
+
+@pytest.mark.parametrize("i", range(len(SDPA_CASES)))
+def test_random_sdpa(w8a8, i):
+    """sdpa_decode against the oracle within the fp32 evaluation bound of the attention
+    tests, with and without a workspace."""
+    import test_gpu_sdpa as ts
+    B, Hq, Hkv, N, Ncap, D, bf16, out = SDPA_CASES[i]
+    q, k, v = ts.inputs(B, Hq, Hkv, N, Ncap, D, seed=5000 + i)
+    r = oracle.sdpa_decode(*((ts.to_bf16_bits(a) for a in (q, k, v)) if bf16 else (q, k, v)), N=N, bf16=bf16)
+    qd, kd, vd = ts.dev(q, bf16), ts.dev(k, bf16), ts.dev(v, bf16)
+    ws_n = w8a8.sdpa_decode_workspace(B, Hq, Hkv, N, D)
+    ws = torch.full((max(ws_n, 16) // 4,), 777, dtype=torch.int32, device="cuda")
+    for w in ((ws, None) if ws_n > 0 else (None,)):
+        what = f"sdpa case {i}: B={B} Hq={Hq} Hkv={Hkv} N={N} Ncap={Ncap} D={D} bf16={bf16} {out} ws={w is not None}"
+        tp.note(what)
+        o = w8a8.sdpa_decode(qd, kd, vd, N=N, out_dtype=out, workspace=w)
+        torch.cuda.synchronize()
+        ts.check(o, r, N, D, what)
