@@ -1,6 +1,8 @@
 """Parity at seeded random shapes: every weight format and output type against the oracle
-(160 cases), the split-K call at random forced configurations and slice counts (40), and
-decode attention at random head counts, cache lengths and formats (40),
+(160 cases), the split-K call at random forced configurations and slice counts (40),
+decode attention at random head counts, cache lengths and formats (40), and the decode
+matrix-vector product, the RMSNorm and SwiGLU producers and the clipped weight quantizer
+(24 each),
 on shapes that no fixed test picks (ragged M, N and K, small M that runs the GEMV, the tile
 configurations the automatic choice reaches at those shapes).
 
@@ -161,3 +163,75 @@ def test_random_sdpa(w8a8, i):
         o = w8a8.sdpa_decode(qd, kd, vd, N=N, out_dtype=out, workspace=w)
         torch.cuda.synchronize()
         ts.check(o, r, N, D, what)
+
+
+# ---- the other entry points at random shapes -------------------------------------------
+
+def _rng_cases(seed, n, draw):
+    rng = np.random.default_rng(seed)
+    return [draw(rng) for _ in range(n)]
+
+
+MV_CASES = _rng_cases(2029, 24, lambda r: (int(r.integers(1, 17)), 16 * int(r.integers(1, 201)),
+                                           128 * int(r.integers(1, 49)), int(r.choice([0, 64, 128])),
+                                           bool(r.integers(2)), int(r.integers(3))))
+
+
+@pytest.mark.parametrize("i", range(len(MV_CASES)))
+def test_random_int8_mv(w8a8, i):
+    """The decode path (no activation quantization) within the fp32 evaluation bound."""
+    import test_gpu_mv as tm
+    M, N, K, gs, x_bf16, o = MV_CASES[i]
+    out = [torch.float16, torch.bfloat16, torch.float32][o]
+    what = f"mv case {i}: M={M} N={N} K={K} gs={gs} bf16x={x_bf16} {out}"
+    tp.note(what)
+    x, W = linear_inputs(M, N, K, seed=6000 + i)
+    yt, wq, sw = tm.run(w8a8, x, W, gs, x_bf16, out)
+    r = tm.reference(x, wq, sw, gs, x_bf16)
+    tm.check_mv(yt, r["y"], r["mag"], K, K // gs if gs else 1, what)
+
+
+RMS_CASES = _rng_cases(2030, 24, lambda r: (int(r.integers(1, 301)), 8 * int(r.integers(1, 2049)),
+                                            bool(r.integers(2)), bool(r.integers(2)), float(r.choice([0.0, 1e-6, 1e-5]))))
+
+
+@pytest.mark.parametrize("i", range(len(RMS_CASES)))
+def test_random_rmsnorm_quantize(w8a8, i):
+    """The RMSNorm producer: codes bit-exact, scale within the fp32 sum bound."""
+    import test_gpu_rmsnorm_quant as tr
+    from synth_inputs import rmsnorm_inputs
+    M, K, x_bf16, g_bf16, eps = RMS_CASES[i]
+    x, g = rmsnorm_inputs(M, K, seed=7000 + i)
+    tr.check(w8a8, x, g, eps, x_bf16, g_bf16, f"rmsnorm case {i}: M={M} K={K} bf16x={x_bf16} bf16g={g_bf16} eps={eps}")
+
+
+SWIGLU_CASES = _rng_cases(2031, 24, lambda r: (int(r.integers(1, 201)), 8 * int(r.integers(1, 2049)), bool(r.integers(2))))
+
+
+@pytest.mark.parametrize("i", range(len(SWIGLU_CASES)))
+def test_random_swiglu_quantize(w8a8, i):
+    """The SwiGLU producer: codes and scales bit-exact."""
+    import test_gpu_swiglu as tw
+    M, I, bf16 = SWIGLU_CASES[i]
+    dtype = torch.bfloat16 if bf16 else torch.float16
+    tp.note(f"swiglu case {i}: M={M} I={I} {dtype}")
+    tw.check(w8a8, tw.inputs(M, I, seed=8000 + i, dtype=dtype), I, f"swiglu case {i}: {M}x{I} {dtype}")
+
+
+CLIP_CASES = _rng_cases(2032, 24, lambda r: (int(r.choice([8, 4])), int(r.choice([0, 64, 128])), 16 * int(r.integers(1, 41)),
+                                             int(r.integers(1, 33)), float(r.choice([99.9, 99.0, 97.5, 50.0, 100.0]))))
+
+
+@pytest.mark.parametrize("i", range(len(CLIP_CASES)))
+def test_random_quantize_weight_clipped(w8a8, i):
+    """Percentile-clipped weight quantization: codes and scales bit-exact."""
+    import test_gpu_clip as tc
+    bits, gs, N, kk, pct = CLIP_CASES[i]
+    K = kk * 128
+    W = tc.weights(N, K, seed=9000 + i)
+    tp.note(f"clip case {i}: bits={bits} gs={gs} N={N} K={K} pct={pct}")
+    wq, sw = w8a8.quantize_weight_clipped(torch.from_numpy(W).cuda(), bits, gs, pct)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_weight_clipped(W, bits, gs, pct)
+    assert (sw.cpu().numpy().view(np.uint32) == rs.view(np.uint32)).all(), f"clip case {i}: scales differ"
+    assert (wq.cpu().numpy() == rq).all(), f"clip case {i}: codes differ"
