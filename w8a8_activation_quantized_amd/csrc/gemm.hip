@@ -906,16 +906,21 @@ __device__ __forceinline__ uint32_t pack_2x16(float a, float b) {
 // Epilogue of the 16-bit outputs: the tile is staged through LDS as [BM][BN] rows (16-byte
 // chunk index XOR-ed with (row & 7): the MFMA layout's 8-byte writes, 16 rows per
 // instruction, and the row-contiguous 16-byte reads both stay free of bank conflicts) and
-// written as 16-byte pieces of output rows, in two halves: rows [64 h, 64 h + 64) of each
-// group's 128 (fragment rows fm in [FM/2 h, FM/2 h + FM/2)). The second half is converted
-// and staged while the first half's stores go out, between them, so the conversion work
-// and the store traffic overlap.
-template <class S, bool BF>
+// written as 16-byte pieces of output rows, in NP parts: rows [WM/NP h, WM/NP (h + 1)) of
+// each group's WM (fragment rows fm in [FM/NP h, FM/NP (h + 1))). Each part is converted and
+// staged while the previous part's stores go out, between them, so the conversion work and
+// the store traffic overlap; with four parts instead of two the first stores start after a
+// quarter of the conversions (M=4096 N=10240 K=2560 82.5 against 83.9 us, M=2048 N=10240
+// K=2560 43.9 against 45.0, M=2048 N=24576 K=4096 on 256 x 256 tiles 150.8 against 153.1;
+// identical outputs).
+template <class S, bool BF, int NP = 2>
 __device__ __forceinline__ void pp_store_staged(const v4i (&acc)[S::FN][S::FM], const float (&sxm)[S::FM],
                                                 const float4 (&s4)[S::FN], int8_t *smem, const GemmProblem &p, int m0,
                                                 int n0, int grp, int wq, int frow, int fchunk, int tid) {
-    constexpr int FN = S::FN, FM = S::FM, HF = FM / 2, RS = S::BN * 2, CPR = S::CPR, HR = S::WM / 2;
-    constexpr int ITS = S::HALF_ITS;
+    constexpr int FN = S::FN, FM = S::FM, RS = S::BN * 2, CPR = S::CPR;
+    constexpr int PF = FM / NP, PR = S::WM / NP;           // fragment rows and rows per group in a part
+    constexpr int PITS = S::BM / NP * CPR / S::NT;          // store iterations per part
+    static_assert(FM % NP == 0 && S::BM / NP * CPR % S::NT == 0, "epilogue parts");
     int coff[FN];  // byte offset in a staged row of this lane's 8-byte piece (row & 7 == frow & 7)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
@@ -935,11 +940,11 @@ __device__ __forceinline__ void pp_store_staged(const v4i (&acc)[S::FN][S::FM], 
     };
     const int rows = min(S::BM, p.M - m0), cols = min(S::BN, p.N - n0);
     uint16_t *y = static_cast<uint16_t *>(p.y);
-    // store iteration `it` of half h: chunk c = tid + NT it of the half's BM/2 rows
+    // store iteration `it` of part h: chunk c = tid + NT it of the part's BM / NP rows
     auto store = [&](int h, int it) __attribute__((always_inline)) {
         const int c = tid + it * S::NT;
         const int rr = c / CPR, cc = c - rr * CPR;
-        const int r = (rr % HR) + (rr / HR) * S::WM + h * HR;
+        const int r = (rr % PR) + (rr / PR) * S::WM + h * PR;
         if (r < rows && cc * 8 < cols) {
             const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + ((cc ^ (r & 7)) << 4));
             // streaming store: the tile's outputs are not read again here, and as ordinary
@@ -949,20 +954,23 @@ __device__ __forceinline__ void pp_store_staged(const v4i (&acc)[S::FN][S::FM], 
             __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(y + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)));
         }
     };
-    static_for<0, HF>([&](auto q) { stage(q); });
+    static_for<0, PF>([&](auto q) { stage(q); });
     lds_barrier();
-    static_for<0, HF>([&](auto q) {
-        constexpr int qi = decltype(q)::value;
-        static_for<qi * ITS / HF, (qi + 1) * ITS / HF>([&](auto it) { store(0, decltype(it)::value); });
-        stage(std::integral_constant<int, HF + qi>{});
+    static_for<1, NP>([&](auto pc) {
+        constexpr int pi = decltype(pc)::value;
+        static_for<0, PF>([&](auto q) {
+            constexpr int qi = decltype(q)::value;
+            static_for<qi * PITS / PF, (qi + 1) * PITS / PF>([&](auto it) { store(pi - 1, decltype(it)::value); });
+            stage(std::integral_constant<int, pi * PF + qi>{});
+        });
+        lds_barrier();
     });
-    lds_barrier();
-    static_for<0, ITS>([&](auto it) { store(1, decltype(it)::value); });
+    static_for<0, PITS>([&](auto it) { store(NP - 1, decltype(it)::value); });
 }
 
 // SPREAD = 16 A + B selects pp_loop3 with that split of each stage's DMA pieces (int8
 // weights, 128-value stages); 0 selects pp_loop2 (or pp_loop for 64-value stages).
-template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8, int SPREAD = 0>
+template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8, int SPREAD = 0, int EPI = 2>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tmap) {
     using S = PpShape<BN, BM, STAGES, BKS, WK>;
     constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW;
@@ -1091,9 +1099,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, TileMap tma
     const int out = p.out;
     if ((out == OUT_F16 || out == OUT_BF16) && p.y_rows16) {
         if (out == OUT_F16)
-            pp_store_staged<S, false>(acc, sxm, s4, smem, p, m0, n0, grp, wq, frow, fchunk, tid);
+            pp_store_staged<S, false, EPI>(acc, sxm, s4, smem, p, m0, n0, grp, wq, frow, fchunk, tid);
         else
-            pp_store_staged<S, true>(acc, sxm, s4, smem, p, m0, n0, grp, wq, frow, fchunk, tid);
+            pp_store_staged<S, true, EPI>(acc, sxm, s4, smem, p, m0, n0, grp, wq, frow, fchunk, tid);
         return;
     }
 #pragma unroll
@@ -2483,8 +2491,8 @@ constexpr Config kConfigs[] = {
     {256, 320, 8},  // 16: as 13 with two stages of 128-value K-tiles (128-byte DMA row segments)
     {256, 320, 8},  // 17: as 16 with int4 weights (per-channel scales or raw int32 sums); int8: 16
     {256, 256, 8},  // 18: as 16 with 256 x 256 tiles (64 x 128 per wave)
-    {256, 320, 8},  // 19: as 16 with each wave's DMA of a stage split over two memory phases
-    {256, 256, 8},  // 20: as 18 with the split DMA of 19
+    {256, 320, 8},  // 19: as 16 with each wave's DMA of a stage split over two memory phases and the epilogue in four parts
+    {256, 256, 8},  // 20: as 18 with the split DMA and four-part epilogue of 19
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -2530,14 +2538,14 @@ hipError_t launch_ms(const GemmProblem &p, int group_m, hipStream_t stream) {
 }
 
 
-template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8, int SPREAD = 0>
+template <int BN, int BM, int STAGES, int BKS = 64, int WK = W_INT8, int SPREAD = 0, int EPI = 2>
 hipError_t launch_pp(const GemmProblem &p, int group_m, hipStream_t stream) {
     TileMap t;
     t.tiles_m = (p.M + BM - 1) / BM;
     t.tiles_n = (p.N + BN - 1) / BN;
     t.group_m = group_m;
     dim3 grid(t.tiles_m * t.tiles_n), block(512);
-    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS, WK, SPREAD>), grid, block, 0, stream, p, t);
+    hipLaunchKernelGGL((gemm_pp_kernel<BN, BM, STAGES, BKS, WK, SPREAD, EPI>), grid, block, 0, stream, p, t);
     return hipGetLastError();
 }
 
@@ -2847,12 +2855,12 @@ hipError_t launch_gemm(const GemmProblem &p, int force_cfg, hipStream_t stream) 
         case 18: return launch_pp<256, 256, 2, 128>(p, gm, stream);
         case 20:
             if ((int64_t)p.N * p.K < ((int64_t)1 << 32) && (int64_t)p.M * p.K < ((int64_t)1 << 32))
-                return launch_pp<256, 256, 2, 128, W_INT8, 4 * 16 + 4>(p, gm, stream);
+                return launch_pp<256, 256, 2, 128, W_INT8, 4 * 16 + 4, 4>(p, gm, stream);
             return launch_pp<256, 256, 2, 128>(p, gm, stream);
         case 19:
             // 32-bit DMA offsets within each operand, else the same tile as 16
             if ((int64_t)p.N * p.K < ((int64_t)1 << 32) && (int64_t)p.M * p.K < ((int64_t)1 << 32))
-                return launch_pp<320, 256, 2, 128, W_INT8, 5 * 16 + 5>(p, gm, stream);
+                return launch_pp<320, 256, 2, 128, W_INT8, 5 * 16 + 5, 4>(p, gm, stream);
             return launch_pp<320, 256, 2, 128>(p, gm, stream);
         case 14: return launch_ms<128, 128, 4, 2, 2>(p, gm, stream);
         case 15: return launch_ms<64, 128, 6, 2, 4>(p, gm, stream);
