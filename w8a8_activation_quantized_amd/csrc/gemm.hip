@@ -576,9 +576,12 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
         // output rows: lane-contiguous runs of a row instead of the MFMA layout's 8-byte
         // pieces of 16 different rows, which store at about 60% of the rate.
         constexpr int RS = ms_out_row_stride<S>();
-        lds_barrier();
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
+        // staged and stored in two halves, rows [WM/2 h, WM/2 (h + 1)) of each wave row's WM:
+        // the second half is converted while the first half's stores go out
+        constexpr int CPR = S::BN / 8, HF = FM / 2, HR = S::WM / 2, ITS = S::BM / 2 * CPR / S::NT;
+        static_assert(FM % 2 == 0 && S::BM / 2 * CPR % S::NT == 0, "staged halves");
+        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
+        auto stage = [&](int fm) __attribute__((always_inline)) {
             const int lr = wm * S::WM + fm * 16 + frow;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
@@ -589,19 +592,30 @@ __global__ __launch_bounds__(512) void gemm_ms_kernel(GemmProblem p, TileMap tma
                                                : make_uint2(bf16_rne(y0) | (bf16_rne(y1) << 16), bf16_rne(y2) | (bf16_rne(y3) << 16));
                 *reinterpret_cast<uint2 *>(smem + lr * RS + 2 * (wn * S::WN + fn * 16 + 4 * fchunk)) = w;
             }
-        }
-        lds_barrier();
-        constexpr int CPR = S::BN / 8;  // 16-byte chunks per output row
-        const int rows = min(S::BM, M - m0), cols = min(S::BN, N - n0);
-#pragma unroll 4
-        for (int c = tid; c < S::BM * CPR; c += S::NT) {
-            const int r = c / CPR, cc = c - r * CPR;
+        };
+        auto store = [&](int h, int it) __attribute__((always_inline)) {
+            const int c = tid + it * S::NT;
+            const int rr = c / CPR, cc = c - rr * CPR;
+            const int r = (rr % HR) + (rr / HR) * S::WM + h * HR;
             if (r < rows && cc * 8 < cols) {
                 const v4u v = *reinterpret_cast<const v4u *>(smem + r * RS + 16 * cc);
                 // streaming store (see pp_store_staged)
                 __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(static_cast<uint16_t *>(p.y) + ((int64_t)(m0 + r) * p.ldy + n0 + cc * 8)));
             }
+        };
+        lds_barrier();
+#pragma unroll
+        for (int fm = 0; fm < HF; ++fm) stage(fm);
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < HF; ++q) {
+#pragma unroll
+            for (int it = q * ITS / HF; it < (q + 1) * ITS / HF; ++it) store(0, it);
+            stage(HF + q);
         }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < ITS; ++it) store(1, it);
         return;
     }
 #pragma unroll
