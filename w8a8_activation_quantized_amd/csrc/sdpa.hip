@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * SD_WAVES) __attribute__((amdgpu_waves_per_eu(2
 }
 
 constexpr int SD_COMBINE_THREADS = 1024;
-constexpr int SD_COMBINE_SPLIT = 4;  // workgroups per head in the merge (4: GQA 32/4, N = 32768: 17.7 against 18.6 us with 1)
+constexpr int SD_COMBINE_SPLIT = 8;  // workgroups per head in the merge (4: GQA 32/4, N = 32768: 17.7 against 18.6 us with 1; 8 against 4: 0.2-2.3 % faster over GQA 32/4 .. 32/32, N = 1024 .. 32768)
 
 // Second pass: merge the slices of one (b, h). Thread (d, part) of 1024 merges every PARTS-th
 // slice's (m, l, o[d]) into a running (M, L, A), eight slices at a time: their loads go out
